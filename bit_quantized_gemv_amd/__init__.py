@@ -1,0 +1,242 @@
+"""Python binding of libqmoe (include/qmoe.h): argument marshalling only.
+
+Every step of the quantized MoE FFN runs in the gfx950 HIP kernels of
+``libqmoe.so``; PyTorch only provides device memory and streams.  The
+library is built in-tree by ``bit_quantized_gemv_amd.build``; importing this
+package without it raises ImportError (there is no fallback path).
+
+Names mirror the C entry points: ``qmoe_gemv_affine4``, ``qmoe_router_topk``,
+``qmoe_expert_ffn``, ``qmoe_moe_decode``, ``qmoe_prefill_grouped``,
+``qmoe_rmsnorm``, ``qmoe_workspace_bytes``, ``qmoe_workspace_status``.
+Tensor arguments are torch tensors on the GPU; bf16/fp16 data may be given as
+``torch.bfloat16`` / ``torch.float16`` or as 16-bit integer bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Dict, Optional
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqmoe.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m bit_quantized_gemv_amd.build` "
+        "(the quantized MoE path has no CPU fallback)")
+
+_lib = C.CDLL(LIB_PATH)
+
+# status codes
+QMOE_OK = 0
+STATUS_NAMES = {0: "QMOE_OK", 1: "QMOE_ERR_NULL_ARG", 2: "QMOE_ERR_BAD_SHAPE",
+                3: "QMOE_ERR_UNSUPPORTED", 4: "QMOE_ERR_WORKSPACE", 5: "QMOE_ERR_ALIGN",
+                6: "QMOE_ERR_HIP", 7: "QMOE_ERR_DEVICE"}
+
+
+class QmoeError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        self.code = code
+        msg = _lib.qmoe_status_string(code).decode()
+        super().__init__(f"{fn}: {STATUS_NAMES.get(code, code)} ({msg})")
+
+
+class _QT(C.Structure):
+    _fields_ = [("q", C.c_void_p), ("scales", C.c_void_p), ("biases", C.c_void_p),
+                ("rows", C.c_int32), ("cols", C.c_int32), ("bits", C.c_int32),
+                ("group", C.c_int32), ("expert_stride_bytes", C.c_int64)]
+
+
+class _Layer(C.Structure):
+    _fields_ = [("hidden", C.c_int32), ("n_experts", C.c_int32), ("top_k", C.c_int32),
+                ("inter", C.c_int32), ("shared_inter", C.c_int32),
+                ("router", _QT), ("gate", _QT), ("up", _QT), ("down", _QT),
+                ("sh_gate", _QT), ("sh_up", _QT), ("sh_down", _QT),
+                ("rms_gamma", C.c_void_p), ("rms_eps", C.c_float), ("logit_bias", C.c_void_p)]
+
+
+_vp = C.c_void_p
+_lib.qmoe_status_string.restype = C.c_char_p
+_lib.qmoe_status_string.argtypes = [C.c_int]
+_lib.qmoe_gemv_affine4.argtypes = [C.POINTER(_QT), _vp, _vp, _vp]
+_lib.qmoe_router_topk.argtypes = [C.POINTER(_QT), _vp, _vp, C.c_int32, C.c_int32, _vp, _vp, _vp,
+                                  _vp, C.c_size_t, _vp]
+_lib.qmoe_expert_ffn.argtypes = [C.POINTER(_Layer), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 C.c_size_t, _vp]
+_lib.qmoe_moe_decode.argtypes = [C.POINTER(_Layer), _vp, _vp, C.c_int32, _vp, _vp, _vp, _vp,
+                                 C.c_size_t, _vp]
+_lib.qmoe_moe_decode_phased.argtypes = _lib.qmoe_moe_decode.argtypes
+_lib.qmoe_prefill_grouped.argtypes = [C.POINTER(_Layer), _vp, C.c_int32, _vp, _vp, _vp, _vp, _vp,
+                                      C.c_size_t, _vp]
+_lib.qmoe_rmsnorm.argtypes = [_vp, _vp, C.c_float, C.c_int32, C.c_int32, _vp, _vp]
+_lib.qmoe_workspace_bytes.restype = C.c_size_t
+_lib.qmoe_workspace_bytes.argtypes = [C.POINTER(_Layer), C.c_int32]
+_lib.qmoe_router_workspace_bytes.restype = C.c_size_t
+_lib.qmoe_router_workspace_bytes.argtypes = [C.c_int32, C.c_int32]
+_lib.qmoe_workspace_status.argtypes = [_vp, C.c_size_t, C.POINTER(C.c_int32), _vp]
+for _f in ("qmoe_gemv_affine4", "qmoe_router_topk", "qmoe_expert_ffn", "qmoe_moe_decode",
+           "qmoe_moe_decode_phased", "qmoe_prefill_grouped", "qmoe_rmsnorm",
+           "qmoe_workspace_status"):
+    getattr(_lib, _f).restype = C.c_int
+
+
+def lib() -> C.CDLL:
+    return _lib
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("expected a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    import torch
+
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(fn: str, code: int) -> None:
+    if code != QMOE_OK:
+        raise QmoeError(fn, code)
+
+
+class QTensor:
+    """One affine-quantized matrix on the GPU (or stacked experts)."""
+
+    def __init__(self, q, scales, biases, rows: int, cols: int, bits: int,
+                 expert_stride_bytes: int = 0, owner=None):
+        self.q, self.scales, self.biases = q, scales, biases
+        self.rows, self.cols, self.bits = rows, cols, bits
+        self.expert_stride_bytes = expert_stride_bytes
+        self._owner = owner  # keeps a backing tensor alive when q/s/b are raw addresses
+
+    def c(self) -> _QT:
+        return _QT(_ptr(self.q), _ptr(self.scales), _ptr(self.biases), self.rows, self.cols,
+                   self.bits, 64, self.expert_stride_bytes)
+
+
+class MoeLayer:
+    """Device weights of one MoE layer, as the C struct qmoe_moe_layer."""
+
+    def __init__(self, hidden: int, n_experts: int, top_k: int, inter: int, shared_inter: int,
+                 router: QTensor, gate: QTensor, up: QTensor, down: QTensor, sh_gate: QTensor,
+                 sh_up: QTensor, sh_down: QTensor, rms_gamma=None, rms_eps: float = 1e-6,
+                 logit_bias=None):
+        self.hidden, self.n_experts, self.top_k = hidden, n_experts, top_k
+        self.inter, self.shared_inter = inter, shared_inter
+        self.router, self.gate, self.up, self.down = router, gate, up, down
+        self.sh_gate, self.sh_up, self.sh_down = sh_gate, sh_up, sh_down
+        self.rms_gamma, self.rms_eps, self.logit_bias = rms_gamma, rms_eps, logit_bias
+        self._c = None
+
+    @staticmethod
+    def stacked_experts(blobs, offsets: Dict[str, int], hidden: int, inter: int):
+        """gate/up/down QTensors over a [E][blob_bytes] uint8 device tensor in
+        which every expert blob holds its parts at the given byte offsets."""
+        base = blobs.data_ptr()
+        stride = blobs.stride(0) * blobs.element_size()
+
+        def qt(name, rows, cols):
+            return QTensor(base + offsets[name + ".q"], base + offsets[name + ".s"],
+                           base + offsets[name + ".b"], rows, cols, 4, stride, owner=blobs)
+
+        return (qt("gate", inter, hidden), qt("up", inter, hidden), qt("down", hidden, inter))
+
+    def c(self) -> _Layer:
+        if self._c is None:
+            self._c = _Layer(self.hidden, self.n_experts, self.top_k, self.inter,
+                             self.shared_inter, self.router.c(), self.gate.c(), self.up.c(),
+                             self.down.c(), self.sh_gate.c(), self.sh_up.c(), self.sh_down.c(),
+                             _ptr(self.rms_gamma), float(self.rms_eps), _ptr(self.logit_bias))
+        return self._c
+
+    def workspace_bytes(self, T: int = 1) -> int:
+        return qmoe_workspace_bytes(self, T)
+
+    def new_workspace(self, T: int = 1, device="cuda"):
+        import torch
+
+        n = self.workspace_bytes(T)
+        if n == 0:
+            raise QmoeError("qmoe_workspace_bytes", 2)
+        return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------- entry points
+def qmoe_workspace_bytes(layer: MoeLayer, T: int = 1) -> int:
+    return int(_lib.qmoe_workspace_bytes(C.byref(layer.c()), T))
+
+
+def qmoe_router_workspace_bytes(n_experts: int, T: int) -> int:
+    return int(_lib.qmoe_router_workspace_bytes(n_experts, T))
+
+
+def qmoe_gemv_affine4(W: QTensor, x, y, stream=None) -> None:
+    qt = W.c()
+    _check("qmoe_gemv_affine4", _lib.qmoe_gemv_affine4(C.byref(qt), _ptr(x), _ptr(y),
+                                                        _stream(stream)))
+
+
+def qmoe_router_topk(Wr: QTensor, logit_bias, x, T: int, top_k: int, idx, w, logits, ws,
+                     stream=None) -> None:
+    qt = Wr.c()
+    _check("qmoe_router_topk", _lib.qmoe_router_topk(
+        C.byref(qt), _ptr(logit_bias), _ptr(x), T, top_k, _ptr(idx), _ptr(w), _ptr(logits),
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def qmoe_expert_ffn(layer: MoeLayer, h, idx, w, expert_slot, residual, out, ws,
+                    stream=None) -> None:
+    _check("qmoe_expert_ffn", _lib.qmoe_expert_ffn(
+        C.byref(layer.c()), _ptr(h), _ptr(idx), _ptr(w), _ptr(expert_slot), _ptr(residual),
+        _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def qmoe_moe_decode(layer: MoeLayer, x, expert_slot, residual: bool, out, idx_out, w_out, ws,
+                    stream=None, phased: bool = False) -> None:
+    fn = _lib.qmoe_moe_decode_phased if phased else _lib.qmoe_moe_decode
+    _check("qmoe_moe_decode", fn(
+        C.byref(layer.c()), _ptr(x), _ptr(expert_slot), int(bool(residual)), _ptr(out),
+        _ptr(idx_out), _ptr(w_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def qmoe_prefill_grouped(layer: MoeLayer, X, T: int, idx, w, residual, out, ws,
+                         stream=None) -> None:
+    _check("qmoe_prefill_grouped", _lib.qmoe_prefill_grouped(
+        C.byref(layer.c()), _ptr(X), T, _ptr(idx), _ptr(w), _ptr(residual), _ptr(out),
+        _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def qmoe_rmsnorm(x, gamma, eps: float, T: int, H: int, out, stream=None) -> None:
+    _check("qmoe_rmsnorm", _lib.qmoe_rmsnorm(_ptr(x), _ptr(gamma), float(eps), T, H, _ptr(out),
+                                             _stream(stream)))
+
+
+def qmoe_workspace_status(ws, stream=None) -> int:
+    """Device error word of a workspace (0 = every in-kernel wait completed);
+    synchronises the stream and clears the word."""
+    code = C.c_int32(0)
+    rc = _lib.qmoe_workspace_status(_ptr(ws), ws.numel() * ws.element_size(), C.byref(code),
+                                    _stream(stream))
+    if rc not in (QMOE_OK, 7):
+        _check("qmoe_workspace_status", rc)
+    return int(code.value)
+
+
+__all__ = [
+    "QTensor", "MoeLayer", "QmoeError", "lib", "LIB_PATH",
+    "qmoe_gemv_affine4", "qmoe_router_topk", "qmoe_expert_ffn", "qmoe_moe_decode",
+    "qmoe_prefill_grouped", "qmoe_rmsnorm", "qmoe_workspace_bytes",
+    "qmoe_router_workspace_bytes", "qmoe_workspace_status",
+]

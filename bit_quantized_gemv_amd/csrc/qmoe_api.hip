@@ -1,0 +1,209 @@
+// qmoe_api.hip -- the extern "C" entry points declared in include/qmoe.h:
+// argument validation, workspace sizing, and dispatch to the launchers.
+// Nothing here allocates, frees or synchronises (qmoe_workspace_status
+// excepted, which reads one word back).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "qmoe.h"
+#include "qmoe_common.h"
+
+namespace qmoe {
+qmoe_status launch_gemv4(const qmoe_qtensor& W, const uint16_t* x, float* y, void* stream);
+qmoe_status launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int T, int H,
+                           uint16_t* out, void* stream);
+qmoe_status launch_router(const qmoe_qtensor& Wr, const float* lbias, const uint16_t* x, int T,
+                          int K, int32_t* idx, float* w, float* logits, uint8_t* ws, void* stream);
+qmoe_status launch_moe_step(const qmoe_moe_layer& L, const uint16_t* x, const int32_t* idx_in,
+                            const float* w_in, const int32_t* slot, const uint16_t* residual,
+                            uint16_t* out, int32_t* idx_out, float* w_out, uint8_t* ws, int mode,
+                            void* stream);
+qmoe_status launch_prefill(const qmoe_moe_layer& L, const uint16_t* X, int T, const int32_t* idx,
+                           const float* w, const uint16_t* residual, uint16_t* out, uint8_t* ws,
+                           void* stream);
+size_t prefill_ws_bytes(const qmoe_moe_layer& L, int T);
+bool moe_step_supported(const qmoe_moe_layer& L);
+
+static bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static qmoe_status check_q(const qmoe_qtensor* t, int bits) {
+  if (!t || !t->q || !t->scales || !t->biases) return QMOE_ERR_NULL_ARG;
+  if (t->bits != bits || t->group != 64) return QMOE_ERR_UNSUPPORTED;
+  if (t->rows <= 0 || t->cols <= 0 || t->cols % 64) return QMOE_ERR_BAD_SHAPE;
+  if (!al16(t->q) || (t->expert_stride_bytes & 15) || t->expert_stride_bytes < 0)
+    return QMOE_ERR_ALIGN;
+  if (!al16(t->scales) || !al16(t->biases)) return QMOE_ERR_ALIGN;
+  return QMOE_OK;
+}
+
+static qmoe_status check_layer(const qmoe_moe_layer* L) {
+  if (!L) return QMOE_ERR_NULL_ARG;
+  const int H = L->hidden, E = L->n_experts, K = L->top_k, I = L->inter, Is = L->shared_inter;
+  if (H <= 0 || E <= 0 || K <= 0 || I <= 0 || Is <= 0) return QMOE_ERR_BAD_SHAPE;
+  if (H % 64 || I % 64 || Is % 64) return QMOE_ERR_BAD_SHAPE;
+  if (K > E) return QMOE_ERR_BAD_SHAPE;
+  if (K > QMOE_MAX_TOP_K || E > QMOE_MAX_EXPERTS || H > QMOE_MAX_HIDDEN) return QMOE_ERR_UNSUPPORTED;
+  // staged fp32 activations of the down projections must fit one block's LDS
+  if ((size_t)(K * I + Is) * 4 > 96 * 1024) return QMOE_ERR_UNSUPPORTED;
+  qmoe_status s;
+  if ((s = check_q(&L->router, 8)) != QMOE_OK) return s;
+  const qmoe_qtensor* m4[6] = {&L->gate, &L->up, &L->down, &L->sh_gate, &L->sh_up, &L->sh_down};
+  for (int i = 0; i < 6; ++i)
+    if ((s = check_q(m4[i], 4)) != QMOE_OK) return s;
+  if (L->router.rows != E || L->router.cols != H) return QMOE_ERR_BAD_SHAPE;
+  if (L->gate.rows != I || L->gate.cols != H || L->up.rows != I || L->up.cols != H)
+    return QMOE_ERR_BAD_SHAPE;
+  if (L->down.rows != H || L->down.cols != I) return QMOE_ERR_BAD_SHAPE;
+  if (L->sh_gate.rows != Is || L->sh_gate.cols != H || L->sh_up.rows != Is || L->sh_up.cols != H)
+    return QMOE_ERR_BAD_SHAPE;
+  if (L->sh_down.rows != H || L->sh_down.cols != Is) return QMOE_ERR_BAD_SHAPE;
+  if (L->rms_gamma && !al16(L->rms_gamma)) return QMOE_ERR_ALIGN;
+  return QMOE_OK;
+}
+
+static size_t ws_bytes_layer(const qmoe_moe_layer* L, int T) {
+  WsLayout wl = ws_layout(L->n_experts, L->top_k, L->inter, L->shared_inter, T);
+  size_t d = wl.total;
+  if (T > 1) {
+    size_t p = wl.pf + prefill_ws_bytes(*L, T);
+    if (p > d) d = p;
+  }
+  return d;
+}
+}  // namespace qmoe
+
+using namespace qmoe;
+
+extern "C" {
+
+const char* qmoe_status_string(qmoe_status s) {
+  switch (s) {
+    case QMOE_OK: return "ok";
+    case QMOE_ERR_NULL_ARG: return "a required pointer is NULL";
+    case QMOE_ERR_BAD_SHAPE: return "inconsistent or out-of-range sizes";
+    case QMOE_ERR_UNSUPPORTED: return "bits, group or size not supported by these kernels";
+    case QMOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case QMOE_ERR_ALIGN: return "pointer or stride not aligned (16 bytes for codes and activations)";
+    case QMOE_ERR_HIP: return "HIP runtime call failed";
+    case QMOE_ERR_DEVICE: return "a device-side wait gave up; outputs of that call are undefined";
+  }
+  return "unknown status";
+}
+
+size_t qmoe_workspace_bytes(const qmoe_moe_layer* L, int32_t T) {
+  if (check_layer(L) != QMOE_OK || T < 1 || T > QMOE_MAX_TOKENS) return 0;
+  return ws_bytes_layer(L, T);
+}
+
+size_t qmoe_router_workspace_bytes(int32_t n_experts, int32_t T) {
+  if (n_experts < 1 || n_experts > QMOE_MAX_EXPERTS || T < 1 || T > QMOE_MAX_TOKENS) return 0;
+  return ws_layout(n_experts, QMOE_MAX_TOP_K, 0, 0, T).total;
+}
+
+qmoe_status qmoe_gemv_affine4(const qmoe_qtensor* W, const uint16_t* x, float* y, void* stream) {
+  if (!W || !x || !y) return QMOE_ERR_NULL_ARG;
+  qmoe_status s = check_q(W, 4);
+  if (s != QMOE_OK) return s;
+  if (W->cols > QMOE_MAX_HIDDEN) return QMOE_ERR_UNSUPPORTED;
+  if (!al16(x)) return QMOE_ERR_ALIGN;
+  return launch_gemv4(*W, x, y, stream);
+}
+
+qmoe_status qmoe_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int32_t T, int32_t H,
+                         uint16_t* out, void* stream) {
+  if (!x || !gamma || !out) return QMOE_ERR_NULL_ARG;
+  if (T < 1 || H < 64 || H % 64 || H > QMOE_MAX_HIDDEN) return QMOE_ERR_BAD_SHAPE;
+  if (!al16(x) || !al16(gamma) || !al16(out)) return QMOE_ERR_ALIGN;
+  return launch_rmsnorm(x, gamma, eps, T, H, out, stream);
+}
+
+qmoe_status qmoe_router_topk(const qmoe_qtensor* Wr, const float* logit_bias, const uint16_t* x,
+                             int32_t T, int32_t top_k, int32_t* idx, float* w, float* logits,
+                             void* ws, size_t ws_bytes, void* stream) {
+  if (!Wr || !x || !idx || !w) return QMOE_ERR_NULL_ARG;
+  qmoe_status s = check_q(Wr, 8);
+  if (s != QMOE_OK) return s;
+  if (T < 1 || T > QMOE_MAX_TOKENS || top_k < 1 || top_k > Wr->rows) return QMOE_ERR_BAD_SHAPE;
+  if (top_k > QMOE_MAX_TOP_K || Wr->rows > QMOE_MAX_EXPERTS || Wr->cols > QMOE_MAX_HIDDEN)
+    return QMOE_ERR_UNSUPPORTED;
+  if (!al16(x)) return QMOE_ERR_ALIGN;
+  if (!ws) return QMOE_ERR_WORKSPACE;
+  if (ws_bytes < qmoe_router_workspace_bytes(Wr->rows, T)) return QMOE_ERR_WORKSPACE;
+  return launch_router(*Wr, logit_bias, x, T, top_k, idx, w, logits, static_cast<uint8_t*>(ws),
+                       stream);
+}
+
+qmoe_status qmoe_expert_ffn(const qmoe_moe_layer* L, const uint16_t* h, const int32_t* idx,
+                            const float* w, const int32_t* expert_slot, const uint16_t* residual,
+                            uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  qmoe_status s = check_layer(L);
+  if (s != QMOE_OK) return s;
+  if (!h || !idx || !w || !out) return QMOE_ERR_NULL_ARG;
+  if (!al16(h) || (residual && (reinterpret_cast<uintptr_t>(residual) & 1u))) return QMOE_ERR_ALIGN;
+  if (!ws) return QMOE_ERR_WORKSPACE;
+  if (ws_bytes < ws_bytes_layer(L, 1)) return QMOE_ERR_WORKSPACE;
+  return launch_moe_step(*L, h, idx, w, expert_slot, residual, out, nullptr, nullptr,
+                         static_cast<uint8_t*>(ws), 0, stream);
+}
+
+qmoe_status qmoe_moe_decode(const qmoe_moe_layer* L, const uint16_t* x, const int32_t* expert_slot,
+                            int32_t residual, uint16_t* out, int32_t* idx_out, float* w_out,
+                            void* ws, size_t ws_bytes, void* stream) {
+  qmoe_status s = check_layer(L);
+  if (s != QMOE_OK) return s;
+  if (!x || !out) return QMOE_ERR_NULL_ARG;
+  if (!al16(x)) return QMOE_ERR_ALIGN;
+  if (!ws) return QMOE_ERR_WORKSPACE;
+  if (ws_bytes < ws_bytes_layer(L, 1)) return QMOE_ERR_WORKSPACE;
+  return launch_moe_step(*L, x, nullptr, nullptr, expert_slot, residual ? x : nullptr, out,
+                         idx_out, w_out, static_cast<uint8_t*>(ws), 0, stream);
+}
+
+qmoe_status qmoe_prefill_grouped(const qmoe_moe_layer* L, const uint16_t* X, int32_t T,
+                                 const int32_t* idx, const float* w, const uint16_t* residual,
+                                 uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  qmoe_status s = check_layer(L);
+  if (s != QMOE_OK) return s;
+  if (!X || !idx || !w || !out) return QMOE_ERR_NULL_ARG;
+  if (T < 1 || T > QMOE_MAX_TOKENS) return QMOE_ERR_BAD_SHAPE;
+  if (!al16(X) || !al16(out) || (residual && !al16(residual))) return QMOE_ERR_ALIGN;
+  if (!ws) return QMOE_ERR_WORKSPACE;
+  if (ws_bytes < ws_bytes_layer(L, T)) return QMOE_ERR_WORKSPACE;
+  return launch_prefill(*L, X, T, idx, w, residual, out, static_cast<uint8_t*>(ws), stream);
+}
+
+qmoe_status qmoe_workspace_status(void* ws, size_t ws_bytes, int32_t* device_code, void* stream) {
+  if (!ws || !device_code) return QMOE_ERR_NULL_ARG;
+  if (ws_bytes < kCtlBytes) return QMOE_ERR_WORKSPACE;
+  uint32_t v = 0;
+  uint8_t* word = static_cast<uint8_t*>(ws) + (size_t)ctl::kError * 4;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(&v, word, 4, hipMemcpyDeviceToHost, st) != hipSuccess) return QMOE_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return QMOE_ERR_HIP;
+  *device_code = (int32_t)v;
+  if (v != 0) {
+    uint32_t zero = 0;
+    if (hipMemcpyAsync(word, &zero, 4, hipMemcpyHostToDevice, st) != hipSuccess) return QMOE_ERR_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return QMOE_ERR_HIP;
+    return QMOE_ERR_DEVICE;
+  }
+  return QMOE_OK;
+}
+
+/* Test-only variant: runs the step as separate launches per role instead of
+ * one launch with in-kernel waits (same kernels, same arithmetic). */
+qmoe_status qmoe_moe_decode_phased(const qmoe_moe_layer* L, const uint16_t* x,
+                                   const int32_t* expert_slot, int32_t residual, uint16_t* out,
+                                   int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
+                                   void* stream) {
+  qmoe_status s = check_layer(L);
+  if (s != QMOE_OK) return s;
+  if (!x || !out) return QMOE_ERR_NULL_ARG;
+  if (!al16(x)) return QMOE_ERR_ALIGN;
+  if (!ws || ws_bytes < ws_bytes_layer(L, 1)) return QMOE_ERR_WORKSPACE;
+  return launch_moe_step(*L, x, nullptr, nullptr, expert_slot, residual ? x : nullptr, out,
+                         idx_out, w_out, static_cast<uint8_t*>(ws), 1, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,1050 @@
+// qmoe_decode.hip -- decode-path kernels for gfx950: the 4-bit GEMV, the
+// 8-bit router with softmax top-k, RMSNorm, and the MoE FFN step (shared +
+// routed gate/up with GELU, down projections, router-weighted combine,
+// residual) in one launch.
+//
+// The step (remio.ai "TurboFieldfare esegue Mac Gemma 4 26B in 2 GB…",
+// section "L'affermazione dei 2 GB trasforma la larghezza di banda dell'SSD
+// nel nuovo vincolo"; devtrends.cc "Come eseguire un modello da 26 miliardi…",
+// section "Qual è il trucco principale dell'architettura"): per layer a router
+// picks 8 experts for the token, the always-on shared expert runs alongside,
+// and the two branches are combined.
+//
+// Decode is bound by HBM bandwidth (about 3.5 flop per weight byte), so the
+// kernels are vector-memory GEMVs: 16-byte loads of packed codes that read
+// 128 contiguous bytes per row per instruction, dequantization in registers,
+// activations staged once per block in LDS, wave shuffles for row sums.  No
+// matrix cores here.
+//
+// One decode step is one launch whose blocks take "roles", ordered so that a
+// block only ever waits for blocks with smaller indices:
+//   R  router: 8 experts per block; publishes its logits
+//   S  shared-expert gate/up (+GELU): 4 row-blocks of 8 rows per block
+//   G  routed-expert gate/up (+GELU): needs the routing
+//   D  8 output rows per block: shared down rows as soon as S is done, then
+//      each routed expert's down rows as soon as that expert's G blocks are
+//      done; weighted combine, residual, bf16 output
+// Every block that needs the routing computes the top-k itself from the
+// published logits (no extra hop).  Workgroups are dispatched in index
+// order, so a waiting block's producers have all been dispatched and never
+// wait on it: every wait ends.  Each wait is also bounded in time and then
+// reports a device error instead of hanging.
+//
+// Hand-offs use flags that carry a per-call epoch (read from the workspace at
+// the start, advanced by the last D block), device-coherent stores/loads for
+// the exchanged values, and per-group arrival counters of at most 16 blocks
+// (same-address atomics serialise across the XCDs).
+//
+// Every weight and scale load is unconditional (out-of-range chunks re-read
+// a valid address and only the arithmetic is predicated) and, for the model
+// shapes, every trip count is a compile-time constant: the compiler then
+// waits for each load just before its first use, so the math of the first
+// chunks overlaps the transfer of the last ones.
+#include "qmoe_common.h"
+
+namespace qmoe {
+
+constexpr int kSP = 11;          // gate/up steps per pass (runtime shapes)
+constexpr int kMaxXW = 2;        // activation words per thread kept in registers
+constexpr int kMS = 6;           // shared-down steps per wave (runtime shapes)
+constexpr int kMR = 4;           // routed-down steps per expert (runtime shapes)
+constexpr int kSR = 8;           // router steps per wave per pass (runtime shapes)
+constexpr uint64_t kWaitTicks = 20000000ull;  // 0.2 s of the 100 MHz clock
+
+// LDS "sys" words at the start of every block's LDS
+constexpr int kSysEpoch = 0, kSysOk = 1, kSysIdx = 8, kSysW = 16, kSysRed = 32;
+constexpr int kSysTkIdx = 96, kSysTkW = 160;  // per-wave top-k of the standalone router
+constexpr int kSysBytes = 1024;
+
+__host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+__host__ __device__ inline size_t al16(size_t n) { return (n + 15) & ~(size_t)15; }
+
+// ----------------------------------------------------------- arguments
+struct DecodeArgs {
+  int H, E, K, I, Is;
+  DevQ router, gate, up, down, shg, shu, shd;
+  const uint16_t* x;        // bf16 [H]: layer input (or expert input h)
+  const uint16_t* gamma;    // bf16 [H] RMSNorm weight, or null
+  float eps;
+  const float* lbias;       // fp32 [E] or null
+  const int32_t* idx_in;    // given routing or null (router runs)
+  const float* w_in;
+  const int32_t* slot;      // expert -> stacked position, or null
+  const uint16_t* residual; // bf16 [H] or null
+  uint16_t* out;
+  int32_t* idx_out;         // optional copies of the routing
+  float* w_out;
+  uint8_t* ws;
+  WsLayout wl;
+  int nR, nS, nG, nD;       // role sizes in blocks
+  int perG;                 // G blocks per expert
+  int role0;                // role index of blockIdx.x == 0
+};
+
+__device__ __forceinline__ uint32_t* ctl_of(const DecodeArgs& a) {
+  return reinterpret_cast<uint32_t*>(a.ws + a.wl.ctl);
+}
+__device__ __forceinline__ float* logits_of(const DecodeArgs& a) {
+  return reinterpret_cast<float*>(a.ws + a.wl.logits);
+}
+__device__ __forceinline__ float* a_sh_of(const DecodeArgs& a) {
+  return reinterpret_cast<float*>(a.ws + a.wl.a_sh);
+}
+__device__ __forceinline__ float* a_rt_of(const DecodeArgs& a) {
+  return reinterpret_cast<float*>(a.ws + a.wl.a_rt);
+}
+
+// --------------------------------------------------------------- waits
+// One full wave: wait until flags[0..n) all equal `epoch` (n <= 64).
+__device__ bool wave_wait_flags(const uint32_t* flags, int n, uint32_t epoch, uint32_t* ctlw,
+                                uint32_t code) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0;; ++it) {
+    bool ok = lane >= n || ld_dev(flags + lane) == epoch;
+    if (__all(ok)) return true;
+    if ((it & 15) == 15) {
+      if (ld_dev(ctlw + ctl::kError) != 0) return false;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+        if (lane == 0) st_dev(ctlw + ctl::kError, code);
+        return false;
+      }
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+// Whole block: wave 0 waits, the others meet it at a barrier.
+__device__ bool block_wait_flags(const uint32_t* flags, int n, uint32_t epoch, uint32_t* ctlw,
+                                 uint32_t code, uint32_t* sys) {
+  if (threadIdx.x < 64) {
+    bool ok = wave_wait_flags(flags, n, epoch, ctlw, code);
+    if (threadIdx.x == 0) sys[kSysOk] = ok ? 1u : 0u;
+  }
+  __syncthreads();
+  bool ok = sys[kSysOk] != 0;
+  __syncthreads();
+  return ok;
+}
+
+// This block's device stores are complete; count it in its group and, as
+// the last arrival, reset the counter and raise the group flag.
+__device__ void block_publish(uint32_t* cnt, uint32_t* flag, uint32_t size, uint32_t epoch) {
+  wait_vm();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t prev = add_dev(cnt, 1u);
+    if (prev == size - 1) {
+      st_dev(cnt, 0u);
+      st_dev(flag, epoch);
+    }
+  }
+}
+
+__device__ uint32_t block_epoch(uint32_t* ctlw, uint32_t* sys) {
+  if (threadIdx.x == 0) sys[kSysEpoch] = ld_dev(ctlw + ctl::kEpoch) + 1u;
+  __syncthreads();
+  return sys[kSysEpoch];
+}
+
+// ------------------------------------------------------------ reductions
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
+                                                                0xF, 0xF, false));
+}
+// Maximum over the wave (every lane gets it).
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x124>(v));  // row_ror:4
+  v = fmaxf(v, dpp_f<0x128>(v));  // row_ror:8
+  float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+  float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+  float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+  float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
+// Block-wide sum of one float per thread (fixed order; same bits everywhere).
+__device__ float block_sum(float v, float* red) {
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  int wave = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  __syncthreads();
+  float s = 0.f;
+  for (int i = 0; i < kWavesPerBlock; ++i) s += red[i];
+  return s;
+}
+
+// ============================================================== routing
+// One wave: top-k of logits[0..E) (descending; ties to the lower index) and
+// the softmax over the kept logits (exp(l - l_max) normalised by their sum).
+// Results go to idx_s/w_s (LDS) and, optionally, to idx2/w2.
+__device__ void wave_topk(const float* lg, bool coherent, int E, int K, int32_t* idx_s,
+                          float* w_s, int32_t* idx2, float* w2) {
+  const int lane = threadIdx.x & 63;
+  constexpr int NV = QMOE_MAX_EXPERTS / 64;
+  float v[NV];
+  uint32_t live = 0;
+#pragma unroll
+  for (int m = 0; m < NV; ++m) {
+    int e = lane + 64 * m;
+    v[m] = -INFINITY;
+    if (e < E) {
+      v[m] = coherent ? ld_dev(lg + e) : lg[e];
+      live |= 1u << m;
+    }
+  }
+  float top = 0.f, sel = 0.f;
+  int sel_i = 0;
+  for (int j = 0; j < K; ++j) {
+    float lm = -INFINITY;
+#pragma unroll
+    for (int m = 0; m < NV; ++m)
+      if ((live >> m) & 1u) lm = fmaxf(lm, v[m]);
+    float mx = wave_max(lm);
+    int e = -1;
+#pragma unroll
+    for (int m = NV - 1; m >= 0; --m) {
+      uint64_t bal = __ballot(((live >> m) & 1u) && v[m] == mx);
+      if (bal) e = 64 * m + (int)__builtin_ctzll(bal);
+    }
+    if ((e & 63) == lane) live &= ~(1u << (e >> 6));
+    if (j == 0) top = mx;
+    if (lane == j) {
+      sel = mx;
+      sel_i = e;
+    }
+  }
+  float p = lane < K ? expf(sel - top) : 0.f;
+  float sum = 0.f;
+  for (int j = 0; j < K; ++j)
+    sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), j));
+  if (lane < K) {
+    float wj = p / sum;
+    idx_s[lane] = sel_i;
+    w_s[lane] = wj;
+    if (idx2) idx2[lane] = sel_i;
+    if (w2) w2[lane] = wj;
+  }
+}
+
+// Routing for a consumer block: from the caller's arrays, or wait for the
+// router blocks and run top-k on their logits.  Leaves idx/w in sys LDS.
+__device__ bool block_routing(const DecodeArgs& a, uint32_t epoch, uint32_t* sys, bool write_out) {
+  int32_t* idx_s = reinterpret_cast<int32_t*>(sys + kSysIdx);
+  float* w_s = reinterpret_cast<float*>(sys + kSysW);
+  if (a.idx_in) {
+    if (threadIdx.x < a.K) {
+      idx_s[threadIdx.x] = a.idx_in[threadIdx.x];
+      w_s[threadIdx.x] = a.w_in[threadIdx.x];
+    }
+    __syncthreads();
+    return true;
+  }
+  uint32_t* ctlw = ctl_of(a);
+  if (!block_wait_flags(ctlw + ctl::kFlagR, a.nR, epoch, ctlw, 1, sys)) return false;
+  if (threadIdx.x < 64)
+    wave_topk(logits_of(a), true, a.E, a.K, idx_s, w_s, write_out ? a.idx_out : nullptr,
+              write_out ? a.w_out : nullptr);
+  __syncthreads();
+  return true;
+}
+
+// -------------------------------------------------------------- staging
+// Eight bf16 values (one uint4) of the expert input: x as is, or
+// bf16(x * inv * gamma).
+__device__ __forceinline__ uint4 norm_word(uint4 r, const uint16_t* gamma, float inv, int v) {
+  if (!gamma) return r;
+  uint4 g = reinterpret_cast<const uint4*>(gamma)[v];
+  uint32_t xr[4] = {r.x, r.y, r.z, r.w}, gr[4] = {g.x, g.y, g.z, g.w}, o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float lo = bf16_to_f32(xr[i] & 0xffffu) * inv * bf16_to_f32(gr[i] & 0xffffu);
+    float hi = bf16_to_f32(xr[i] >> 16) * inv * bf16_to_f32(gr[i] >> 16);
+    o[i] = (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+  }
+  return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+// The activation words of this thread, loaded first so that nothing issued
+// later has to complete before they can be staged.
+struct XRegs {
+  uint4 w[kMaxXW];
+};
+__device__ __forceinline__ void x_load(XRegs& X, const uint16_t* x, int H) {
+  const uint4* x4 = reinterpret_cast<const uint4*>(x);
+  const int Wn = H / 8;
+#pragma unroll
+  for (int i = 0; i < kMaxXW; ++i) X.w[i] = x4[min((int)threadIdx.x + i * kBlock, Wn - 1)];
+}
+
+__device__ float x_inv_rms(const XRegs& X, const uint16_t* x, int H, float eps, float* red) {
+  float ss = 0.f;
+  const int Wn = H / 8;
+  const uint4* x4 = reinterpret_cast<const uint4*>(x);
+  for (int i = 0; i * kBlock < Wn; ++i) {
+    int v = threadIdx.x + i * kBlock;
+    if (v >= Wn) break;
+    uint4 w;
+    if (i < kMaxXW) {
+      w = X.w[0];
+#pragma unroll
+      for (int k = 1; k < kMaxXW; ++k)
+        if (i == k) w = X.w[k];
+    } else {
+      w = x4[v];
+    }
+    uint32_t r[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float lo = bf16_to_f32(r[k] & 0xffffu), hi = bf16_to_f32(r[k] >> 16);
+      ss = fmaf(lo, lo, ss);
+      ss = fmaf(hi, hi, ss);
+    }
+  }
+  ss = block_sum(ss, red);
+  return 1.0f / sqrtf(ss / (float)H + eps);
+}
+
+// Word v's eight bf16 values -> the dot2 pair layout xs[j*CH + c] (v = 4c+j)
+// and chunk sums xh[c].
+__device__ __forceinline__ void put_pairs(uint4 r, int v, bool ok, int CH, uint4* xs, float* xh) {
+  uint4 pr;
+  pr.x = (r.x & 0xffffu) | (r.y << 16);          // x0, x2
+  pr.y = (r.z & 0xffffu) | (r.w << 16);          // x4, x6
+  pr.z = (r.x >> 16) | (r.y & 0xffff0000u);      // x1, x3
+  pr.w = (r.z >> 16) | (r.w & 0xffff0000u);      // x5, x7
+  float s = ((bf16_to_f32(r.x & 0xffffu) + bf16_to_f32(r.x >> 16)) +
+             (bf16_to_f32(r.y & 0xffffu) + bf16_to_f32(r.y >> 16))) +
+            ((bf16_to_f32(r.z & 0xffffu) + bf16_to_f32(r.z >> 16)) +
+             (bf16_to_f32(r.w & 0xffffu) + bf16_to_f32(r.w >> 16)));
+  s += __shfl_xor(s, 1);
+  s += __shfl_xor(s, 2);
+  if (ok) {
+    int c = v >> 2, j = v & 3;
+    xs[j * CH + c] = pr;
+    if (j == 0) xh[c] = s;
+  }
+}
+
+// Word v's values -> router layout xr[j*CH8 + c] (fp32, column order), sums.
+__device__ __forceinline__ void put_f32(uint4 r, int v, bool ok, int CH8, float4* xr, float* xh) {
+  float4 f0 = make_float4(bf16_to_f32(r.x & 0xffffu), bf16_to_f32(r.x >> 16),
+                          bf16_to_f32(r.y & 0xffffu), bf16_to_f32(r.y >> 16));
+  float4 f1 = make_float4(bf16_to_f32(r.z & 0xffffu), bf16_to_f32(r.z >> 16),
+                          bf16_to_f32(r.w & 0xffffu), bf16_to_f32(r.w >> 16));
+  float s = ((f0.x + f0.y) + (f0.z + f0.w)) + ((f1.x + f1.y) + (f1.z + f1.w));
+  s += __shfl_xor(s, 1);
+  if (ok) {
+    int c = v >> 1, j = (v & 1) * 2;
+    xr[j * CH8 + c] = f0;
+    xr[(j + 1) * CH8 + c] = f1;
+    if ((v & 1) == 0) xh[c] = s;
+  }
+}
+
+// Stage the expert input h into LDS (pairs layout or router layout).  The
+// words held in X are used; words beyond kMaxXW per thread are loaded here.
+template <bool PAIRS>
+__device__ void x_stage(const XRegs& X, const uint16_t* x, const uint16_t* gamma, float inv, int H,
+                        void* dst, float* xh) {
+  const int Wn = H / 8;
+  const uint4* x4 = reinterpret_cast<const uint4*>(x);
+#pragma unroll
+  for (int i = 0; i < kMaxXW; ++i) {
+    if (i * kBlock < Wn) {
+      int v = threadIdx.x + i * kBlock;
+      bool ok = v < Wn;
+      uint4 r = ok ? norm_word(X.w[i], gamma, inv, v) : make_uint4(0, 0, 0, 0);
+      if (PAIRS)
+        put_pairs(r, v, ok, H / 32, reinterpret_cast<uint4*>(dst), xh);
+      else
+        put_f32(r, v, ok, H / 16, reinterpret_cast<float4*>(dst), xh);
+    }
+  }
+  for (int i = kMaxXW; i * kBlock < Wn; ++i) {
+    int v = threadIdx.x + i * kBlock;
+    bool ok = v < Wn;
+    uint4 r = ok ? norm_word(x4[v], gamma, inv, v) : make_uint4(0, 0, 0, 0);
+    if (PAIRS)
+      put_pairs(r, v, ok, H / 32, reinterpret_cast<uint4*>(dst), xh);
+    else
+      put_f32(r, v, ok, H / 16, reinterpret_cast<float4*>(dst), xh);
+  }
+}
+
+// ------------------------------------------------- 4-bit row-block GEMV
+// NM matrices with the same shape and the same input (gate and up) share
+// the staged activations.  Each wave owns a row-block of 8 rows; its
+// scale/bias pairs go through a wave-private LDS table sbl[k][8][G] of
+// (s | b << 16), filled with one 16-byte load of s and one of b per lane.
+// SP: steps per pass (8 chunks per step); CHC: chunks per row when known at
+// compile time (0: runtime, passes of SP steps).
+template <int NM, int SP>
+struct Rows4 {
+  uint4 w[NM][SP];
+  uint4 sv[NM], bv[NM];
+};
+
+// Scale units (8 fp16 each) of the row-block; the load is unconditional,
+// lanes past the row-block's units re-read its last one.
+template <int NM, int SP>
+__device__ __forceinline__ void rows4_load_sb(Rows4<NM, SP>& R, const DevQ (&m)[NM], int row0,
+                                              int rows, int G) {
+  const int lane = threadIdx.x & 63;
+  const int64_t total = (int64_t)rows * G / 8;          // whole units in the array
+  const int64_t first = (int64_t)min(row0, rows - 1) * G / 8;
+  const int64_t u = min(first + min(lane, G - 1), total - 1);
+#pragma unroll
+  for (int k = 0; k < NM; ++k) {
+    R.sv[k] = reinterpret_cast<const uint4*>(m[k].s)[u];
+    R.bv[k] = reinterpret_cast<const uint4*>(m[k].b)[u];
+  }
+}
+
+__device__ __forceinline__ void put_sb8(uint4 sv, uint4 bv, uint32_t* dst) {
+  uint4 lo, hi;
+  lo.x = (sv.x & 0xffffu) | (bv.x << 16);
+  lo.y = (sv.x >> 16) | (bv.x & 0xffff0000u);
+  lo.z = (sv.y & 0xffffu) | (bv.y << 16);
+  lo.w = (sv.y >> 16) | (bv.y & 0xffff0000u);
+  hi.x = (sv.z & 0xffffu) | (bv.z << 16);
+  hi.y = (sv.z >> 16) | (bv.z & 0xffff0000u);
+  hi.z = (sv.w & 0xffffu) | (bv.w << 16);
+  hi.w = (sv.w >> 16) | (bv.w & 0xffff0000u);
+  reinterpret_cast<uint4*>(dst)[0] = lo;
+  reinterpret_cast<uint4*>(dst)[1] = hi;
+}
+
+// Fill the table.  The fast path covers row-blocks of 8 whole rows with
+// G <= 64 (one unit per lane); otherwise pairs are copied one by one.
+template <int NM, int SP>
+__device__ __forceinline__ void rows4_put_sb(const Rows4<NM, SP>& R, const DevQ (&m)[NM], int row0,
+                                             int rows, int G, uint32_t* sbl) {
+  const int lane = threadIdx.x & 63;
+  const int nr = max(0, min(kRowsPerUnit, rows - row0));
+  const bool fast = nr == kRowsPerUnit && G <= 64;
+#pragma unroll
+  for (int k = 0; k < NM; ++k) {
+    uint32_t* t = sbl + k * kRowsPerUnit * G;
+    if (fast) {
+      if (lane < G) put_sb8(R.sv[k], R.bv[k], t + 8 * lane);
+    } else {
+      const uint16_t* s = m[k].s + (int64_t)row0 * G;
+      const uint16_t* b = m[k].b + (int64_t)row0 * G;
+      for (int h = lane; h < nr * G; h += 64) t[h] = (uint32_t)s[h] | ((uint32_t)b[h] << 16);
+    }
+  }
+}
+
+template <int NM, int SP>
+__device__ __forceinline__ void rows4_load(Rows4<NM, SP>& R, const DevQ (&m)[NM], int row,
+                                           int CH, int step0, int p) {
+#pragma unroll
+  for (int i = 0; i < SP; ++i) {
+    int c = min((step0 + i) * kSlots + p, CH - 1);
+    int64_t o = ((int64_t)row * CH + c) * 16;
+#pragma unroll
+    for (int k = 0; k < NM; ++k) R.w[k][i] = ldg16(m[k].q + o);
+  }
+}
+
+template <int NM, int SP>
+__device__ __forceinline__ void rows4_compute(const Rows4<NM, SP>& R, const uint4* xs,
+                                              const float* xh, const uint32_t* sbl, int r, int G,
+                                              int CH, int step0, int p, float (&acc)[NM]) {
+#pragma unroll
+  for (int i = 0; i < SP; ++i) {
+    int c = (step0 + i) * kSlots + p;
+    if (c < CH) {
+      uint4 x0 = xs[c], x1 = xs[CH + c], x2 = xs[2 * CH + c], x3 = xs[3 * CH + c];
+      float X = xh[c];
+#pragma unroll
+      for (int k = 0; k < NM; ++k) {
+        uint32_t sb = sbl[(k * kRowsPerUnit + r) * G + (c >> 1)];
+        float d = 0.f;
+        d = dot_word4_bf16(R.w[k][i].x, x0, d);
+        d = dot_word4_bf16(R.w[k][i].y, x1, d);
+        d = dot_word4_bf16(R.w[k][i].z, x2, d);
+        d = dot_word4_bf16(R.w[k][i].w, x3, d);
+        acc[k] = fmaf(half_to_f32(sb & 0xffffu), d, acc[k]);
+        acc[k] = fmaf(half_to_f32(sb >> 16), X, acc[k]);
+      }
+    }
+  }
+}
+
+// One wave: rows [row0, row0+8) of NM matrices of `rows` rows and H columns.
+// `stage` runs between the first pass's loads and its math and must end
+// with a block barrier.  sbl: this wave's LDS table (NM*8*G words).
+template <int NM, int CHC, typename StageFn>
+__device__ __forceinline__ void rows4_run(const DevQ (&m)[NM], int row0, int rows, int H_rt,
+                                          const uint4* xs, const float* xh, uint32_t* sbl,
+                                          StageFn stage, float (&acc)[NM]) {
+  constexpr int SP = CHC ? cdiv(CHC, kSlots) : kSP;
+  const int CH = CHC ? CHC : H_rt / 32;
+  const int G = CH / 2, nsteps = cdiv(CH, kSlots);
+  const int lane = threadIdx.x & 63, r = lane & 7, p = lane >> 3;
+  const int row = min(row0 + r, rows - 1);
+  Rows4<NM, SP> R;
+#pragma unroll
+  for (int k = 0; k < NM; ++k) acc[k] = 0.f;
+  rows4_load_sb<NM, SP>(R, m, row0, rows, G);
+  rows4_load<NM, SP>(R, m, row, CH, 0, p);
+  rows4_put_sb<NM, SP>(R, m, row0, rows, G, sbl);
+  stage();
+  rows4_compute<NM, SP>(R, xs, xh, sbl, r, G, CH, 0, p, acc);
+  if (!CHC) {
+    for (int s0 = SP; s0 < nsteps; s0 += SP) {
+      rows4_load<NM, SP>(R, m, row, CH, s0, p);
+      rows4_compute<NM, SP>(R, xs, xh, sbl, r, G, CH, s0, p, acc);
+    }
+  }
+#pragma unroll
+  for (int k = 0; k < NM; ++k) acc[k] = rowblock_sum(acc[k]);
+}
+
+// LDS carve-ups (bytes).  Gate/up: sys | xs pairs (H*2) | xh (H/32 floats)
+// | per-wave scale tables (4 waves x NM matrices x 8 rows x H/64 words).
+__host__ __device__ inline size_t gu_xh_off(int H) { return kSysBytes + (size_t)H * 2; }
+__host__ __device__ inline size_t gu_sb_off(int H) { return al16(gu_xh_off(H) + (size_t)(H / 32) * 4); }
+__host__ __device__ inline size_t gu_sb_words(int H) { return (size_t)2 * kRowsPerUnit * (H / 64); }
+__host__ __device__ inline size_t gu_lds(int H) {
+  return gu_sb_off(H) + (size_t)kWavesPerBlock * gu_sb_words(H) * 4;
+}
+__host__ __device__ inline size_t router_lds(int H) {
+  return kSysBytes + (size_t)H * 4 + (size_t)(H / 16) * 4;
+}
+// Down: sys | a_s (Is floats) | its chunk sums | per-wave a_k (I floats) + sums
+__host__ __device__ inline size_t down_w_off(int Is) {
+  return al16(kSysBytes + (size_t)Is * 4 + (size_t)(Is / 32) * 4);
+}
+__host__ __device__ inline size_t down_w_stride(int I) { return al16((size_t)I * 4 + (size_t)(I / 32) * 4); }
+__host__ __device__ inline size_t down_lds(int I, int Is) {
+  return down_w_off(Is) + (size_t)kWavesPerBlock * down_w_stride(I);
+}
+
+// ======================================================= qmoe_gemv_affine4
+template <int CHC>
+__global__ __launch_bounds__(kBlock) void k_gemv4(DevQ W, int rows, int cols, const uint16_t* x,
+                                                  float* y) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint4* xs = reinterpret_cast<uint4*>(smem + kSysBytes);
+  float* xh = reinterpret_cast<float*>(smem + gu_xh_off(cols));
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t* sbl = reinterpret_cast<uint32_t*>(smem + gu_sb_off(cols)) + wave * gu_sb_words(cols);
+  const int row0 = (blockIdx.x * kWavesPerBlock + wave) * kRowsPerUnit;
+  XRegs X;
+  x_load(X, x, cols);
+  DevQ m[1] = {W};
+  float acc[1];
+  rows4_run<1, CHC>(m, row0, rows, cols, xs, xh, sbl,
+                    [&] {
+                      x_stage<true>(X, x, nullptr, 1.f, cols, xs, xh);
+                      __syncthreads();
+                    },
+                    acc);
+  if ((lane >> 3) == 0 && row0 + (lane & 7) < rows) y[row0 + (lane & 7)] = acc[0];
+}
+
+// ============================================================= RMSNorm
+__global__ __launch_bounds__(kBlock) void k_rmsnorm(const uint16_t* x, const uint16_t* gamma,
+                                                    float eps, int H, uint16_t* out) {
+  __shared__ float red[kWavesPerBlock];
+  const uint16_t* xt = x + (size_t)blockIdx.x * H;
+  const uint4* x4 = reinterpret_cast<const uint4*>(xt);
+  float ss = 0.f;
+  for (int v = threadIdx.x; v < H / 8; v += kBlock) {
+    uint4 r = x4[v];
+    uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      float lo = bf16_to_f32(w[k] & 0xffffu), hi = bf16_to_f32(w[k] >> 16);
+      ss = fmaf(lo, lo, ss);
+      ss = fmaf(hi, hi, ss);
+    }
+  }
+  ss = block_sum(ss, red);
+  float inv = 1.0f / sqrtf(ss / (float)H + eps);
+  uint4* o4 = reinterpret_cast<uint4*>(out + (size_t)blockIdx.x * H);
+  for (int v = threadIdx.x; v < H / 8; v += kBlock) o4[v] = norm_word(x4[v], gamma, inv, v);
+}
+
+// ============================================================== router
+// Logits of rows [row0, row0+8) of the 8-bit router for one staged token;
+// wave w takes steps w, w+4, ...  SR steps per wave per pass.
+template <int SR>
+struct RRegs {
+  uint4 w[SR];
+  uint32_t sb[SR];
+};
+template <int SR>
+__device__ __forceinline__ void router_load(RRegs<SR>& R, const DevQ& Wr, int row0, int E, int H,
+                                            int s0) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 7, p = lane >> 3;
+  const int CH8 = H / 16, G = H / 64, row = min(row0 + r, E - 1);
+#pragma unroll
+  for (int i = 0; i < SR; ++i) {
+    int c = min((s0 + wave + i * kWavesPerBlock) * kSlots + p, CH8 - 1);
+    R.w[i] = ldg16(Wr.q + ((int64_t)row * CH8 + c) * 16);
+    R.sb[i] = ld_sb(Wr.s, Wr.b, (int64_t)row * G + (c >> 2));
+  }
+}
+template <int SR>
+__device__ __forceinline__ float router_compute(const RRegs<SR>& R, int H, int s0,
+                                                const float4* xr, const float* xh, float acc) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, p = lane >> 3;
+  const int CH8 = H / 16;
+#pragma unroll
+  for (int i = 0; i < SR; ++i) {
+    int c = (s0 + wave + i * kWavesPerBlock) * kSlots + p;
+    if (c < CH8) {
+      float d = 0.f;
+      d = dot_word8_f32(R.w[i].x, xr[c], d);
+      d = dot_word8_f32(R.w[i].y, xr[CH8 + c], d);
+      d = dot_word8_f32(R.w[i].z, xr[2 * CH8 + c], d);
+      d = dot_word8_f32(R.w[i].w, xr[3 * CH8 + c], d);
+      acc = fmaf(half_to_f32(R.sb[i] & 0xffffu), d, acc);
+      acc = fmaf(half_to_f32(R.sb[i] >> 16), xh[c], acc);
+    }
+  }
+  return acc;
+}
+// Sum the 4 waves' row partials: returns the logit in threads 0..7.
+__device__ float router_finish(float acc, float* red) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  acc = rowblock_sum(acc);
+  if ((lane >> 3) == 0) red[wave * 8 + (lane & 7)] = acc;
+  __syncthreads();
+  float s = 0.f;
+  if (threadIdx.x < 8)
+    for (int w = 0; w < kWavesPerBlock; ++w) s += red[w * 8 + threadIdx.x];
+  __syncthreads();
+  return s;
+}
+
+// One token's logits for rows [row0, row0+8) (threads 0..7 hold them).
+// H8C: H/16 when known at compile time (0: runtime).
+template <int H8C>
+__device__ float router_token(const DevQ& Wr, int row0, int E, int H_rt, const uint16_t* x,
+                              const uint16_t* gamma, float eps, float4* xr, float* xh, float* red) {
+  constexpr int SR = H8C ? cdiv(cdiv(H8C, kSlots), kWavesPerBlock) : kSR;
+  const int H = H8C ? H8C * 16 : H_rt;
+  const int nsteps = cdiv(H / 16, kSlots);
+  XRegs X;
+  x_load(X, x, H);
+  float acc = 0.f;
+  {
+    RRegs<SR> R;
+    router_load<SR>(R, Wr, row0, E, H, 0);
+    float inv = gamma ? x_inv_rms(X, x, H, eps, red) : 1.f;
+    x_stage<false>(X, x, gamma, inv, H, xr, xh);
+    __syncthreads();
+    acc = router_compute<SR>(R, H, 0, xr, xh, acc);
+  }
+  if (!H8C) {
+    for (int s0 = SR * kWavesPerBlock; s0 < nsteps; s0 += SR * kWavesPerBlock) {
+      RRegs<SR> R;
+      router_load<SR>(R, Wr, row0, E, H, s0);
+      acc = router_compute<SR>(R, H, s0, xr, xh, acc);
+    }
+  }
+  return router_finish(acc, red);
+}
+
+// Standalone router for T tokens: grid (ceil(E/8), ceil(T/kTokTile)); the
+// last row-block of a token tile (per-tile counter) runs top-k.
+constexpr int kTokTile = 8;
+template <int H8C>
+__global__ __launch_bounds__(kBlock) void k_router(DevQ Wr, const float* lbias, const uint16_t* x,
+                                                   int T, int E, int H, int K, int32_t* idx,
+                                                   float* w, float* logits_out, float* logits_ws,
+                                                   uint32_t* ctlw) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint32_t* sys = reinterpret_cast<uint32_t*>(smem);
+  float4* xr = reinterpret_cast<float4*>(smem + kSysBytes);
+  float* xh = reinterpret_cast<float*>(smem + kSysBytes + (size_t)H * 4);
+  float* red = reinterpret_cast<float*>(sys + kSysRed);
+  const int row0 = blockIdx.x * kRowsPerUnit;
+  const int t0 = blockIdx.y * kTokTile, t1 = min(T, t0 + kTokTile);
+  for (int t = t0; t < t1; ++t) {
+    float s = router_token<H8C>(Wr, row0, E, H, x + (size_t)t * H, nullptr, 0.f, xr, xh, red);
+    if (threadIdx.x < 8 && row0 + (int)threadIdx.x < E) {
+      int e = row0 + threadIdx.x;
+      if (lbias) s += lbias[e];
+      st_dev(logits_ws + (size_t)t * E + e, s);
+      if (logits_out) logits_out[(size_t)t * E + e] = s;
+    }
+  }
+  wait_vm();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t* cnt = ctlw + ctl::kCntRouterTile + 16 * blockIdx.y;
+    uint32_t prev = add_dev(cnt, 1u);
+    sys[kSysOk] = prev == gridDim.x - 1;
+    if (prev == gridDim.x - 1) st_dev(cnt, 0u);
+  }
+  __syncthreads();
+  if (!sys[kSysOk]) return;
+  const int wave = threadIdx.x >> 6;
+  int32_t* idx_s = reinterpret_cast<int32_t*>(sys + kSysTkIdx) + wave * 8;
+  float* w_s = reinterpret_cast<float*>(sys + kSysTkW) + wave * 8;
+  for (int t = t0 + wave; t < t1; t += kWavesPerBlock)
+    wave_topk(logits_ws + (size_t)t * E, true, E, K, idx_s, w_s, idx + (size_t)t * K,
+              w + (size_t)t * K);
+}
+
+// ========================================================= MoE FFN step
+template <int HC>
+__device__ void role_router(const DecodeArgs& a, int b, uint8_t* smem, uint32_t epoch) {
+  uint32_t* sys = reinterpret_cast<uint32_t*>(smem);
+  const int H = HC ? HC : a.H;
+  float4* xr = reinterpret_cast<float4*>(smem + kSysBytes);
+  float* xh = reinterpret_cast<float*>(smem + kSysBytes + (size_t)H * 4);
+  float* red = reinterpret_cast<float*>(sys + kSysRed);
+  uint32_t* ctlw = ctl_of(a);
+  const int row0 = b * kRowsPerUnit;
+  float s = router_token<HC / 16>(a.router, row0, a.E, H, a.x, a.gamma, a.eps, xr, xh, red);
+  if (threadIdx.x < 8 && row0 + (int)threadIdx.x < a.E) {
+    int e = row0 + threadIdx.x;
+    if (a.lbias) s += a.lbias[e];
+    st_dev(logits_of(a) + e, s);
+  }
+  wait_vm();
+  __syncthreads();
+  if (threadIdx.x == 0) st_dev(ctlw + ctl::kFlagR + b, epoch);
+}
+
+// Gate/up of 4 row-blocks (one per wave).  expert_rank < 0: shared expert.
+template <int HC>
+__device__ void role_gate_up(const DecodeArgs& a, int expert_rank, int rb0, int rows,
+                             uint8_t* smem, uint32_t epoch) {
+  uint32_t* sys = reinterpret_cast<uint32_t*>(smem);
+  const int H = HC ? HC : a.H;
+  uint4* xs = reinterpret_cast<uint4*>(smem + kSysBytes);
+  float* xh = reinterpret_cast<float*>(smem + gu_xh_off(H));
+  float* red = reinterpret_cast<float*>(sys + kSysRed);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t* sbl = reinterpret_cast<uint32_t*>(smem + gu_sb_off(H)) + wave * gu_sb_words(H);
+  const int row0 = (rb0 + wave) * kRowsPerUnit;
+  XRegs X;
+  x_load(X, a.x, H);
+  DevQ m[2];
+  float* dst;
+  float acc[2];
+  if (expert_rank < 0) {
+    m[0] = a.shg;
+    m[1] = a.shu;
+    dst = a_sh_of(a);
+    rows4_run<2, HC / 32>(m, row0, rows, H, xs, xh, sbl,
+                          [&] {
+                            float inv = a.gamma ? x_inv_rms(X, a.x, H, a.eps, red) : 1.f;
+                            x_stage<true>(X, a.x, a.gamma, inv, H, xs, xh);
+                            __syncthreads();
+                          },
+                          acc);
+  } else {
+    // stage h while the router finishes, then resolve the expert
+    float inv = a.gamma ? x_inv_rms(X, a.x, H, a.eps, red) : 1.f;
+    x_stage<true>(X, a.x, a.gamma, inv, H, xs, xh);
+    __syncthreads();
+    if (!block_routing(a, epoch, sys, false)) return;
+    int e = reinterpret_cast<int32_t*>(sys + kSysIdx)[expert_rank];
+    int s = a.slot ? a.slot[e] : e;
+    m[0] = devq_at(a.gate, s);
+    m[1] = devq_at(a.up, s);
+    dst = a_rt_of(a) + (size_t)expert_rank * a.I;
+    rows4_run<2, HC / 32>(m, row0, rows, H, xs, xh, sbl, [] {}, acc);
+  }
+  const int row = row0 + (lane & 7);
+  if ((lane >> 3) == 0 && row < rows) st_dev(dst + row, gelu_tanh(acc[0]) * acc[1]);
+}
+
+// fp32 activations a[n] (device-coherent reads) -> even/odd LDS layout:
+// as[(2j+e)*CH + c], ah[c] = chunk sums.  `nthr` threads starting at `t`.
+__device__ __forceinline__ void stage_a(const float* a, int n, float4* as, float* ah, int t,
+                                        int nthr) {
+  const int CH = n / 32, Wn = n / 8;
+  for (int v0 = 0; v0 < Wn; v0 += nthr) {
+    int v = v0 + t;
+    bool ok = v < Wn;
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = ok ? ld_dev(a + 8 * v + i) : 0.f;
+    float s = ((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7]));
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    if (ok) {
+      int c = v >> 2, j = v & 3;
+      as[(2 * j) * CH + c] = make_float4(f[0], f[2], f[4], f[6]);
+      as[(2 * j + 1) * CH + c] = make_float4(f[1], f[3], f[5], f[7]);
+      if (j == 0) ah[c] = s;
+    }
+  }
+}
+
+// One down task: chunk c of a row of a 4-bit matrix against staged fp32
+// activations; returns s*sum(q a) + b*sum(a).
+__device__ __forceinline__ float down_chunk(uint4 w, uint32_t sb, const float4* as, const float* ah,
+                                            int CH, int c) {
+  float a0 = 0.f, a1 = 0.f;
+  dot_word4_f32(w.x, as[c], as[CH + c], a0, a1);
+  dot_word4_f32(w.y, as[2 * CH + c], as[3 * CH + c], a0, a1);
+  dot_word4_f32(w.z, as[4 * CH + c], as[5 * CH + c], a0, a1);
+  dot_word4_f32(w.w, as[6 * CH + c], as[7 * CH + c], a0, a1);
+  // the fp8 conversion gave q * 2^-9: fold 2^9 into the scale
+  return fmaf(512.0f * half_to_f32(sb & 0xffffu), a0 + a1, half_to_f32(sb >> 16) * ah[c]);
+}
+
+// Down projections + combine for output rows [8b, 8b+8).
+// IC/ISC: expert and shared intermediate sizes when known (0: runtime).
+template <int IC, int ISC>
+__device__ void role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t epoch) {
+  uint32_t* sys = reinterpret_cast<uint32_t*>(smem);
+  const int K = a.K;
+  const int I = IC ? IC : a.I, Is = ISC ? ISC : a.Is;
+  const int CHk = I / 32, CHs = Is / 32, Gk = I / 64, Gs = Is / 64;
+  const int Sk = cdiv(CHk, kSlots);
+  constexpr int MS = ISC ? cdiv(cdiv(ISC / 32, kSlots), kWavesPerBlock) : kMS;
+  constexpr int MR = IC ? cdiv(IC / 32, kSlots) : kMR;
+  float4* as_sh = reinterpret_cast<float4*>(smem + kSysBytes);
+  float* ah_sh = reinterpret_cast<float*>(as_sh + Is / 4);
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 7, p = lane >> 3;
+  float4* as_w = reinterpret_cast<float4*>(smem + down_w_off(Is) + (size_t)wave * down_w_stride(I));
+  float* ah_w = reinterpret_cast<float*>(as_w + I / 4);
+  float* red = reinterpret_cast<float*>(sys + kSysRed);
+  uint32_t* ctlw = ctl_of(a);
+  const int row = b * kRowsPerUnit + r;  // H is a multiple of 64: always valid
+
+  // 1. shared-down weights: wave w takes steps w, w+4, ...
+  uint4 wsh[MS];
+  uint32_t ssh[MS];
+#pragma unroll
+  for (int m = 0; m < MS; ++m) {
+    int c = min((wave + m * kWavesPerBlock) * kSlots + p, CHs - 1);
+    wsh[m] = ldg16(a.shd.q + ((int64_t)row * CHs + c) * 16);
+    ssh[m] = ld_sb(a.shd.s, a.shd.b, (int64_t)row * Gs + (c >> 1));
+  }
+  // 2. shared activations once the S groups are published
+  if (!block_wait_flags(ctlw + ctl::kFlagS, cdiv(a.nS, ctl::kGroup), epoch, ctlw, 2, sys)) return;
+  stage_a(a_sh_of(a), Is, as_sh, ah_sh, threadIdx.x, kBlock);
+  __syncthreads();
+  float acc = 0.f;
+#pragma unroll
+  for (int m = 0; m < MS; ++m) {
+    int c = (wave + m * kWavesPerBlock) * kSlots + p;
+    if (c < CHs) acc += down_chunk(wsh[m], ssh[m], as_sh, ah_sh, CHs, c);
+  }
+  // 3. routing, then the routed-down weights of this wave's experts (k, k+4)
+  if (!block_routing(a, epoch, sys, b == 0)) return;
+  const int32_t* idx_s = reinterpret_cast<const int32_t*>(sys + kSysIdx);
+  const float* w_s = reinterpret_cast<const float*>(sys + kSysW);
+  uint4 wrt[2][MR];
+  uint32_t srt[2][MR];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    int k = min(wave + j * kWavesPerBlock, K - 1);
+    int e = idx_s[k];
+    DevQ d = devq_at(a.down, a.slot ? a.slot[e] : e);
+#pragma unroll
+    for (int i = 0; i < MR; ++i) {
+      int c = min(min(i, Sk - 1) * kSlots + p, CHk - 1);
+      wrt[j][i] = ldg16(d.q + ((int64_t)row * CHk + c) * 16);
+      srt[j][i] = ld_sb(d.s, d.b, (int64_t)row * Gk + (c >> 1));
+    }
+  }
+  // 4. each wave: its experts in turn, as soon as their G groups are done
+  const int nGg = cdiv(a.perG, ctl::kGroup);
+  bool ok = true;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    int k = wave + j * kWavesPerBlock;
+    if (k < K && ok) {
+      ok = wave_wait_flags(ctlw + ctl::kFlagG + k * ctl::kMaxGGroups, nGg, epoch, ctlw, 3);
+      if (ok) {
+        stage_a(a_rt_of(a) + (size_t)k * I, I, as_w, ah_w, lane, 64);
+        float part = 0.f;
+#pragma unroll
+        for (int i = 0; i < MR; ++i) {
+          int c = i * kSlots + p;
+          if (i < Sk && c < CHk) part += down_chunk(wrt[j][i], srt[j][i], as_w, ah_w, CHk, c);
+        }
+        acc = fmaf(w_s[k], part, acc);
+      }
+    }
+  }
+  // 5. combine: row sums, then the 4 waves in order, residual, bf16
+  acc = rowblock_sum(acc);
+  __syncthreads();
+  if (p == 0) red[wave * 8 + r] = acc;
+  __syncthreads();
+  if (threadIdx.x < 8) {
+    int rr = b * kRowsPerUnit + threadIdx.x;
+    float s = 0.f;
+    for (int w = 0; w < kWavesPerBlock; ++w) s += red[w * 8 + threadIdx.x];
+    if (a.residual) s += bf16_to_f32(a.residual[rr]);
+    a.out[rr] = f32_to_bf16(s);
+  }
+}
+
+// Called by every D block at its end: the last one (over all D blocks, via
+// counters of at most 16 arrivals) advances the epoch.  Every other block has
+// read the epoch before publishing anything a D block waited for.
+__device__ void d_finish(const DecodeArgs& a, int b) {
+  __syncthreads();
+  if (threadIdx.x != 0) return;
+  uint32_t* ctlw = ctl_of(a);
+  const int grp = b / ctl::kGroup;
+  const int ngrp = cdiv(a.nD, ctl::kGroup);
+  const uint32_t size = (uint32_t)min(ctl::kGroup, a.nD - grp * ctl::kGroup);
+  uint32_t* cnt = ctlw + ctl::kCntD + 16 * grp;
+  if (add_dev(cnt, 1u) != size - 1) return;
+  st_dev(cnt, 0u);
+  uint32_t* top = ctlw + ctl::kCntTop;
+  if (add_dev(top, 1u) != (uint32_t)ngrp - 1) return;
+  st_dev(top, 0u);
+  st_dev(ctlw + ctl::kEpoch, ld_dev(ctlw + ctl::kEpoch) + 1u);
+}
+
+template <int HC, int IC, int ISC>
+__global__ __launch_bounds__(kBlock) void k_moe_step(DecodeArgs a) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint32_t* sys = reinterpret_cast<uint32_t*>(smem);
+  uint32_t* ctlw = ctl_of(a);
+  const uint32_t epoch = block_epoch(ctlw, sys);
+  const int rb = a.role0 + blockIdx.x;
+  if (rb < a.nR) {
+    role_router<HC>(a, rb, smem, epoch);
+  } else if (rb < a.nR + a.nS) {
+    const int s = rb - a.nR;
+    role_gate_up<HC>(a, -1, s * kWavesPerBlock, ISC ? ISC : a.Is, smem, epoch);
+    const int g = s / ctl::kGroup;
+    block_publish(ctlw + ctl::kCntS + 16 * g, ctlw + ctl::kFlagS + g,
+                  (uint32_t)min(ctl::kGroup, a.nS - g * ctl::kGroup), epoch);
+  } else if (rb < a.nR + a.nS + a.nG) {
+    const int gb = rb - a.nR - a.nS;
+    const int k = gb / a.perG, i = gb % a.perG, g = i / ctl::kGroup;
+    role_gate_up<HC>(a, k, i * kWavesPerBlock, IC ? IC : a.I, smem, epoch);
+    block_publish(ctlw + ctl::kCntG + 16 * (k * ctl::kMaxGGroups + g),
+                  ctlw + ctl::kFlagG + k * ctl::kMaxGGroups + g,
+                  (uint32_t)min(ctl::kGroup, a.perG - g * ctl::kGroup), epoch);
+  } else {
+    const int b = rb - a.nR - a.nS - a.nG;
+    role_down<IC, ISC>(a, b, smem, epoch);
+    d_finish(a, b);
+  }
+}
+
+// ======================================================== host launchers
+static hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+qmoe_status launch_gemv4(const qmoe_qtensor& W, const uint16_t* x, float* y, void* stream) {
+  const int units = cdiv(W.rows, kRowsPerUnit);
+  const int blocks = cdiv(units, kWavesPerBlock);
+  const size_t lds = gu_lds(W.cols);
+  const DevQ d = devq(W);
+  switch (W.cols / 32) {
+    case 88: hipLaunchKernelGGL(k_gemv4<88>, dim3(blocks), dim3(kBlock), lds, S(stream), d, W.rows, W.cols, x, y); break;
+    case 66: hipLaunchKernelGGL(k_gemv4<66>, dim3(blocks), dim3(kBlock), lds, S(stream), d, W.rows, W.cols, x, y); break;
+    case 22: hipLaunchKernelGGL(k_gemv4<22>, dim3(blocks), dim3(kBlock), lds, S(stream), d, W.rows, W.cols, x, y); break;
+    case 16: hipLaunchKernelGGL(k_gemv4<16>, dim3(blocks), dim3(kBlock), lds, S(stream), d, W.rows, W.cols, x, y); break;
+    default: hipLaunchKernelGGL(k_gemv4<0>, dim3(blocks), dim3(kBlock), lds, S(stream), d, W.rows, W.cols, x, y); break;
+  }
+  return hipGetLastError() == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
+}
+
+qmoe_status launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int T, int H,
+                           uint16_t* out, void* stream) {
+  hipLaunchKernelGGL(k_rmsnorm, dim3(T), dim3(kBlock), 0, S(stream), x, gamma, eps, H, out);
+  return hipGetLastError() == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
+}
+
+qmoe_status launch_router(const qmoe_qtensor& Wr, const float* lbias, const uint16_t* x, int T,
+                          int K, int32_t* idx, float* w, float* logits, uint8_t* ws,
+                          void* stream) {
+  const int E = Wr.rows, H = Wr.cols;
+  WsLayout wl = ws_layout(E, K, 0, 0, T);
+  dim3 grid(cdiv(E, kRowsPerUnit), cdiv(T, kTokTile));
+  float* lw = reinterpret_cast<float*>(ws + wl.logits);
+  uint32_t* c = reinterpret_cast<uint32_t*>(ws + wl.ctl);
+  if (H == 2816)
+    hipLaunchKernelGGL(k_router<176>, grid, dim3(kBlock), router_lds(H), S(stream), devq(Wr), lbias,
+                       x, T, E, H, K, idx, w, logits, lw, c);
+  else
+    hipLaunchKernelGGL(k_router<0>, grid, dim3(kBlock), router_lds(H), S(stream), devq(Wr), lbias,
+                       x, T, E, H, K, idx, w, logits, lw, c);
+  return hipGetLastError() == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
+}
+
+bool moe_step_supported(const qmoe_moe_layer& L) {
+  const int Ss = cdiv(L.shared_inter / 32, kSlots), Sk = cdiv(L.inter / 32, kSlots);
+  const int nR = cdiv(L.n_experts, kRowsPerUnit);
+  const int perG = cdiv(L.inter / kRowsPerUnit, kWavesPerBlock);
+  const int nS = cdiv(L.shared_inter / kRowsPerUnit, kWavesPerBlock);
+  const int nD = L.hidden / kRowsPerUnit;
+  return Ss <= kMS * kWavesPerBlock && Sk <= kMR && L.hidden / 8 <= kMaxXW * kBlock && nR <= 64 &&
+         cdiv(nS, ctl::kGroup) <= 32 && cdiv(perG, ctl::kGroup) <= ctl::kMaxGGroups &&
+         cdiv(nD, ctl::kGroup) <= 256;
+}
+
+template <int HC, int IC, int ISC>
+static void launch_step_kernel(const DecodeArgs& a, int blocks, size_t lds, void* stream) {
+  hipLaunchKernelGGL((k_moe_step<HC, IC, ISC>), dim3(blocks), dim3(kBlock), lds, S(stream), a);
+}
+
+static void launch_step(const DecodeArgs& a, int blocks, size_t lds, void* stream) {
+  if (a.H == 2816 && a.I == 704 && a.Is == 2112)
+    launch_step_kernel<2816, 704, 2112>(a, blocks, lds, stream);
+  else if (a.H == 512 && a.I == 256 && a.Is == 512)
+    launch_step_kernel<512, 256, 512>(a, blocks, lds, stream);
+  else
+    launch_step_kernel<0, 0, 0>(a, blocks, lds, stream);
+}
+
+// phased: 0 = one launch with in-kernel waits; 1 = three ordered launches
+qmoe_status launch_moe_step(const qmoe_moe_layer& L, const uint16_t* x, const int32_t* idx_in,
+                            const float* w_in, const int32_t* slot, const uint16_t* residual,
+                            uint16_t* out, int32_t* idx_out, float* w_out, uint8_t* ws, int phased,
+                            void* stream) {
+  if (!moe_step_supported(L)) return QMOE_ERR_UNSUPPORTED;
+  DecodeArgs a;
+  a.H = L.hidden; a.E = L.n_experts; a.K = L.top_k; a.I = L.inter; a.Is = L.shared_inter;
+  a.router = devq(L.router); a.gate = devq(L.gate); a.up = devq(L.up); a.down = devq(L.down);
+  a.shg = devq(L.sh_gate); a.shu = devq(L.sh_up); a.shd = devq(L.sh_down);
+  a.x = x;
+  a.gamma = idx_in ? nullptr : L.rms_gamma;
+  a.eps = L.rms_eps;
+  a.lbias = L.logit_bias;
+  a.idx_in = idx_in; a.w_in = w_in; a.slot = slot; a.residual = residual;
+  a.out = out; a.idx_out = idx_out; a.w_out = w_out;
+  a.ws = ws;
+  a.wl = ws_layout(a.E, a.K, a.I, a.Is, 1);
+  a.nR = idx_in ? 0 : cdiv(a.E, kRowsPerUnit);
+  a.nS = cdiv(a.Is / kRowsPerUnit, kWavesPerBlock);
+  a.perG = cdiv(a.I / kRowsPerUnit, kWavesPerBlock);
+  a.nG = a.K * a.perG;
+  a.nD = a.H / kRowsPerUnit;
+  size_t lds = gu_lds(a.H);
+  if (router_lds(a.H) > lds) lds = router_lds(a.H);
+  if (down_lds(a.I, a.Is) > lds) lds = down_lds(a.I, a.Is);
+  if (!phased) {
+    a.role0 = 0;
+    launch_step(a, a.nR + a.nS + a.nG + a.nD, lds, stream);
+    return hipGetLastError() == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
+  }
+  // router; shared + routed gate/up; down (waits are then satisfied on entry)
+  if (a.nR) {
+    a.role0 = 0;
+    launch_step(a, a.nR, lds, stream);
+  }
+  a.role0 = a.nR;
+  launch_step(a, a.nS + a.nG, lds, stream);
+  a.role0 = a.nR + a.nS + a.nG;
+  launch_step(a, a.nD, lds, stream);
+  return hipGetLastError() == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
+}
+
+}  // namespace qmoe

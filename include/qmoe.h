@@ -1,0 +1,191 @@
+/*
+ * qmoe.h -- C ABI of the MI355X (gfx950) quantized Mixture-of-Experts FFN
+ * step: 8-bit affine router with softmax top-k, 4-bit affine (MLX-style,
+ * group 64) expert GEMVs for the routed and the shared expert, router-
+ * weighted combine, and the chunked-prefill variant.
+ *
+ * What the step computes is described in words on these pages:
+ *  - devtrends.cc, "Come eseguire un modello da 26 miliardi di parametri in
+ *    due gigabyte di memoria su un Mac normale", section "Qual è il trucco
+ *    principale dell'architettura" (a router per layer selects 8 experts;
+ *    16-slot LFU expert cache; the shared branch is computed while missing
+ *    experts are read) and section "Prestazioni nel mondo reale" (128-token
+ *    prefill chunks so one loaded expert serves a group of rows);
+ *  - remio.ai, "TurboFieldfare esegue Mac Gemma 4 26B in 2 GB, ma la velocità
+ *    dell'SSD diventa il compromesso", section "L'affermazione dei 2 GB
+ *    trasforma la larghezza di banda dell'SSD nel nuovo vincolo" (4-bit MLX
+ *    affine weights, 8-bit router, shared and routed branches combined, 30
+ *    layers, prefill chunks of up to 128 tokens);
+ *  - iitog.ru, "TurboFieldfare: движок с открытым кодом запускает Gemma 4 26B
+ *    на Mac с 8 ГБ памяти", technical paragraph (quantized GEMV, MoE routing
+ *    and normalisation kernels);
+ *  - elsolitario.org, TurboFieldfare article, section "Detalles técnicos y
+ *    rendimiento" (MLX affine 4-bit, group size 64; router at 8 bits).
+ *
+ * Conventions shared by every entry point
+ *  - Tensor pointers are DEVICE pointers owned by the caller.  Structs are
+ *    host memory and are read only during the call.
+ *  - Every call is asynchronous on `stream` (a hipStream_t; NULL = the
+ *    default stream).  No entry point allocates, frees or synchronises,
+ *    except qmoe_workspace_status(), which reads back one word.
+ *  - Scratch memory comes from the caller through `ws`/`ws_bytes`, sized by
+ *    qmoe_workspace_bytes().  A workspace must be zero-filled once before its
+ *    first use; every call leaves it ready for the next one.  One workspace
+ *    serves one call at a time (calls sharing a workspace must be ordered on
+ *    one stream).
+ *  - Arguments are validated before anything is launched; on error nothing
+ *    is launched and a qmoe_status other than QMOE_OK is returned.  Device-
+ *    side faults surface at the caller's next synchronisation.  NaN/Inf
+ *    inputs give undefined (but finite-time) results.
+ *  - Numbers: bf16 and fp16 values travel as their uint16_t bit patterns.
+ *    Arithmetic is fp32 with fp32 accumulation; each layer output is rounded
+ *    to bf16 (round to nearest even) once, after the residual add.
+ */
+#ifndef QMOE_H
+#define QMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QMOE_OK = 0,
+  QMOE_ERR_NULL_ARG = 1,    /* a required pointer is NULL */
+  QMOE_ERR_BAD_SHAPE = 2,   /* inconsistent or out-of-range sizes */
+  QMOE_ERR_UNSUPPORTED = 3, /* bits/group/size outside what the kernels do */
+  QMOE_ERR_WORKSPACE = 4,   /* ws NULL or smaller than qmoe_workspace_bytes */
+  QMOE_ERR_ALIGN = 5,       /* a pointer or stride is not 16-byte aligned */
+  QMOE_ERR_HIP = 6,         /* a HIP runtime call failed */
+  QMOE_ERR_DEVICE = 7       /* the device reported a failed wait (status read) */
+} qmoe_status;
+
+/* One affine-quantized matrix W[rows][cols] (MLX-style, group 64):
+ *   W[r][c] = scale[r][c/64] * q[r][c] + bias[r][c/64]
+ * q: uint32 words, codes packed least-significant-bits first along the
+ *    column axis (8 codes per word for bits=4, 4 for bits=8), rows
+ *    contiguous: [rows][cols*bits/32].  16-byte aligned.
+ * scales, biases: fp16 bit patterns, [rows][cols/64].
+ * expert_stride_bytes: for stacked experts, expert e's q/scales/biases are
+ *    at the given pointers plus e*expert_stride_bytes (all three advance by
+ *    the same stride, which suits one contiguous blob per expert); 0 for a
+ *    single matrix.  Multiple of 16. */
+typedef struct {
+  const uint32_t* q;
+  const uint16_t* scales;
+  const uint16_t* biases;
+  int32_t rows, cols, bits, group;
+  int64_t expert_stride_bytes;
+} qmoe_qtensor;
+
+/* One MoE layer.  router: bits=8, [n_experts x hidden].  gate/up: bits=4,
+ * [inter x hidden] per expert; down: bits=4, [hidden x inter] per expert
+ * (stacked through expert_stride_bytes).  sh_gate/sh_up: [shared_inter x
+ * hidden]; sh_down: [hidden x shared_inter].
+ * rms_gamma: bf16 [hidden] RMSNorm weight applied before the router and the
+ * experts (NULL: the experts see the input as is); rms_eps its epsilon.
+ * logit_bias: fp32 [n_experts] added to the router logits (NULL: none). */
+typedef struct {
+  int32_t hidden, n_experts, top_k, inter, shared_inter;
+  qmoe_qtensor router;
+  qmoe_qtensor gate, up, down;
+  qmoe_qtensor sh_gate, sh_up, sh_down;
+  const uint16_t* rms_gamma;
+  float rms_eps;
+  const float* logit_bias;
+} qmoe_moe_layer;
+
+/* Limits of this build (checked; larger sizes give QMOE_ERR_UNSUPPORTED). */
+#define QMOE_MAX_TOP_K 8
+#define QMOE_MAX_EXPERTS 512
+#define QMOE_MAX_HIDDEN 16384
+#define QMOE_MAX_TOKENS 128
+
+/* y[r] = sum_c W[r][c] x[c] for a 4-bit affine matrix (the quantized GEMV).
+ * W: bits=4, group=64, expert_stride_bytes ignored.  x: bf16 [cols].
+ * y: fp32 [rows].  Returns QMOE_ERR_UNSUPPORTED for bits != 4. */
+qmoe_status qmoe_gemv_affine4(const qmoe_qtensor* W, const uint16_t* x, float* y,
+                              void* stream);
+
+/* Router of T tokens: logits[t][e] = sum_c Wr[e][c] x[t][c] (+ bias[e]);
+ * keep the top_k largest (ties: lower expert index first), ordered by
+ * descending logit; w[t][j] = softmax over the kept logits (equal to a full
+ * softmax renormalised over the kept experts).
+ * Wr: bits=8 [E x H].  x: bf16 [T][H].  idx: int32 [T][top_k].
+ * w: fp32 [T][top_k].  logits: fp32 [T][E] or NULL.  1 <= T <= 128,
+ * 1 <= top_k <= min(8, E).  ws: at least qmoe_router_workspace_bytes(E, T). */
+qmoe_status qmoe_router_topk(const qmoe_qtensor* Wr, const float* logit_bias,
+                             const uint16_t* x, int32_t T, int32_t top_k,
+                             int32_t* idx, float* w, float* logits, void* ws,
+                             size_t ws_bytes, void* stream);
+
+/* FFN of one token given its routing: for M in {shared, idx[0..k)}
+ *   a_M = gelu_tanh(W_gate,M h) * (W_up,M h);   y_M = W_down,M a_M
+ *   out = bf16( y_shared + sum_j w[j] y_idx[j]  (+ residual) )
+ * h: bf16 [H] (the expert input, already normalised if the model norms).
+ * idx: int32 [top_k] device; w: fp32 [top_k] device.
+ * expert_slot: int32 [n_experts] device map expert -> position in the
+ *   stacked routed tensors, or NULL for the identity.
+ * residual: bf16 [H] or NULL.  out: bf16 [H]. */
+qmoe_status qmoe_expert_ffn(const qmoe_moe_layer* L, const uint16_t* h,
+                            const int32_t* idx, const float* w,
+                            const int32_t* expert_slot, const uint16_t* residual,
+                            uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+
+/* One whole decode step of one layer for one token, in a single launch:
+ *   h = L->rms_gamma ? bf16(rmsnorm(x) * gamma) : x
+ *   routing = top-k softmax of the router on h (+ logit_bias)
+ *   out = bf16( FFN combine as in qmoe_expert_ffn  (+ x if residual) )
+ * x: bf16 [H].  idx_out/w_out: optional copies of the routing (device,
+ * [top_k]).  expert_slot as in qmoe_expert_ffn. */
+qmoe_status qmoe_moe_decode(const qmoe_moe_layer* L, const uint16_t* x,
+                            const int32_t* expert_slot, int32_t residual,
+                            uint16_t* out, int32_t* idx_out, float* w_out,
+                            void* ws, size_t ws_bytes, void* stream);
+
+/* The same step as qmoe_moe_decode, run as three ordered launches (router;
+ * shared and routed gate/up; down and combine) instead of one launch whose
+ * blocks wait on each other.  Same kernels and arithmetic, so the results
+ * are bitwise equal; kept for diagnosis and for comparing launch overheads. */
+qmoe_status qmoe_moe_decode_phased(const qmoe_moe_layer* L, const uint16_t* x,
+                                   const int32_t* expert_slot, int32_t residual,
+                                   uint16_t* out, int32_t* idx_out, float* w_out,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/* Chunked prefill of T <= 128 tokens that share one loaded copy of each
+ * expert: the (token, rank) pairs are grouped by expert (stable: expert,
+ * then token, then rank) and every expert runs one grouped dequantizing
+ * GEMM over its rows on the matrix cores; the shared expert runs as a dense
+ * GEMM over all T rows; then
+ *   out[t] = bf16( y_shared[t] + sum_j w[t][j] y_idx[t][j][t]  (+ residual[t]) )
+ * X: bf16 [T][H] (expert input).  idx/w: [T][top_k] device (from
+ * qmoe_router_topk).  residual: bf16 [T][H] or NULL.  out: bf16 [T][H]. */
+qmoe_status qmoe_prefill_grouped(const qmoe_moe_layer* L, const uint16_t* X,
+                                 int32_t T, const int32_t* idx, const float* w,
+                                 const uint16_t* residual, uint16_t* out,
+                                 void* ws, size_t ws_bytes, void* stream);
+
+/* out[t][i] = bf16( x[t][i] * gamma[i] / sqrt(mean_i x[t][i]^2 + eps) ).
+ * x, out: bf16 [T][H]; gamma: bf16 [H]. */
+qmoe_status qmoe_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps,
+                         int32_t T, int32_t H, uint16_t* out, void* stream);
+
+/* Workspace sizes in bytes (0 when the layer description is invalid). */
+size_t qmoe_workspace_bytes(const qmoe_moe_layer* L, int32_t T);
+size_t qmoe_router_workspace_bytes(int32_t n_experts, int32_t T);
+
+/* Reads (synchronising `stream`) and clears the device error word of a
+ * workspace.  *device_code receives 0 when every in-kernel wait completed,
+ * nonzero when one gave up (the outputs of that call are then undefined).
+ * Returns QMOE_OK, QMOE_ERR_DEVICE when the word was nonzero, or an error. */
+qmoe_status qmoe_workspace_status(void* ws, size_t ws_bytes, int32_t* device_code,
+                                  void* stream);
+
+const char* qmoe_status_string(qmoe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QMOE_H */
