@@ -142,8 +142,24 @@ __device__ __forceinline__ void st_dev(uint32_t* p, uint32_t v) {
 __device__ __forceinline__ uint32_t ld_dev(const uint32_t* p) {
   return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+__device__ __forceinline__ void st_dev(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 __device__ __forceinline__ uint32_t add_dev(uint32_t* p, uint32_t v) {
   return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// 16-byte device-coherent load (buffer load with the sc1 bit) of
+// base[byte_off .. byte_off+16); `base` must be wave-uniform, reads past
+// `nbytes` return zeros.
+__device__ __forceinline__ float4 ld_dev16(const float* base, uint32_t nbytes, uint32_t byte_off) {
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(base), 0, (int)nbytes, 0x00020000);
+  v4i v = __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 16 /* sc1 */);
+  return __builtin_bit_cast(float4, v);
 }
 // Wait until every vector memory operation of this wave has completed.
 __device__ __forceinline__ void wait_vm() {
@@ -179,32 +195,35 @@ __device__ __forceinline__ DevQ devq_at(DevQ d, int64_t slot) {
 }
 
 // ----------------------------------------------------------- workspace
-// Control area (uint32 words).  Flags are packed so one wave polls many with
-// one load; counters sit on their own 64-byte lines.
+// Control area.  Small values that many blocks poll (the router's logits
+// and the per-group flags) are published in kRep replicas kRepStride bytes
+// apart, so that pollers spread over memory channels instead of all
+// hitting one line; consumer block b reads replica b % kRep.
 namespace ctl {
-constexpr int kEpoch = 0;        // last completed call's epoch
-constexpr int kError = 16;       // nonzero: an in-kernel wait gave up
-constexpr int kFlagR = 64;       // [64]  router row-block b published logits
-constexpr int kFlagS = 128;      // [32]  shared gate/up group g published
-constexpr int kFlagG = 160;      // [8*32] routed expert k group g published
-constexpr int kCntS = 512;       // counters, stride 16 words
-constexpr int kCntG = kCntS + 16 * 32;
-constexpr int kCntD = kCntG + 16 * 256;
-constexpr int kCntTop = kCntD + 16 * 256;
-constexpr int kCntRouterTile = kCntTop + 16;  // standalone router: per token tile
-constexpr int kWords = kCntRouterTile + 16 * 16;
-constexpr int kGroup = 16;       // producer blocks per counter
-constexpr int kMaxGGroups = 32;  // groups per expert
+constexpr int kError = 0;             // word: nonzero when an in-kernel wait gave up
+constexpr int kRep = 16;
+constexpr int kRepStride = 4352;      // bytes between replicas (4 KiB + 256)
+constexpr int kTagBase = 4096;        // byte offset of the tagged-logit replicas
+constexpr int kFlagBase = kTagBase + kRep * kRepStride;   // per-block flag replicas:
+                                      // words [0, nS) shared gate/up blocks, then
+                                      // [nS + k*perG + i) routed expert k block i
+constexpr int kMaxFlags = kRepStride / 4;
+constexpr int kCntBase = kFlagBase + kRep * kRepStride;   // counters, 64 B apart
+constexpr int kCntRouterTile = 0;     // [16] standalone router: per token tile
+constexpr int kNCnt = kCntRouterTile + 16;
+constexpr int kBytes = kCntBase + kNCnt * 64;
 }  // namespace ctl
-constexpr size_t kCtlBytes = (size_t)ctl::kWords * 4;
+constexpr size_t kCtlBytes = (size_t)ctl::kBytes;
 
 __host__ __device__ inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 struct WsLayout {
-  size_t ctl, logits, idx, w, a_sh, a_rt, pf, total;
+  size_t ctl, logits, idx, w, act, act_stride, pf, total;
 };
 
-// Decode/FFN/router workspace for T tokens.  Prefill extras start at `pf`.
+// Decode/FFN/router workspace for T tokens.  The gate/up activations of a
+// decode step (shared [Is] then routed [K][I], fp32) are published in
+// ctl::kRep replicas act_stride bytes apart.  Prefill extras start at `pf`.
 __host__ __device__ inline WsLayout ws_layout(int E, int K, int I, int Is, int T) {
   WsLayout L;
   size_t o = 0;
@@ -212,8 +231,8 @@ __host__ __device__ inline WsLayout ws_layout(int E, int K, int I, int Is, int T
   L.logits = o; o += align256((size_t)T * E * 4);
   L.idx = o; o += align256((size_t)T * K * 4);
   L.w = o; o += align256((size_t)T * K * 4);
-  L.a_sh = o; o += align256((size_t)Is * 4);
-  L.a_rt = o; o += align256((size_t)K * I * 4);
+  L.act_stride = align256(((size_t)Is + (size_t)K * I) * 4) + 256;
+  L.act = o; o += L.act_stride * ctl::kRep;
   L.pf = o;
   L.total = o;
   return L;

@@ -50,6 +50,10 @@ constexpr int kMS = 6;           // shared-down steps per wave (runtime shapes)
 constexpr int kMR = 4;           // routed-down steps per expert (runtime shapes)
 constexpr int kSR = 8;           // router steps per wave per pass (runtime shapes)
 constexpr uint64_t kWaitTicks = 20000000ull;  // 0.2 s of the 100 MHz clock
+// Blocks whose first weight loads are not on the critical path hold them
+// back this long (100 MHz ticks), so the router's loads reach the memory
+// queues first.
+constexpr uint64_t kHoldTicks = 0;
 
 // LDS "sys" words at the start of every block's LDS
 constexpr int kSysEpoch = 0, kSysOk = 1, kSysIdx = 8, kSysW = 16, kSysRed = 32;
@@ -79,30 +83,50 @@ struct DecodeArgs {
   int nR, nS, nG, nD;       // role sizes in blocks
   int perG;                 // G blocks per expert
   int role0;                // role index of blockIdx.x == 0
+  int nowait;               // 1: producers ran in earlier launches (no waits)
 };
 
 __device__ __forceinline__ uint32_t* ctl_of(const DecodeArgs& a) {
   return reinterpret_cast<uint32_t*>(a.ws + a.wl.ctl);
 }
+// Replica `r` of a published area at byte offset `base` of the control area.
+__device__ __forceinline__ uint8_t* rep_of(const DecodeArgs& a, int base, int r) {
+  return a.ws + a.wl.ctl + base + (size_t)r * ctl::kRepStride;
+}
 __device__ __forceinline__ float* logits_of(const DecodeArgs& a) {
   return reinterpret_cast<float*>(a.ws + a.wl.logits);
 }
-__device__ __forceinline__ float* a_sh_of(const DecodeArgs& a) {
-  return reinterpret_cast<float*>(a.ws + a.wl.a_sh);
-}
-__device__ __forceinline__ float* a_rt_of(const DecodeArgs& a) {
-  return reinterpret_cast<float*>(a.ws + a.wl.a_rt);
+// Replica r of the activations: shared [Is], then routed [K][I].
+__device__ __forceinline__ float* act_of(const DecodeArgs& a, int r) {
+  return reinterpret_cast<float*>(a.ws + a.wl.act + (size_t)r * a.wl.act_stride);
 }
 
 // --------------------------------------------------------------- waits
-// One full wave: wait until flags[0..n) all equal `epoch` (n <= 64).
+// The epoch of this call: every launch is a new packet of its queue, so the
+// packet's address differs from the previous launch's and is the same for
+// all of the launch's blocks.  Every flag and tag is rewritten by every
+// call, so only the previous call's values can be present when one starts.
+__device__ __forceinline__ uint32_t launch_epoch() {
+  uint32_t e = (uint32_t)(reinterpret_cast<uintptr_t>(__builtin_amdgcn_dispatch_ptr()) >> 6);
+  return e ? e : 0x80000000u;
+}
+
+// One full wave: wait until flags[0..n) all equal `epoch`.  Polling reads
+// one sentinel (the flag of the last producer, which is usually the last to
+// be raised) until it is set and only then checks all of them, so that
+// waiting blocks add almost no memory traffic.
+constexpr int kPollSleep = 6;  // s_sleep units (64 cycles) between polls
 __device__ bool wave_wait_flags(const uint32_t* flags, int n, uint32_t epoch, uint32_t* ctlw,
                                 uint32_t code) {
   const int lane = threadIdx.x & 63;
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   for (int it = 0;; ++it) {
-    bool ok = lane >= n || ld_dev(flags + lane) == epoch;
-    if (__all(ok)) return true;
+    uint32_t sent = __builtin_amdgcn_readfirstlane(ld_dev(flags + n - 1));
+    if (sent == epoch) {
+      bool ok = true;
+      for (int i = lane; i < n; i += 64) ok = ok && ld_dev(flags + i) == epoch;
+      if (__all(ok)) return true;
+    }
     if ((it & 15) == 15) {
       if (ld_dev(ctlw + ctl::kError) != 0) return false;
       if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
@@ -110,8 +134,13 @@ __device__ bool wave_wait_flags(const uint32_t* flags, int n, uint32_t epoch, ui
         return false;
       }
     }
-    __builtin_amdgcn_s_sleep(2);
+    __builtin_amdgcn_s_sleep(kPollSleep);
   }
+}
+
+// Spin until `ticks` of the constant clock have passed since `t0`.
+__device__ __forceinline__ void hold_until(uint64_t t0, uint64_t ticks) {
+  while (__builtin_amdgcn_s_memrealtime() - t0 < ticks) __builtin_amdgcn_s_sleep(1);
 }
 
 // Whole block: wave 0 waits, the others meet it at a barrier.
@@ -127,24 +156,13 @@ __device__ bool block_wait_flags(const uint32_t* flags, int n, uint32_t epoch, u
   return ok;
 }
 
-// This block's device stores are complete; count it in its group and, as
-// the last arrival, reset the counter and raise the group flag.
-__device__ void block_publish(uint32_t* cnt, uint32_t* flag, uint32_t size, uint32_t epoch) {
+// This block's device stores are complete: raise its flag (word `flag` of
+// every flag replica).
+__device__ void block_publish(const DecodeArgs& a, int flag, uint32_t epoch) {
   wait_vm();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t prev = add_dev(cnt, 1u);
-    if (prev == size - 1) {
-      st_dev(cnt, 0u);
-      st_dev(flag, epoch);
-    }
-  }
-}
-
-__device__ uint32_t block_epoch(uint32_t* ctlw, uint32_t* sys) {
-  if (threadIdx.x == 0) sys[kSysEpoch] = ld_dev(ctlw + ctl::kEpoch) + 1u;
-  __syncthreads();
-  return sys[kSysEpoch];
+  if (threadIdx.x < ctl::kRep)
+    st_dev(reinterpret_cast<uint32_t*>(rep_of(a, ctl::kFlagBase, threadIdx.x)) + flag, epoch);
 }
 
 // ------------------------------------------------------------ reductions
@@ -179,24 +197,18 @@ __device__ float block_sum(float v, float* red) {
 }
 
 // ============================================================== routing
-// One wave: top-k of logits[0..E) (descending; ties to the lower index) and
-// the softmax over the kept logits (exp(l - l_max) normalised by their sum).
-// Results go to idx_s/w_s (LDS) and, optionally, to idx2/w2.
-__device__ void wave_topk(const float* lg, bool coherent, int E, int K, int32_t* idx_s,
-                          float* w_s, int32_t* idx2, float* w2) {
+// One wave: top-k of E logits held as v[m] = logit[lane + 64 m]
+// (descending; ties to the lower index) and the softmax over the kept
+// logits (exp(l - l_max) normalised by their sum).  Results go to idx_s/w_s
+// (LDS) and, optionally, to idx2/w2.
+template <int NV>
+__device__ void wave_topk_vals(const float (&v)[NV], int E, int K, int32_t* idx_s, float* w_s,
+                               int32_t* idx2, float* w2) {
   const int lane = threadIdx.x & 63;
-  constexpr int NV = QMOE_MAX_EXPERTS / 64;
-  float v[NV];
   uint32_t live = 0;
 #pragma unroll
-  for (int m = 0; m < NV; ++m) {
-    int e = lane + 64 * m;
-    v[m] = -INFINITY;
-    if (e < E) {
-      v[m] = coherent ? ld_dev(lg + e) : lg[e];
-      live |= 1u << m;
-    }
-  }
+  for (int m = 0; m < NV; ++m)
+    if (lane + 64 * m < E) live |= 1u << m;
   float top = 0.f, sel = 0.f;
   int sel_i = 0;
   for (int j = 0; j < K; ++j) {
@@ -231,8 +243,69 @@ __device__ void wave_topk(const float* lg, bool coherent, int E, int K, int32_t*
   }
 }
 
-// Routing for a consumer block: from the caller's arrays, or wait for the
-// router blocks and run top-k on their logits.  Leaves idx/w in sys LDS.
+// Top-k of logits in memory (device-coherent reads).
+__device__ void wave_topk(const float* lg, int E, int K, int32_t* idx_s, float* w_s, int32_t* idx2,
+                          float* w2) {
+  const int lane = threadIdx.x & 63;
+  float v[QMOE_MAX_EXPERTS / 64];
+#pragma unroll
+  for (int m = 0; m < QMOE_MAX_EXPERTS / 64; ++m) {
+    int e = lane + 64 * m;
+    v[m] = e < E ? ld_dev(lg + e) : -INFINITY;
+  }
+  wave_topk_vals<QMOE_MAX_EXPERTS / 64>(v, E, K, idx_s, w_s, idx2, w2);
+}
+
+// One wave: wait until all E tagged logits of one replica carry `epoch`
+// (each is (epoch << 32) | fp32 bits, written with one 64-bit store), then
+// top-k on them.  The poll reads the last expert's tag until it is current,
+// then all of them.  In a launch that follows its producers, no waiting.
+template <int NV>
+__device__ bool wave_routing(const DecodeArgs& a, uint32_t epoch, int32_t* idx_s, float* w_s,
+                             bool write_out) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t* tag = reinterpret_cast<const uint64_t*>(
+      rep_of(a, ctl::kTagBase, blockIdx.x % ctl::kRep));
+  uint32_t* ctlw = ctl_of(a);
+  float v[NV];
+  const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  for (int it = 0;; ++it) {
+    bool ready = a.nowait;
+    if (!ready) {
+      uint64_t t = ld_dev(tag + a.E - 1);
+      ready = __builtin_amdgcn_readfirstlane((uint32_t)(t >> 32)) == epoch;
+    }
+    if (ready) {
+      bool ok = true;
+#pragma unroll
+      for (int m = 0; m < NV; ++m) {
+        int e = lane + 64 * m;
+        v[m] = -INFINITY;
+        if (e < a.E) {
+          uint64_t t = ld_dev(tag + e);
+          v[m] = __uint_as_float((uint32_t)t);
+          ok = ok && (a.nowait || (uint32_t)(t >> 32) == epoch);
+        }
+      }
+      if (__all(ok)) break;
+    }
+    if ((it & 15) == 15) {
+      if (ld_dev(ctlw + ctl::kError) != 0) return false;
+      if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+        if (lane == 0) st_dev(ctlw + ctl::kError, 1u);
+        return false;
+      }
+    }
+    __builtin_amdgcn_s_sleep(kPollSleep);
+  }
+  wave_topk_vals<NV>(v, a.E, a.K, idx_s, w_s, write_out ? a.idx_out : nullptr,
+                     write_out ? a.w_out : nullptr);
+  return true;
+}
+
+// Routing for a consumer block: from the caller's arrays, or from the
+// router blocks' published logits.  Leaves idx/w in sys LDS.
+template <int NV>
 __device__ bool block_routing(const DecodeArgs& a, uint32_t epoch, uint32_t* sys, bool write_out) {
   int32_t* idx_s = reinterpret_cast<int32_t*>(sys + kSysIdx);
   float* w_s = reinterpret_cast<float*>(sys + kSysW);
@@ -244,13 +317,14 @@ __device__ bool block_routing(const DecodeArgs& a, uint32_t epoch, uint32_t* sys
     __syncthreads();
     return true;
   }
-  uint32_t* ctlw = ctl_of(a);
-  if (!block_wait_flags(ctlw + ctl::kFlagR, a.nR, epoch, ctlw, 1, sys)) return false;
-  if (threadIdx.x < 64)
-    wave_topk(logits_of(a), true, a.E, a.K, idx_s, w_s, write_out ? a.idx_out : nullptr,
-              write_out ? a.w_out : nullptr);
+  if (threadIdx.x < 64) {
+    bool ok = wave_routing<NV>(a, epoch, idx_s, w_s, write_out);
+    if (threadIdx.x == 0) sys[kSysOk] = ok ? 1u : 0u;
+  }
   __syncthreads();
-  return true;
+  bool ok = sys[kSysOk] != 0;
+  __syncthreads();
+  return ok;
 }
 
 // -------------------------------------------------------------- staging
@@ -442,10 +516,10 @@ __device__ __forceinline__ void rows4_put_sb(const Rows4<NM, SP>& R, const DevQ 
 
 template <int NM, int SP>
 __device__ __forceinline__ void rows4_load(Rows4<NM, SP>& R, const DevQ (&m)[NM], int row,
-                                           int CH, int step0, int p) {
+                                           int CH, int c0, int CW, int step0, int p) {
 #pragma unroll
   for (int i = 0; i < SP; ++i) {
-    int c = min((step0 + i) * kSlots + p, CH - 1);
+    int c = c0 + min((step0 + i) * kSlots + p, CW - 1);
     int64_t o = ((int64_t)row * CH + c) * 16;
 #pragma unroll
     for (int k = 0; k < NM; ++k) R.w[k][i] = ldg16(m[k].q + o);
@@ -455,11 +529,13 @@ __device__ __forceinline__ void rows4_load(Rows4<NM, SP>& R, const DevQ (&m)[NM]
 template <int NM, int SP>
 __device__ __forceinline__ void rows4_compute(const Rows4<NM, SP>& R, const uint4* xs,
                                               const float* xh, const uint32_t* sbl, int r, int G,
-                                              int CH, int step0, int p, float (&acc)[NM]) {
+                                              int CH, int c0, int CW, int step0, int p,
+                                              float (&acc)[NM]) {
 #pragma unroll
   for (int i = 0; i < SP; ++i) {
-    int c = (step0 + i) * kSlots + p;
-    if (c < CH) {
+    int cl = (step0 + i) * kSlots + p;
+    if (cl < CW) {
+      int c = c0 + cl;
       uint4 x0 = xs[c], x1 = xs[CH + c], x2 = xs[2 * CH + c], x3 = xs[3 * CH + c];
       float X = xh[c];
 #pragma unroll
@@ -477,30 +553,31 @@ __device__ __forceinline__ void rows4_compute(const Rows4<NM, SP>& R, const uint
   }
 }
 
-// One wave: rows [row0, row0+8) of NM matrices of `rows` rows and H columns.
+// One wave: rows [row0, row0+8) of NM matrices of `rows` rows and H columns,
+// chunks [c0, c0+CW) of each row (CWC: CW when known at compile time).
 // `stage` runs between the first pass's loads and its math and must end
 // with a block barrier.  sbl: this wave's LDS table (NM*8*G words).
-template <int NM, int CHC, typename StageFn>
-__device__ __forceinline__ void rows4_run(const DevQ (&m)[NM], int row0, int rows, int H_rt,
-                                          const uint4* xs, const float* xh, uint32_t* sbl,
-                                          StageFn stage, float (&acc)[NM]) {
-  constexpr int SP = CHC ? cdiv(CHC, kSlots) : kSP;
-  const int CH = CHC ? CHC : H_rt / 32;
-  const int G = CH / 2, nsteps = cdiv(CH, kSlots);
+template <int NM, int CWC, typename StageFn>
+__device__ __forceinline__ void rows4_run(const DevQ (&m)[NM], int row0, int rows, int H, int c0,
+                                          int CW_rt, const uint4* xs, const float* xh,
+                                          uint32_t* sbl, StageFn stage, float (&acc)[NM]) {
+  constexpr int SP = CWC ? cdiv(CWC, kSlots) : kSP;
+  const int CW = CWC ? CWC : CW_rt;
+  const int CH = H / 32, G = CH / 2, nsteps = cdiv(CW, kSlots);
   const int lane = threadIdx.x & 63, r = lane & 7, p = lane >> 3;
   const int row = min(row0 + r, rows - 1);
   Rows4<NM, SP> R;
 #pragma unroll
   for (int k = 0; k < NM; ++k) acc[k] = 0.f;
   rows4_load_sb<NM, SP>(R, m, row0, rows, G);
-  rows4_load<NM, SP>(R, m, row, CH, 0, p);
+  rows4_load<NM, SP>(R, m, row, CH, c0, CW, 0, p);
   rows4_put_sb<NM, SP>(R, m, row0, rows, G, sbl);
   stage();
-  rows4_compute<NM, SP>(R, xs, xh, sbl, r, G, CH, 0, p, acc);
-  if (!CHC) {
+  rows4_compute<NM, SP>(R, xs, xh, sbl, r, G, CH, c0, CW, 0, p, acc);
+  if (!CWC) {
     for (int s0 = SP; s0 < nsteps; s0 += SP) {
-      rows4_load<NM, SP>(R, m, row, CH, s0, p);
-      rows4_compute<NM, SP>(R, xs, xh, sbl, r, G, CH, s0, p, acc);
+      rows4_load<NM, SP>(R, m, row, CH, c0, CW, s0, p);
+      rows4_compute<NM, SP>(R, xs, xh, sbl, r, G, CH, c0, CW, s0, p, acc);
     }
   }
 #pragma unroll
@@ -508,10 +585,10 @@ __device__ __forceinline__ void rows4_run(const DevQ (&m)[NM], int row0, int row
 }
 
 // LDS carve-ups (bytes).  Gate/up: sys | xs pairs (H*2) | xh (H/32 floats)
-// | per-wave scale tables (4 waves x NM matrices x 8 rows x H/64 words).
+// | per-wave scale tables (4 waves x 8 rows x H/64 words).
 __host__ __device__ inline size_t gu_xh_off(int H) { return kSysBytes + (size_t)H * 2; }
 __host__ __device__ inline size_t gu_sb_off(int H) { return al16(gu_xh_off(H) + (size_t)(H / 32) * 4); }
-__host__ __device__ inline size_t gu_sb_words(int H) { return (size_t)2 * kRowsPerUnit * (H / 64); }
+__host__ __device__ inline size_t gu_sb_words(int H) { return (size_t)kRowsPerUnit * (H / 64); }
 __host__ __device__ inline size_t gu_lds(int H) {
   return gu_sb_off(H) + (size_t)kWavesPerBlock * gu_sb_words(H) * 4;
 }
@@ -541,7 +618,7 @@ __global__ __launch_bounds__(kBlock) void k_gemv4(DevQ W, int rows, int cols, co
   x_load(X, x, cols);
   DevQ m[1] = {W};
   float acc[1];
-  rows4_run<1, CHC>(m, row0, rows, cols, xs, xh, sbl,
+  rows4_run<1, CHC>(m, row0, rows, cols, 0, cols / 32, xs, xh, sbl,
                     [&] {
                       x_stage<true>(X, x, nullptr, 1.f, cols, xs, xh);
                       __syncthreads();
@@ -682,7 +759,8 @@ __global__ __launch_bounds__(kBlock) void k_router(DevQ Wr, const float* lbias, 
   wait_vm();
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t* cnt = ctlw + ctl::kCntRouterTile + 16 * blockIdx.y;
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(ctlw) + ctl::kCntBase +
+                                                64 * (ctl::kCntRouterTile + blockIdx.y));
     uint32_t prev = add_dev(cnt, 1u);
     sys[kSysOk] = prev == gridDim.x - 1;
     if (prev == gridDim.x - 1) st_dev(cnt, 0u);
@@ -693,11 +771,13 @@ __global__ __launch_bounds__(kBlock) void k_router(DevQ Wr, const float* lbias, 
   int32_t* idx_s = reinterpret_cast<int32_t*>(sys + kSysTkIdx) + wave * 8;
   float* w_s = reinterpret_cast<float*>(sys + kSysTkW) + wave * 8;
   for (int t = t0 + wave; t < t1; t += kWavesPerBlock)
-    wave_topk(logits_ws + (size_t)t * E, true, E, K, idx_s, w_s, idx + (size_t)t * K,
+    wave_topk(logits_ws + (size_t)t * E, E, K, idx_s, w_s, idx + (size_t)t * K,
               w + (size_t)t * K);
 }
 
 // ========================================================= MoE FFN step
+constexpr int kSysLg = 64;  // sys words: the router block's 8 logits
+
 template <int HC>
 __device__ void role_router(const DecodeArgs& a, int b, uint8_t* smem, uint32_t epoch) {
   uint32_t* sys = reinterpret_cast<uint32_t*>(smem);
@@ -705,41 +785,48 @@ __device__ void role_router(const DecodeArgs& a, int b, uint8_t* smem, uint32_t 
   float4* xr = reinterpret_cast<float4*>(smem + kSysBytes);
   float* xh = reinterpret_cast<float*>(smem + kSysBytes + (size_t)H * 4);
   float* red = reinterpret_cast<float*>(sys + kSysRed);
-  uint32_t* ctlw = ctl_of(a);
   const int row0 = b * kRowsPerUnit;
   float s = router_token<HC / 16>(a.router, row0, a.E, H, a.x, a.gamma, a.eps, xr, xh, red);
-  if (threadIdx.x < 8 && row0 + (int)threadIdx.x < a.E) {
-    int e = row0 + threadIdx.x;
+  if (threadIdx.x < 8) {
+    int e = min(row0 + (int)threadIdx.x, a.E - 1);
     if (a.lbias) s += a.lbias[e];
-    st_dev(logits_of(a) + e, s);
+    reinterpret_cast<float*>(sys + kSysLg)[threadIdx.x] = s;
   }
-  wait_vm();
   __syncthreads();
-  if (threadIdx.x == 0) st_dev(ctlw + ctl::kFlagR + b, epoch);
+  // publish (epoch, logit) pairs in every replica: one 64-bit store each
+  const int j = threadIdx.x & 7, rep = threadIdx.x >> 3;
+  if (rep < ctl::kRep && row0 + j < a.E) {
+    uint64_t v = ((uint64_t)epoch << 32) | __float_as_uint(reinterpret_cast<float*>(sys + kSysLg)[j]);
+    st_dev(reinterpret_cast<uint64_t*>(rep_of(a, ctl::kTagBase, rep)) + row0 + j, v);
+  }
 }
 
-// Gate/up of 4 row-blocks (one per wave).  expert_rank < 0: shared expert.
-template <int HC>
-__device__ void role_gate_up(const DecodeArgs& a, int expert_rank, int rb0, int rows,
-                             uint8_t* smem, uint32_t epoch) {
+// Gate/up of one row-block of 8 rows: wave w computes matrix (w & 1: gate,
+// up) over column half (w >> 1); the block sums the halves and applies the
+// GELU gating.  expert_rank < 0: shared expert.
+template <int HC, int NV>
+__device__ void role_gate_up(const DecodeArgs& a, int expert_rank, int rb, int rows,
+                             uint8_t* smem, uint32_t epoch, uint64_t t_start) {
   uint32_t* sys = reinterpret_cast<uint32_t*>(smem);
   const int H = HC ? HC : a.H;
   uint4* xs = reinterpret_cast<uint4*>(smem + kSysBytes);
   float* xh = reinterpret_cast<float*>(smem + gu_xh_off(H));
   float* red = reinterpret_cast<float*>(sys + kSysRed);
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int mi = wave & 1, half = wave >> 1;
   uint32_t* sbl = reinterpret_cast<uint32_t*>(smem + gu_sb_off(H)) + wave * gu_sb_words(H);
-  const int row0 = (rb0 + wave) * kRowsPerUnit;
+  const int row0 = rb * kRowsPerUnit;
+  const int CWh = H / 64;  // chunks per column half
   XRegs X;
   x_load(X, a.x, H);
-  DevQ m[2];
-  float* dst;
-  float acc[2];
+  DevQ m[1];
+  size_t dst;  // element offset inside an activation replica
+  float acc[1];
   if (expert_rank < 0) {
-    m[0] = a.shg;
-    m[1] = a.shu;
-    dst = a_sh_of(a);
-    rows4_run<2, HC / 32>(m, row0, rows, H, xs, xh, sbl,
+    hold_until(t_start, kHoldTicks);
+    m[0] = mi ? a.shu : a.shg;
+    dst = 0;
+    rows4_run<1, HC / 64>(m, row0, rows, H, half * CWh, CWh, xs, xh, sbl,
                           [&] {
                             float inv = a.gamma ? x_inv_rms(X, a.x, H, a.eps, red) : 1.f;
                             x_stage<true>(X, a.x, a.gamma, inv, H, xs, xh);
@@ -751,36 +838,41 @@ __device__ void role_gate_up(const DecodeArgs& a, int expert_rank, int rb0, int 
     float inv = a.gamma ? x_inv_rms(X, a.x, H, a.eps, red) : 1.f;
     x_stage<true>(X, a.x, a.gamma, inv, H, xs, xh);
     __syncthreads();
-    if (!block_routing(a, epoch, sys, false)) return;
+    if (!block_routing<NV>(a, epoch, sys, false)) return;
     int e = reinterpret_cast<int32_t*>(sys + kSysIdx)[expert_rank];
     int s = a.slot ? a.slot[e] : e;
-    m[0] = devq_at(a.gate, s);
-    m[1] = devq_at(a.up, s);
-    dst = a_rt_of(a) + (size_t)expert_rank * a.I;
-    rows4_run<2, HC / 32>(m, row0, rows, H, xs, xh, sbl, [] {}, acc);
+    m[0] = devq_at(mi ? a.up : a.gate, s);
+    dst = (size_t)a.Is + (size_t)expert_rank * a.I;
+    rows4_run<1, HC / 64>(m, row0, rows, H, half * CWh, CWh, xs, xh, sbl, [] {}, acc);
   }
-  const int row = row0 + (lane & 7);
-  if ((lane >> 3) == 0 && row < rows) st_dev(dst + row, gelu_tanh(acc[0]) * acc[1]);
+  if ((lane >> 3) == 0) red[wave * 8 + (lane & 7)] = acc[0];
+  __syncthreads();
+  // a = gelu(g) * u for the 8 rows, stored in every activation replica
+  const int t = threadIdx.x & 7, rep = threadIdx.x >> 3;
+  if (rep < ctl::kRep && row0 + t < rows) {
+    float g = red[0 * 8 + t] + red[2 * 8 + t];
+    float u = red[1 * 8 + t] + red[3 * 8 + t];
+    st_dev(act_of(a, rep) + dst + row0 + t, gelu_tanh(g) * u);
+  }
 }
 
-// fp32 activations a[n] (device-coherent reads) -> even/odd LDS layout:
-// as[(2j+e)*CH + c], ah[c] = chunk sums.  `nthr` threads starting at `t`.
+// fp32 activations a[n] (device-coherent 16-byte reads) -> even/odd LDS
+// layout as[(2j+e)*CH + c], ah[c] = chunk sums.  `nthr` threads from `t`.
 __device__ __forceinline__ void stage_a(const float* a, int n, float4* as, float* ah, int t,
                                         int nthr) {
   const int CH = n / 32, Wn = n / 8;
   for (int v0 = 0; v0 < Wn; v0 += nthr) {
     int v = v0 + t;
     bool ok = v < Wn;
-    float f[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) f[i] = ok ? ld_dev(a + 8 * v + i) : 0.f;
-    float s = ((f[0] + f[1]) + (f[2] + f[3])) + ((f[4] + f[5]) + (f[6] + f[7]));
+    float4 lo = ld_dev16(a, (uint32_t)n * 4, (uint32_t)v * 32);
+    float4 hi = ld_dev16(a, (uint32_t)n * 4, (uint32_t)v * 32 + 16);
+    float s = ((lo.x + lo.y) + (lo.z + lo.w)) + ((hi.x + hi.y) + (hi.z + hi.w));
     s += __shfl_xor(s, 1);
     s += __shfl_xor(s, 2);
     if (ok) {
       int c = v >> 2, j = v & 3;
-      as[(2 * j) * CH + c] = make_float4(f[0], f[2], f[4], f[6]);
-      as[(2 * j + 1) * CH + c] = make_float4(f[1], f[3], f[5], f[7]);
+      as[(2 * j) * CH + c] = make_float4(lo.x, lo.z, hi.x, hi.z);
+      as[(2 * j + 1) * CH + c] = make_float4(lo.y, lo.w, hi.y, hi.w);
       if (j == 0) ah[c] = s;
     }
   }
@@ -799,10 +891,16 @@ __device__ __forceinline__ float down_chunk(uint4 w, uint32_t sb, const float4* 
   return fmaf(512.0f * half_to_f32(sb & 0xffffu), a0 + a1, half_to_f32(sb >> 16) * ah[c]);
 }
 
-// Down projections + combine for output rows [8b, 8b+8).
+// Down projections + combine for output rows [8b, 8b+8).  Order: shared
+// weights (held back briefly) -> shared activations once the shared gate/up
+// blocks are done, and the shared part -> routing -> routed weights of this
+// wave's experts -> each expert as soon as its gate/up blocks are done.
+// The shared part comes first so that its waits and activation loads are
+// not queued behind the routed weights.
 // IC/ISC: expert and shared intermediate sizes when known (0: runtime).
-template <int IC, int ISC>
-__device__ void role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t epoch) {
+template <int IC, int ISC, int NV>
+__device__ void role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t epoch,
+                          uint64_t t_start) {
   uint32_t* sys = reinterpret_cast<uint32_t*>(smem);
   const int K = a.K;
   const int I = IC ? IC : a.I, Is = ISC ? ISC : a.Is;
@@ -817,9 +915,12 @@ __device__ void role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
   float* ah_w = reinterpret_cast<float*>(as_w + I / 4);
   float* red = reinterpret_cast<float*>(sys + kSysRed);
   uint32_t* ctlw = ctl_of(a);
+  const uint32_t* flags =
+      reinterpret_cast<const uint32_t*>(rep_of(a, ctl::kFlagBase, blockIdx.x % ctl::kRep));
   const int row = b * kRowsPerUnit + r;  // H is a multiple of 64: always valid
 
   // 1. shared-down weights: wave w takes steps w, w+4, ...
+  hold_until(t_start, kHoldTicks);
   uint4 wsh[MS];
   uint32_t ssh[MS];
 #pragma unroll
@@ -828,9 +929,10 @@ __device__ void role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
     wsh[m] = ldg16(a.shd.q + ((int64_t)row * CHs + c) * 16);
     ssh[m] = ld_sb(a.shd.s, a.shd.b, (int64_t)row * Gs + (c >> 1));
   }
-  // 2. shared activations once the S groups are published
-  if (!block_wait_flags(ctlw + ctl::kFlagS, cdiv(a.nS, ctl::kGroup), epoch, ctlw, 2, sys)) return;
-  stage_a(a_sh_of(a), Is, as_sh, ah_sh, threadIdx.x, kBlock);
+  // 2. shared activations once the S blocks are published, shared part
+  if (!a.nowait && !block_wait_flags(flags, a.nS, epoch, ctlw, 2, sys)) return;
+  const float* act = act_of(a, blockIdx.x % ctl::kRep);
+  stage_a(act, Is, as_sh, ah_sh, threadIdx.x, kBlock);
   __syncthreads();
   float acc = 0.f;
 #pragma unroll
@@ -839,7 +941,7 @@ __device__ void role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
     if (c < CHs) acc += down_chunk(wsh[m], ssh[m], as_sh, ah_sh, CHs, c);
   }
   // 3. routing, then the routed-down weights of this wave's experts (k, k+4)
-  if (!block_routing(a, epoch, sys, b == 0)) return;
+  if (!block_routing<NV>(a, epoch, sys, b == 0)) return;
   const int32_t* idx_s = reinterpret_cast<const int32_t*>(sys + kSysIdx);
   const float* w_s = reinterpret_cast<const float*>(sys + kSysW);
   uint4 wrt[2][MR];
@@ -856,16 +958,15 @@ __device__ void role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
       srt[j][i] = ld_sb(d.s, d.b, (int64_t)row * Gk + (c >> 1));
     }
   }
-  // 4. each wave: its experts in turn, as soon as their G groups are done
-  const int nGg = cdiv(a.perG, ctl::kGroup);
+  // 4. each wave: its experts in turn, as soon as their G blocks are done
   bool ok = true;
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     int k = wave + j * kWavesPerBlock;
     if (k < K && ok) {
-      ok = wave_wait_flags(ctlw + ctl::kFlagG + k * ctl::kMaxGGroups, nGg, epoch, ctlw, 3);
+      if (!a.nowait) ok = wave_wait_flags(flags + a.nS + k * a.perG, a.perG, epoch, ctlw, 3);
       if (ok) {
-        stage_a(a_rt_of(a) + (size_t)k * I, I, as_w, ah_w, lane, 64);
+        stage_a(act + Is + (size_t)k * I, I, as_w, ah_w, lane, 64);
         float part = 0.f;
 #pragma unroll
         for (int i = 0; i < MR; ++i) {
@@ -890,51 +991,26 @@ __device__ void role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
   }
 }
 
-// Called by every D block at its end: the last one (over all D blocks, via
-// counters of at most 16 arrivals) advances the epoch.  Every other block has
-// read the epoch before publishing anything a D block waited for.
-__device__ void d_finish(const DecodeArgs& a, int b) {
-  __syncthreads();
-  if (threadIdx.x != 0) return;
-  uint32_t* ctlw = ctl_of(a);
-  const int grp = b / ctl::kGroup;
-  const int ngrp = cdiv(a.nD, ctl::kGroup);
-  const uint32_t size = (uint32_t)min(ctl::kGroup, a.nD - grp * ctl::kGroup);
-  uint32_t* cnt = ctlw + ctl::kCntD + 16 * grp;
-  if (add_dev(cnt, 1u) != size - 1) return;
-  st_dev(cnt, 0u);
-  uint32_t* top = ctlw + ctl::kCntTop;
-  if (add_dev(top, 1u) != (uint32_t)ngrp - 1) return;
-  st_dev(top, 0u);
-  st_dev(ctlw + ctl::kEpoch, ld_dev(ctlw + ctl::kEpoch) + 1u);
-}
-
-template <int HC, int IC, int ISC>
+// EC: number of experts when known at compile time (0: up to 512).
+template <int HC, int IC, int ISC, int EC>
 __global__ __launch_bounds__(kBlock) void k_moe_step(DecodeArgs a) {
+  constexpr int NV = EC ? cdiv(EC, 64) : QMOE_MAX_EXPERTS / 64;
   extern __shared__ __align__(16) uint8_t smem[];
-  uint32_t* sys = reinterpret_cast<uint32_t*>(smem);
-  uint32_t* ctlw = ctl_of(a);
-  const uint32_t epoch = block_epoch(ctlw, sys);
+  const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
+  const uint32_t epoch = launch_epoch();
   const int rb = a.role0 + blockIdx.x;
   if (rb < a.nR) {
     role_router<HC>(a, rb, smem, epoch);
   } else if (rb < a.nR + a.nS) {
     const int s = rb - a.nR;
-    role_gate_up<HC>(a, -1, s * kWavesPerBlock, ISC ? ISC : a.Is, smem, epoch);
-    const int g = s / ctl::kGroup;
-    block_publish(ctlw + ctl::kCntS + 16 * g, ctlw + ctl::kFlagS + g,
-                  (uint32_t)min(ctl::kGroup, a.nS - g * ctl::kGroup), epoch);
+    role_gate_up<HC, NV>(a, -1, s, ISC ? ISC : a.Is, smem, epoch, t_start);
+    block_publish(a, s, epoch);
   } else if (rb < a.nR + a.nS + a.nG) {
     const int gb = rb - a.nR - a.nS;
-    const int k = gb / a.perG, i = gb % a.perG, g = i / ctl::kGroup;
-    role_gate_up<HC>(a, k, i * kWavesPerBlock, IC ? IC : a.I, smem, epoch);
-    block_publish(ctlw + ctl::kCntG + 16 * (k * ctl::kMaxGGroups + g),
-                  ctlw + ctl::kFlagG + k * ctl::kMaxGGroups + g,
-                  (uint32_t)min(ctl::kGroup, a.perG - g * ctl::kGroup), epoch);
+    role_gate_up<HC, NV>(a, gb / a.perG, gb % a.perG, IC ? IC : a.I, smem, epoch, t_start);
+    block_publish(a, a.nS + gb, epoch);
   } else {
-    const int b = rb - a.nR - a.nS - a.nG;
-    role_down<IC, ISC>(a, b, smem, epoch);
-    d_finish(a, b);
+    role_down<IC, ISC, NV>(a, rb - a.nR - a.nS - a.nG, smem, epoch, t_start);
   }
 }
 
@@ -982,26 +1058,24 @@ qmoe_status launch_router(const qmoe_qtensor& Wr, const float* lbias, const uint
 bool moe_step_supported(const qmoe_moe_layer& L) {
   const int Ss = cdiv(L.shared_inter / 32, kSlots), Sk = cdiv(L.inter / 32, kSlots);
   const int nR = cdiv(L.n_experts, kRowsPerUnit);
-  const int perG = cdiv(L.inter / kRowsPerUnit, kWavesPerBlock);
-  const int nS = cdiv(L.shared_inter / kRowsPerUnit, kWavesPerBlock);
-  const int nD = L.hidden / kRowsPerUnit;
+  const int perG = L.inter / kRowsPerUnit;
+  const int nS = L.shared_inter / kRowsPerUnit;
   return Ss <= kMS * kWavesPerBlock && Sk <= kMR && L.hidden / 8 <= kMaxXW * kBlock && nR <= 64 &&
-         cdiv(nS, ctl::kGroup) <= 32 && cdiv(perG, ctl::kGroup) <= ctl::kMaxGGroups &&
-         cdiv(nD, ctl::kGroup) <= 256;
+         L.n_experts * 8 <= ctl::kRepStride && nS + L.top_k * perG <= ctl::kMaxFlags;
 }
 
-template <int HC, int IC, int ISC>
+template <int HC, int IC, int ISC, int EC>
 static void launch_step_kernel(const DecodeArgs& a, int blocks, size_t lds, void* stream) {
-  hipLaunchKernelGGL((k_moe_step<HC, IC, ISC>), dim3(blocks), dim3(kBlock), lds, S(stream), a);
+  hipLaunchKernelGGL((k_moe_step<HC, IC, ISC, EC>), dim3(blocks), dim3(kBlock), lds, S(stream), a);
 }
 
 static void launch_step(const DecodeArgs& a, int blocks, size_t lds, void* stream) {
-  if (a.H == 2816 && a.I == 704 && a.Is == 2112)
-    launch_step_kernel<2816, 704, 2112>(a, blocks, lds, stream);
-  else if (a.H == 512 && a.I == 256 && a.Is == 512)
-    launch_step_kernel<512, 256, 512>(a, blocks, lds, stream);
+  if (a.H == 2816 && a.I == 704 && a.Is == 2112 && a.E == 128)
+    launch_step_kernel<2816, 704, 2112, 128>(a, blocks, lds, stream);
+  else if (a.H == 512 && a.I == 256 && a.Is == 512 && a.E == 32)
+    launch_step_kernel<512, 256, 512, 32>(a, blocks, lds, stream);
   else
-    launch_step_kernel<0, 0, 0>(a, blocks, lds, stream);
+    launch_step_kernel<0, 0, 0, 0>(a, blocks, lds, stream);
 }
 
 // phased: 0 = one launch with in-kernel waits; 1 = three ordered launches
@@ -1023,13 +1097,14 @@ qmoe_status launch_moe_step(const qmoe_moe_layer& L, const uint16_t* x, const in
   a.ws = ws;
   a.wl = ws_layout(a.E, a.K, a.I, a.Is, 1);
   a.nR = idx_in ? 0 : cdiv(a.E, kRowsPerUnit);
-  a.nS = cdiv(a.Is / kRowsPerUnit, kWavesPerBlock);
-  a.perG = cdiv(a.I / kRowsPerUnit, kWavesPerBlock);
+  a.nS = a.Is / kRowsPerUnit;
+  a.perG = a.I / kRowsPerUnit;
   a.nG = a.K * a.perG;
   a.nD = a.H / kRowsPerUnit;
   size_t lds = gu_lds(a.H);
   if (router_lds(a.H) > lds) lds = router_lds(a.H);
   if (down_lds(a.I, a.Is) > lds) lds = down_lds(a.I, a.Is);
+  a.nowait = phased;
   if (!phased) {
     a.role0 = 0;
     launch_step(a, a.nR + a.nS + a.nG + a.nD, lds, stream);
