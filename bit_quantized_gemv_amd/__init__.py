@@ -68,6 +68,9 @@ _lib.qmoe_moe_decode.argtypes = [C.POINTER(_Layer), _vp, _vp, C.c_int32, _vp, _v
 _lib.qmoe_moe_decode_phased.argtypes = _lib.qmoe_moe_decode.argtypes
 _lib.qmoe_prefill_grouped.argtypes = [C.POINTER(_Layer), _vp, C.c_int32, _vp, _vp, _vp, _vp, _vp,
                                       C.c_size_t, _vp]
+_lib.qmoe_prefill_dispatch_offsets.argtypes = [C.POINTER(_Layer), C.c_int32,
+                                               C.POINTER(C.c_size_t), C.POINTER(C.c_size_t),
+                                               C.POINTER(C.c_size_t)]
 _lib.qmoe_rmsnorm.argtypes = [_vp, _vp, C.c_float, C.c_int32, C.c_int32, _vp, _vp]
 _lib.qmoe_workspace_bytes.restype = C.c_size_t
 _lib.qmoe_workspace_bytes.argtypes = [C.POINTER(_Layer), C.c_int32]
@@ -76,7 +79,7 @@ _lib.qmoe_router_workspace_bytes.argtypes = [C.c_int32, C.c_int32]
 _lib.qmoe_workspace_status.argtypes = [_vp, C.c_size_t, C.POINTER(C.c_int32), _vp]
 for _f in ("qmoe_gemv_affine4", "qmoe_router_topk", "qmoe_expert_ffn", "qmoe_moe_decode",
            "qmoe_moe_decode_phased", "qmoe_prefill_grouped", "qmoe_rmsnorm",
-           "qmoe_workspace_status"):
+           "qmoe_workspace_status", "qmoe_prefill_dispatch_offsets"):
     getattr(_lib, _f).restype = C.c_int
 
 
@@ -218,6 +221,15 @@ def qmoe_prefill_grouped(layer: MoeLayer, X, T: int, idx, w, residual, out, ws,
         _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def qmoe_prefill_dispatch_offsets(layer: MoeLayer, T: int):
+    """Byte offsets (counts, offsets, perm) of the dispatch arrays that the last
+    qmoe_prefill_grouped call for T tokens wrote into its workspace."""
+    c, o, p = C.c_size_t(0), C.c_size_t(0), C.c_size_t(0)
+    _check("qmoe_prefill_dispatch_offsets", _lib.qmoe_prefill_dispatch_offsets(
+        C.byref(layer.c()), T, C.byref(c), C.byref(o), C.byref(p)))
+    return int(c.value), int(o.value), int(p.value)
+
+
 def qmoe_rmsnorm(x, gamma, eps: float, T: int, H: int, out, stream=None) -> None:
     _check("qmoe_rmsnorm", _lib.qmoe_rmsnorm(_ptr(x), _ptr(gamma), float(eps), T, H, _ptr(out),
                                              _stream(stream)))
@@ -237,6 +249,7 @@ def qmoe_workspace_status(ws, stream=None) -> int:
 __all__ = [
     "QTensor", "MoeLayer", "QmoeError", "lib", "LIB_PATH",
     "qmoe_gemv_affine4", "qmoe_router_topk", "qmoe_expert_ffn", "qmoe_moe_decode",
-    "qmoe_prefill_grouped", "qmoe_rmsnorm", "qmoe_workspace_bytes",
+    "qmoe_prefill_grouped", "qmoe_prefill_dispatch_offsets", "qmoe_rmsnorm",
+    "qmoe_workspace_bytes",
     "qmoe_router_workspace_bytes", "qmoe_workspace_status",
 ]

@@ -23,6 +23,8 @@ qmoe_status launch_prefill(const qmoe_moe_layer& L, const uint16_t* X, int T, co
                            const float* w, const uint16_t* residual, uint16_t* out, uint8_t* ws,
                            void* stream);
 size_t prefill_ws_bytes(const qmoe_moe_layer& L, int T);
+void prefill_dispatch_offsets(const qmoe_moe_layer& L, int T, size_t* counts, size_t* offsets,
+                              size_t* perm);
 bool moe_step_supported(const qmoe_moe_layer& L);
 
 static bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -65,11 +67,8 @@ static qmoe_status check_layer(const qmoe_moe_layer* L) {
 static size_t ws_bytes_layer(const qmoe_moe_layer* L, int T) {
   WsLayout wl = ws_layout(L->n_experts, L->top_k, L->inter, L->shared_inter, T);
   size_t d = wl.total;
-  if (T > 1) {
-    size_t p = wl.pf + prefill_ws_bytes(*L, T);
-    if (p > d) d = p;
-  }
-  return d;
+  size_t p = wl.pf + prefill_ws_bytes(*L, T);
+  return p > d ? p : d;
 }
 }  // namespace qmoe
 
@@ -171,6 +170,16 @@ qmoe_status qmoe_prefill_grouped(const qmoe_moe_layer* L, const uint16_t* X, int
   if (!ws) return QMOE_ERR_WORKSPACE;
   if (ws_bytes < ws_bytes_layer(L, T)) return QMOE_ERR_WORKSPACE;
   return launch_prefill(*L, X, T, idx, w, residual, out, static_cast<uint8_t*>(ws), stream);
+}
+
+qmoe_status qmoe_prefill_dispatch_offsets(const qmoe_moe_layer* L, int32_t T,
+                                          size_t* counts, size_t* offsets, size_t* perm) {
+  qmoe_status s = check_layer(L);
+  if (s != QMOE_OK) return s;
+  if (!counts || !offsets || !perm) return QMOE_ERR_NULL_ARG;
+  if (T < 1 || T > QMOE_MAX_TOKENS) return QMOE_ERR_BAD_SHAPE;
+  prefill_dispatch_offsets(*L, T, counts, offsets, perm);
+  return QMOE_OK;
 }
 
 qmoe_status qmoe_workspace_status(void* ws, size_t ws_bytes, int32_t* device_code, void* stream) {

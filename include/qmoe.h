@@ -161,11 +161,25 @@ qmoe_status qmoe_moe_decode_phased(const qmoe_moe_layer* L, const uint16_t* x,
  * GEMM over all T rows; then
  *   out[t] = bf16( y_shared[t] + sum_j w[t][j] y_idx[t][j][t]  (+ residual[t]) )
  * X: bf16 [T][H] (expert input).  idx/w: [T][top_k] device (from
- * qmoe_router_topk).  residual: bf16 [T][H] or NULL.  out: bf16 [T][H]. */
+ * qmoe_router_topk); idx values must lie in [0, n_experts) (others are
+ * clamped into that range); an expert may repeat within a token.
+ * residual: bf16 [T][H] or NULL.  out: bf16 [T][H].
+ * The matrix cores take fp16 operands: X and the gate/up activations are
+ * rounded to fp16 and each weight s*q + b is rounded to fp16 once (fp32
+ * accumulation), so |X| and the activations must stay below 65504. */
 qmoe_status qmoe_prefill_grouped(const qmoe_moe_layer* L, const uint16_t* X,
                                  int32_t T, const int32_t* idx, const float* w,
                                  const uint16_t* residual, uint16_t* out,
                                  void* ws, size_t ws_bytes, void* stream);
+
+/* Inspection hook for tests: byte offsets inside the workspace of the
+ * dispatch arrays that the last qmoe_prefill_grouped call on it wrote for
+ * T tokens: counts int32[n_experts], offsets int32[n_experts + 1] (exclusive
+ * prefix of counts), perm int32[T*top_k] (flat pair index t*top_k + j, in
+ * the order expert, then t, then j). */
+qmoe_status qmoe_prefill_dispatch_offsets(const qmoe_moe_layer* L, int32_t T,
+                                          size_t* counts, size_t* offsets,
+                                          size_t* perm);
 
 /* out[t][i] = bf16( x[t][i] * gamma[i] / sqrt(mean_i x[t][i]^2 + eps) ).
  * x, out: bf16 [T][H]; gamma: bf16 [H]. */

@@ -230,10 +230,10 @@ def _check_decode_token(ol, x, got, gidx, gw, residual=False):
     r = ol.forward(x, residual=residual)
     if list(gidx) != list(r["idx"]):
         lg = r["logits"]
-        diff = set(gidx) ^ set(r["idx"])
         gap = max(lg) - min(lg)
-        spread = max(abs(lg[e] - lg[r["idx"][-1]]) for e in diff)
-        log(f"  routing differs {sorted(diff)}; fp64 gap {spread:.3g} of range {gap:.3g}")
+        spread = max(abs(lg[a] - lg[b]) for a, b in zip(gidx, r["idx"]))
+        log(f"  routing differs {list(gidx)} vs {list(r['idx'])}; fp64 gap {spread:.3g} "
+            f"of range {gap:.3g}")
         assert spread <= 1e-3 * max(1.0, abs(lg).max()), "routing flip is not a near-tie"
         from scipy.special import softmax
 
