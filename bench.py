@@ -14,11 +14,16 @@ launch of the library.  To measure HBM and not the 256 MB Infinity Cache,
 the layer's weights are held in 32 separate copies (~14 GB) and consecutive
 steps cycle through them, each with its own input token.
 
+The 128-token prefill chunk (router with the Zipf prior, then the grouped
+MFMA prefill) is timed as a second, reported-only leg on the same weights.
+
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+                    [--no-prefill] [--copy-calibration]
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -31,12 +36,55 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFS = 2500.0
 COPIES = 32
 N_TOKENS = 64
+PF_TOKENS = 128
+COPY_BYTES = 1 << 30
+# HBM traffic of the decode kernel from rocprofv3 counters (FETCH_SIZE and
+# WRITE_SIZE, scaled by the same counters on a plain copy of known size);
+# valid only for the kernel sources it was measured on.
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_moe_step_layer_decode_pmc.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "bit_quantized_gemv_amd", "csrc", f)
+                  for f in ("qmoe_decode.hip", "qmoe_common.h")]
 
 
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
+
+
+def kernel_sources_sha256() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """(bytes per launch, note) from the committed counter summary, or
+    (None, reason) when it is missing or the kernel changed since."""
+    if not os.path.exists(PMC_SUMMARY):
+        return None, "no counter summary"
+    kv = {}
+    for line in open(PMC_SUMMARY):
+        if ":" in line and not line.startswith(" "):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources_sha256") != kernel_sources_sha256():
+        return None, "kernel changed since the counters were taken"
+    try:
+        return int(kv["traffic_bytes_per_launch"]), "rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-scaled"
+    except (KeyError, ValueError):
+        return None, "counter summary incomplete"
+
+
+def host_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(n, 16))
 
 
 def cpu_baseline(lw, X, seconds_hint: float = 15.0):
@@ -45,7 +93,7 @@ def cpu_baseline(lw, X, seconds_hint: float = 15.0):
     import oracle
 
     L = oracle.OracleLayer(lw)
-    cores = os.cpu_count() or 1
+    cores = host_threads()
     t0 = time.perf_counter()
     L.forward(X[0])
     one = time.perf_counter() - t0
@@ -66,6 +114,9 @@ def main():
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true", help="skip the prefill leg")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for counter scaling)")
     ap.add_argument("--phased", action="store_true",
                     help="time the three-launch variant instead of the single launch")
     args = ap.parse_args()
@@ -104,11 +155,34 @@ def main():
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
 
-    def step(i):
+    def step(i, e0=None, e1=None):
         L = layers[i % COPIES].layer
         t = i % N_TOKENS
-        q.qmoe_moe_decode(L, Xd[t], None, False, outs[t], idx, w, ws, stream=sptr,
-                          phased=args.phased)
+        if e0 is not None and not args.phased:
+            q.qmoe_moe_decode_timed(L, Xd[t], None, False, outs[t], idx, w, ws,
+                                    e0.cuda_event, e1.cuda_event, stream=sptr)
+        else:
+            q.qmoe_moe_decode(L, Xd[t], None, False, outs[t], idx, w, ws, stream=sptr,
+                              phased=args.phased)
+
+    # The timed loop calls the C entry point with its arguments marshalled
+    # beforehand (layer structs and device addresses), so that host-side
+    # Python work does not throttle the launches.
+    import ctypes
+
+    lib = q.lib()
+    timed_fn = lib.qmoe_moe_decode_timed
+    cstructs = [ctypes.byref(dl.layer.c()) for dl in layers]
+    xs = [Xd[t].data_ptr() for t in range(N_TOKENS)]
+    os_ = [outs[t].data_ptr() for t in range(N_TOKENS)]
+    ws_args = (idx.data_ptr(), w.data_ptr(), ws.data_ptr(), ws.numel())
+
+    def timed_step(i, e0, e1):
+        t = i % N_TOKENS
+        rc = timed_fn(cstructs[i % COPIES], xs[t], None, 0, os_[t], ws_args[0], ws_args[1],
+                      ws_args[2], ws_args[3], sptr, e0, e1)
+        if rc:
+            raise q.QmoeError("qmoe_moe_decode_timed", rc)
 
     log("warmup")
     for i in range(args.warmup):
@@ -117,16 +191,24 @@ def main():
     if q.qmoe_workspace_status(ws) != 0:
         raise SystemExit("device wait failure during warmup")
 
-    # timed region: K steps; HIP events on the launch stream bracket each
-    # step's launch(es) to time the kernel(s) themselves
+    # timed region: K steps.  Each launch records a pair of HIP events at
+    # its kernel's start and end (the launch's own timestamps, on the launch
+    # stream); the three-launch variant is bracketed by event records.
     K = args.steps
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * K)]
+    for e in ev:  # create the underlying hipEvents before the timed region
+        e.record(stream)
+    evh = [e.cuda_event for e in ev]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K):
-        ev[2 * i].record(stream)
-        step(args.warmup + i)
-        ev[2 * i + 1].record(stream)
+    if args.phased:
+        for i in range(K):
+            ev[2 * i].record(stream)
+            step(args.warmup + i)
+            ev[2 * i + 1].record(stream)
+    else:
+        for i in range(K):
+            timed_step(args.warmup + i, evh[2 * i], evh[2 * i + 1])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     code = q.qmoe_workspace_status(ws)
@@ -139,6 +221,7 @@ def main():
     ms_per_step = elapsed * 1e3 / K
     tok_s = K / elapsed
     achieved = algo_bytes / (kern_us * 1e-6) / 1e9
+    traffic, traffic_note = measured_traffic()
     log(f"step {ms_per_step * 1e3:.2f} us, kernel mean {kern_us:.2f} us median {kern_med_us:.2f} us, "
         f"{achieved:.0f} GB/s algorithmic")
 
@@ -153,21 +236,95 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32 accumulation over u4/u8 affine codes, bf16 activations",
+        "dtype": "f32",
         "data": "synthetic (seeded; 4-bit/8-bit affine g64 weights, bf16 N(0,1) tokens)",
         "config": {"workload": "MoE layer decode, batch 1: hidden 2816, 128 experts, top-8, "
                                "expert inter 704, shared inter 2112, 8-bit router",
                    "launch": "phased (3 launches)" if args.phased else "single launch",
-                   "weight_copies": COPIES, "algorithmic_bytes_per_step": algo_bytes},
+                   "weight_copies": COPIES, "algorithmic_bytes_per_step": algo_bytes,
+                   "codes": "u4 experts / u8 router, affine g64, fp16 scale+bias",
+                   "activations": "bf16 in, f32 accumulation, bf16 out"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                     "kernel": "k_moe_step (whole decode step)",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "traffic_source": traffic_note,
+                     "kernel": "k_moe_step (whole decode step)" if not args.phased else
+                               "k_moe_step (three role launches)",
                      "kernel_us_mean": kern_us, "kernel_us_median": kern_med_us},
     }
+    if not args.no_prefill:
+        res["prefill"] = prefill_leg(torch, q, synth, sd, lw, layers, wl, sptr)
+    if args.copy_calibration:
+        copy_calibration(torch)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(lw, X)
     print(json.dumps(res), flush=True)
+
+
+def prefill_leg(torch, q, synth, sd, lw, layers, wl, sptr, iters: int = 64):
+    """Time one 128-token chunk (router top-8 with the Zipf log-prior, then
+    the grouped prefill) per iteration, cycling through the weight copies."""
+    pw = synth.WORKLOADS["prefill128"]
+    prior = synth.zipf_prior(pw, 0)
+    bias = torch.from_numpy(prior.astype(np.float32)).cuda()
+    Xp = torch.from_numpy(synth.make_tokens(pw, PF_TOKENS, stream=2).view(np.int16)).cuda()
+    T, E, K = PF_TOKENS, wl.n_experts, wl.top_k
+    idx = torch.empty(T, K, dtype=torch.int32, device="cuda")
+    w = torch.empty(T, K, dtype=torch.float32, device="cuda")
+    out = torch.empty(T, wl.hidden, dtype=torch.int16, device="cuda")
+    rws = torch.zeros(q.qmoe_router_workspace_bytes(E, T), dtype=torch.uint8, device="cuda")
+    ws = layers[0].layer.new_workspace(T)
+    saved = [dl.layer.logit_bias for dl in layers]
+    for dl in layers:
+        dl.layer.logit_bias = bias
+        dl.layer._c = None
+
+    def chunk(i):
+        L = layers[i % COPIES].layer
+        q.qmoe_router_topk(L.router, bias, Xp, T, K, idx, w, None, rws, stream=sptr)
+        q.qmoe_prefill_grouped(L, Xp, T, idx, w, None, out, ws, stream=sptr)
+
+    for i in range(8):
+        chunk(i)
+    torch.cuda.synchronize()
+    distinct = int(torch.unique(idx).numel())
+    hottest = int(torch.bincount(idx.flatten().long(), minlength=E).max())
+    stream = torch.cuda.current_stream()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * iters)]
+    for i in range(iters):
+        ev[2 * i].record(stream)
+        chunk(8 + i)
+        ev[2 * i + 1].record(stream)
+    torch.cuda.synchronize()
+    us = float(np.mean([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(iters)]) * 1e3)
+    for dl, b in zip(layers, saved):
+        dl.layer.logit_bias = b
+        dl.layer._c = None
+    g, u, d = lw.expert(0)
+    blob = sum(m.q.nbytes + m.s.nbytes + m.b.nbytes for m in (g, u, d))
+    shared = sum(m.q.nbytes + m.s.nbytes + m.b.nbytes for m in (lw.sh_gate, lw.sh_up, lw.sh_down))
+    router = lw.router.q.nbytes + lw.router.s.nbytes + lw.router.b.nbytes
+    nbytes = router + shared + distinct * blob + 2 * 2 * T * wl.hidden
+    H, I, Is = wl.hidden, wl.inter, wl.shared_inter
+    flops = 2.0 * T * K * 3 * H * I + 2.0 * T * 3 * H * Is
+    log(f"prefill chunk {us:.1f} us: {distinct} experts, hottest {hottest} rows")
+    return {"workload": "128-token prefill chunk, Zipf(1.1) log-prior on the router logits, "
+                        "weights of the decode layer",
+            "tokens_per_s": T / (us * 1e-6), "us_per_chunk": us,
+            "distinct_experts": distinct, "hottest_expert_rows": hottest,
+            "algorithmic_bytes": nbytes, "achieved_GBps": nbytes / (us * 1e-6) / 1e9,
+            "flops": flops, "achieved_TFLOPs": flops / (us * 1e-6) / 1e12,
+            "mfma_f16_peak_TFLOPs": MFMA_F16_PEAK_TFS}
+
+
+def copy_calibration(torch, reps: int = 3):
+    """A plain device copy of COPY_BYTES, for scaling the byte counters."""
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy calibration: {reps} x {COPY_BYTES} bytes read and written")
 
 
 if __name__ == "__main__":

@@ -66,6 +66,7 @@ _lib.qmoe_expert_ffn.argtypes = [C.POINTER(_Layer), _vp, _vp, _vp, _vp, _vp, _vp
 _lib.qmoe_moe_decode.argtypes = [C.POINTER(_Layer), _vp, _vp, C.c_int32, _vp, _vp, _vp, _vp,
                                  C.c_size_t, _vp]
 _lib.qmoe_moe_decode_phased.argtypes = _lib.qmoe_moe_decode.argtypes
+_lib.qmoe_moe_decode_timed.argtypes = _lib.qmoe_moe_decode.argtypes + [_vp, _vp]
 _lib.qmoe_prefill_grouped.argtypes = [C.POINTER(_Layer), _vp, C.c_int32, _vp, _vp, _vp, _vp, _vp,
                                       C.c_size_t, _vp]
 _lib.qmoe_prefill_dispatch_offsets.argtypes = [C.POINTER(_Layer), C.c_int32,
@@ -79,7 +80,7 @@ _lib.qmoe_router_workspace_bytes.argtypes = [C.c_int32, C.c_int32]
 _lib.qmoe_workspace_status.argtypes = [_vp, C.c_size_t, C.POINTER(C.c_int32), _vp]
 for _f in ("qmoe_gemv_affine4", "qmoe_router_topk", "qmoe_expert_ffn", "qmoe_moe_decode",
            "qmoe_moe_decode_phased", "qmoe_prefill_grouped", "qmoe_rmsnorm",
-           "qmoe_workspace_status", "qmoe_prefill_dispatch_offsets"):
+           "qmoe_workspace_status", "qmoe_prefill_dispatch_offsets", "qmoe_moe_decode_timed"):
     getattr(_lib, _f).restype = C.c_int
 
 
@@ -214,6 +215,16 @@ def qmoe_moe_decode(layer: MoeLayer, x, expert_slot, residual: bool, out, idx_ou
         _ptr(idx_out), _ptr(w_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def qmoe_moe_decode_timed(layer: MoeLayer, x, expert_slot, residual: bool, out, idx_out, w_out,
+                          ws, ev_start, ev_stop, stream=None) -> None:
+    """qmoe_moe_decode whose launch records two HIP events (raw handles, e.g.
+    ``torch.cuda.Event.cuda_event``) at its kernel's start and end."""
+    _check("qmoe_moe_decode_timed", _lib.qmoe_moe_decode_timed(
+        C.byref(layer.c()), _ptr(x), _ptr(expert_slot), int(bool(residual)), _ptr(out),
+        _ptr(idx_out), _ptr(w_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream),
+        ev_start, ev_stop))
+
+
 def qmoe_prefill_grouped(layer: MoeLayer, X, T: int, idx, w, residual, out, ws,
                          stream=None) -> None:
     _check("qmoe_prefill_grouped", _lib.qmoe_prefill_grouped(
@@ -249,7 +260,8 @@ def qmoe_workspace_status(ws, stream=None) -> int:
 __all__ = [
     "QTensor", "MoeLayer", "QmoeError", "lib", "LIB_PATH",
     "qmoe_gemv_affine4", "qmoe_router_topk", "qmoe_expert_ffn", "qmoe_moe_decode",
-    "qmoe_prefill_grouped", "qmoe_prefill_dispatch_offsets", "qmoe_rmsnorm",
+    "qmoe_moe_decode_timed", "qmoe_prefill_grouped", "qmoe_prefill_dispatch_offsets",
+    "qmoe_rmsnorm",
     "qmoe_workspace_bytes",
     "qmoe_router_workspace_bytes", "qmoe_workspace_status",
 ]

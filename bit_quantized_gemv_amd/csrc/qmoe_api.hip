@@ -18,7 +18,7 @@ qmoe_status launch_router(const qmoe_qtensor& Wr, const float* lbias, const uint
 qmoe_status launch_moe_step(const qmoe_moe_layer& L, const uint16_t* x, const int32_t* idx_in,
                             const float* w_in, const int32_t* slot, const uint16_t* residual,
                             uint16_t* out, int32_t* idx_out, float* w_out, uint8_t* ws, int mode,
-                            void* stream);
+                            void* stream, void* ev_start = nullptr, void* ev_stop = nullptr);
 qmoe_status launch_prefill(const qmoe_moe_layer& L, const uint16_t* X, int T, const int32_t* idx,
                            const float* w, const uint16_t* residual, uint16_t* out, uint8_t* ws,
                            void* stream);
@@ -198,6 +198,19 @@ qmoe_status qmoe_workspace_status(void* ws, size_t ws_bytes, int32_t* device_cod
     return QMOE_ERR_DEVICE;
   }
   return QMOE_OK;
+}
+
+qmoe_status qmoe_moe_decode_timed(const qmoe_moe_layer* L, const uint16_t* x,
+                                  const int32_t* expert_slot, int32_t residual, uint16_t* out,
+                                  int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
+                                  void* stream, void* ev_start, void* ev_stop) {
+  qmoe_status s = check_layer(L);
+  if (s != QMOE_OK) return s;
+  if (!x || !out) return QMOE_ERR_NULL_ARG;
+  if (!al16(x)) return QMOE_ERR_ALIGN;
+  if (!ws || ws_bytes < ws_bytes_layer(L, 1)) return QMOE_ERR_WORKSPACE;
+  return launch_moe_step(*L, x, nullptr, nullptr, expert_slot, residual ? x : nullptr, out,
+                         idx_out, w_out, static_cast<uint8_t*>(ws), 0, stream, ev_start, ev_stop);
 }
 
 /* Test-only variant: runs the step as separate launches per role instead of

@@ -40,6 +40,8 @@
 // shapes, every trip count is a compile-time constant: the compiler then
 // waits for each load just before its first use, so the math of the first
 // chunks overlaps the transfer of the last ones.
+#include <hip/hip_ext.h>
+
 #include "qmoe_common.h"
 
 namespace qmoe {
@@ -1064,26 +1066,38 @@ bool moe_step_supported(const qmoe_moe_layer& L) {
          L.n_experts * 8 <= ctl::kRepStride && nS + L.top_k * perG <= ctl::kMaxFlags;
 }
 
+// ev0/ev1: optional hipEvent_t recorded by the dispatch itself at the
+// kernel's start and end (hipExtLaunchKernelGGL), for exact kernel timing.
 template <int HC, int IC, int ISC, int EC>
-static void launch_step_kernel(const DecodeArgs& a, int blocks, size_t lds, void* stream) {
-  hipLaunchKernelGGL((k_moe_step<HC, IC, ISC, EC>), dim3(blocks), dim3(kBlock), lds, S(stream), a);
-}
-
-static void launch_step(const DecodeArgs& a, int blocks, size_t lds, void* stream) {
-  if (a.H == 2816 && a.I == 704 && a.Is == 2112 && a.E == 128)
-    launch_step_kernel<2816, 704, 2112, 128>(a, blocks, lds, stream);
-  else if (a.H == 512 && a.I == 256 && a.Is == 512 && a.E == 32)
-    launch_step_kernel<512, 256, 512, 32>(a, blocks, lds, stream);
+static void launch_step_kernel(const DecodeArgs& a, int blocks, size_t lds, void* stream,
+                               hipEvent_t ev0, hipEvent_t ev1) {
+  if (ev0 || ev1)
+    hipExtLaunchKernelGGL((k_moe_step<HC, IC, ISC, EC>), dim3(blocks), dim3(kBlock), lds,
+                          S(stream), ev0, ev1, 0, a);
   else
-    launch_step_kernel<0, 0, 0, 0>(a, blocks, lds, stream);
+    hipLaunchKernelGGL((k_moe_step<HC, IC, ISC, EC>), dim3(blocks), dim3(kBlock), lds, S(stream), a);
 }
 
-// phased: 0 = one launch with in-kernel waits; 1 = three ordered launches
+static void launch_step(const DecodeArgs& a, int blocks, size_t lds, void* stream,
+                        hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
+  if (a.H == 2816 && a.I == 704 && a.Is == 2112 && a.E == 128)
+    launch_step_kernel<2816, 704, 2112, 128>(a, blocks, lds, stream, ev0, ev1);
+  else if (a.H == 512 && a.I == 256 && a.Is == 512 && a.E == 32)
+    launch_step_kernel<512, 256, 512, 32>(a, blocks, lds, stream, ev0, ev1);
+  else
+    launch_step_kernel<0, 0, 0, 0>(a, blocks, lds, stream, ev0, ev1);
+}
+
+// phased: 0 = one launch with in-kernel waits; 1 = three ordered launches.
+// ev_start/ev_stop (hipEvent_t or null): recorded at the start of the first
+// and the end of the last kernel of the step.
 qmoe_status launch_moe_step(const qmoe_moe_layer& L, const uint16_t* x, const int32_t* idx_in,
                             const float* w_in, const int32_t* slot, const uint16_t* residual,
                             uint16_t* out, int32_t* idx_out, float* w_out, uint8_t* ws, int phased,
-                            void* stream) {
+                            void* stream, void* ev_start, void* ev_stop) {
   if (!moe_step_supported(L)) return QMOE_ERR_UNSUPPORTED;
+  hipEvent_t e0 = reinterpret_cast<hipEvent_t>(ev_start);
+  hipEvent_t e1 = reinterpret_cast<hipEvent_t>(ev_stop);
   DecodeArgs a;
   a.H = L.hidden; a.E = L.n_experts; a.K = L.top_k; a.I = L.inter; a.Is = L.shared_inter;
   a.router = devq(L.router); a.gate = devq(L.gate); a.up = devq(L.up); a.down = devq(L.down);
@@ -1107,18 +1121,19 @@ qmoe_status launch_moe_step(const qmoe_moe_layer& L, const uint16_t* x, const in
   a.nowait = phased;
   if (!phased) {
     a.role0 = 0;
-    launch_step(a, a.nR + a.nS + a.nG + a.nD, lds, stream);
+    launch_step(a, a.nR + a.nS + a.nG + a.nD, lds, stream, e0, e1);
     return hipGetLastError() == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
   }
   // router; shared + routed gate/up; down (waits are then satisfied on entry)
   if (a.nR) {
     a.role0 = 0;
-    launch_step(a, a.nR, lds, stream);
+    launch_step(a, a.nR, lds, stream, e0, nullptr);
+    e0 = nullptr;
   }
   a.role0 = a.nR;
-  launch_step(a, a.nS + a.nG, lds, stream);
+  launch_step(a, a.nS + a.nG, lds, stream, e0, nullptr);
   a.role0 = a.nR + a.nS + a.nG;
-  launch_step(a, a.nD, lds, stream);
+  launch_step(a, a.nD, lds, stream, nullptr, e1);
   return hipGetLastError() == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
 }
 

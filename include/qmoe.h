@@ -154,6 +154,16 @@ qmoe_status qmoe_moe_decode_phased(const qmoe_moe_layer* L, const uint16_t* x,
                                    uint16_t* out, int32_t* idx_out, float* w_out,
                                    void* ws, size_t ws_bytes, void* stream);
 
+/* qmoe_moe_decode with kernel timing: ev_start and ev_stop (hipEvent_t, or
+ * NULL) are recorded by the launch itself at the start and at the end of
+ * the step's kernel, so hipEventElapsedTime gives the kernel's duration
+ * without the gaps around it.  Otherwise identical to qmoe_moe_decode. */
+qmoe_status qmoe_moe_decode_timed(const qmoe_moe_layer* L, const uint16_t* x,
+                                  const int32_t* expert_slot, int32_t residual,
+                                  uint16_t* out, int32_t* idx_out, float* w_out,
+                                  void* ws, size_t ws_bytes, void* stream,
+                                  void* ev_start, void* ev_stop);
+
 /* Chunked prefill of T <= 128 tokens that share one loaded copy of each
  * expert: the (token, rank) pairs are grouped by expert (stable: expert,
  * then token, then rank) and every expert runs one grouped dequantizing

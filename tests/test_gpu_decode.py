@@ -301,3 +301,28 @@ def test_rmsnorm_matches_oracle(torch_cuda, q):
         d = np.abs(got[t].astype(np.int32) - ref.astype(np.int32))
         # equal, or one bf16 step apart at a rounding boundary (fp32 vs fp64)
         assert np.all(d <= 1) and np.mean(d) < 1e-2
+
+
+def test_moe_decode_timed_equals_untimed(torch_cuda, q, big_layer):
+    """The timing variant records its events and computes the same bits."""
+    torch = torch_cuda
+    lw, ol, dl = big_layer
+    L = dl.layer
+    x = synth.make_tokens(lw.wl, 1, stream=71)[0]
+    ref, ridx, rw = _decode(torch, q, dl, x, residual=True)
+    ws = L.new_workspace(1)
+    xd = _dev_u16(torch, x)
+    out = torch.empty(L.hidden, dtype=torch.int16, device="cuda")
+    idx = torch.empty(L.top_k, dtype=torch.int32, device="cuda")
+    w = torch.empty(L.top_k, dtype=torch.float32, device="cuda")
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    e1.record()
+    q.qmoe_moe_decode_timed(L, xd, None, True, out, idx, w, ws, e0.cuda_event, e1.cuda_event)
+    torch.cuda.synchronize()
+    assert q.qmoe_workspace_status(ws) == 0
+    assert np.array_equal(to_u16(out), ref)
+    assert list(idx.cpu().numpy()) == list(ridx)
+    ms = e0.elapsed_time(e1)
+    log(f"  timed step kernel {ms * 1e3:.1f} us")
+    assert 0 < ms < 100
