@@ -30,10 +30,12 @@
 // wait on it: every wait ends.  Each wait is also bounded in time and then
 // reports a device error instead of hanging.
 //
-// Hand-offs use flags that carry a per-call epoch (read from the workspace at
-// the start, advanced by the last D block), device-coherent stores/loads for
-// the exchanged values, and per-group arrival counters of at most 16 blocks
-// (same-address atomics serialise across the XCDs).
+// Hand-offs: every producer block raises its own flag word to the call's
+// epoch (derived from the launch's dispatch-packet address, so it differs
+// from the previous call's without any reset); exchanged values travel as
+// device-coherent stores/loads; small values that many blocks poll (router
+// logits, flags, gate/up activations) are written in 16 replicas so that
+// pollers spread over memory channels.  No atomics, no cache fences.
 //
 // Every weight and scale load is unconditional (out-of-range chunks re-read
 // a valid address and only the arithmetic is predicated) and, for the model
