@@ -72,6 +72,23 @@ _lib.qmoe_prefill_grouped.argtypes = [C.POINTER(_Layer), _vp, C.c_int32, _vp, _v
 _lib.qmoe_prefill_dispatch_offsets.argtypes = [C.POINTER(_Layer), C.c_int32,
                                                C.POINTER(C.c_size_t), C.POINTER(C.c_size_t),
                                                C.POINTER(C.c_size_t)]
+_lib.qmoe_expert_ffn_shared.argtypes = [C.POINTER(_Layer), _vp, _vp, C.c_size_t, _vp]
+_lib.qmoe_expert_ffn_routed.argtypes = _lib.qmoe_expert_ffn.argtypes
+
+
+class PoolStats(C.Structure):
+    _fields_ = [("hits", C.c_int64), ("misses", C.c_int64), ("h2d_bytes", C.c_int64),
+                ("last_hits", C.c_int32), ("last_misses", C.c_int32)]
+
+
+_lib.qmoe_pool_create.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_size_t, _vp, _vp,
+                                  C.POINTER(_vp)]
+_lib.qmoe_pool_plan.argtypes = [_vp, C.c_int32, _vp, C.c_int32, _vp, _vp, _vp]
+_lib.qmoe_pool_acquire.argtypes = [_vp, C.c_int32, _vp, C.c_int32, _vp, _vp, _vp,
+                                   C.POINTER(PoolStats)]
+_lib.qmoe_pool_stats_get.argtypes = [_vp, C.POINTER(PoolStats)]
+_lib.qmoe_pool_destroy.argtypes = [_vp]
+_lib.qmoe_pool_destroy.restype = None
 _lib.qmoe_rmsnorm.argtypes = [_vp, _vp, C.c_float, C.c_int32, C.c_int32, _vp, _vp]
 _lib.qmoe_workspace_bytes.restype = C.c_size_t
 _lib.qmoe_workspace_bytes.argtypes = [C.POINTER(_Layer), C.c_int32]
@@ -80,7 +97,9 @@ _lib.qmoe_router_workspace_bytes.argtypes = [C.c_int32, C.c_int32]
 _lib.qmoe_workspace_status.argtypes = [_vp, C.c_size_t, C.POINTER(C.c_int32), _vp]
 for _f in ("qmoe_gemv_affine4", "qmoe_router_topk", "qmoe_expert_ffn", "qmoe_moe_decode",
            "qmoe_moe_decode_phased", "qmoe_prefill_grouped", "qmoe_rmsnorm",
-           "qmoe_workspace_status", "qmoe_prefill_dispatch_offsets", "qmoe_moe_decode_timed"):
+           "qmoe_workspace_status", "qmoe_prefill_dispatch_offsets", "qmoe_moe_decode_timed",
+           "qmoe_expert_ffn_shared", "qmoe_expert_ffn_routed", "qmoe_pool_create",
+           "qmoe_pool_plan", "qmoe_pool_acquire", "qmoe_pool_stats_get"):
     getattr(_lib, _f).restype = C.c_int
 
 
@@ -207,6 +226,72 @@ def qmoe_expert_ffn(layer: MoeLayer, h, idx, w, expert_slot, residual, out, ws,
         _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def qmoe_expert_ffn_shared(layer: MoeLayer, h, ws, stream=None) -> None:
+    _check("qmoe_expert_ffn_shared", _lib.qmoe_expert_ffn_shared(
+        C.byref(layer.c()), _ptr(h), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def qmoe_expert_ffn_routed(layer: MoeLayer, h, idx, w, expert_slot, residual, out, ws,
+                           stream=None) -> None:
+    _check("qmoe_expert_ffn_routed", _lib.qmoe_expert_ffn_routed(
+        C.byref(layer.c()), _ptr(h), _ptr(idx), _ptr(w), _ptr(expert_slot), _ptr(residual),
+        _ptr(out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+class Pool:
+    """The host-resident expert pool (qmoe_pool_*).  ``host_blobs``: one
+    pinned host address per (layer, expert), layer-major; ``arenas``: one
+    device address per layer (``slots`` blobs each).  Both None: a
+    planning-only pool."""
+
+    def __init__(self, layers: int, experts: int, slots: int, blob_bytes: int,
+                 host_blobs=None, arenas=None):
+        self.layers, self.experts, self.slots = layers, experts, slots
+        hb = ar = None
+        if host_blobs is not None:
+            self._hb = (_vp * (layers * experts))(*host_blobs)
+            self._ar = (_vp * layers)(*arenas)
+            hb, ar = self._hb, self._ar
+        h = _vp()
+        _check("qmoe_pool_create", _lib.qmoe_pool_create(layers, experts, slots, blob_bytes,
+                                                          hb, ar, C.byref(h)))
+        self._h = h
+
+    def plan(self, layer: int, idx):
+        import numpy as np
+
+        idx = np.ascontiguousarray(idx, dtype=np.int32)
+        k = idx.shape[0]
+        slot = np.zeros(k, np.int32)
+        hit = np.zeros(k, np.int32)
+        victim = np.zeros(k, np.int32)
+        _check("qmoe_pool_plan", _lib.qmoe_pool_plan(
+            self._h, layer, idx.ctypes.data, k, slot.ctypes.data, hit.ctypes.data,
+            victim.ctypes.data))
+        return slot, hit, victim
+
+    def acquire(self, layer: int, host_idx_ptr: int, k: int, dev_expert_slot, copy_stream,
+                ready_event: int) -> PoolStats:
+        st = PoolStats()
+        _check("qmoe_pool_acquire", _lib.qmoe_pool_acquire(
+            self._h, layer, host_idx_ptr, k, _ptr(dev_expert_slot), _stream(copy_stream),
+            ready_event, C.byref(st)))
+        return st
+
+    def stats(self) -> PoolStats:
+        st = PoolStats()
+        _check("qmoe_pool_stats_get", _lib.qmoe_pool_stats_get(self._h, C.byref(st)))
+        return st
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            _lib.qmoe_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+
 def qmoe_moe_decode(layer: MoeLayer, x, expert_slot, residual: bool, out, idx_out, w_out, ws,
                     stream=None, phased: bool = False) -> None:
     fn = _lib.qmoe_moe_decode_phased if phased else _lib.qmoe_moe_decode
@@ -260,7 +345,8 @@ def qmoe_workspace_status(ws, stream=None) -> int:
 __all__ = [
     "QTensor", "MoeLayer", "QmoeError", "lib", "LIB_PATH",
     "qmoe_gemv_affine4", "qmoe_router_topk", "qmoe_expert_ffn", "qmoe_moe_decode",
-    "qmoe_moe_decode_timed", "qmoe_prefill_grouped", "qmoe_prefill_dispatch_offsets",
+    "qmoe_moe_decode_timed", "qmoe_expert_ffn_shared", "qmoe_expert_ffn_routed", "Pool",
+    "PoolStats", "qmoe_prefill_grouped", "qmoe_prefill_dispatch_offsets",
     "qmoe_rmsnorm",
     "qmoe_workspace_bytes",
     "qmoe_router_workspace_bytes", "qmoe_workspace_status",

@@ -146,6 +146,30 @@ qmoe_status qmoe_expert_ffn(const qmoe_moe_layer* L, const uint16_t* h, const in
                          static_cast<uint8_t*>(ws), 0, stream);
 }
 
+qmoe_status qmoe_expert_ffn_shared(const qmoe_moe_layer* L, const uint16_t* h, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  qmoe_status s = check_layer(L);
+  if (s != QMOE_OK) return s;
+  if (!h) return QMOE_ERR_NULL_ARG;
+  if (!al16(h)) return QMOE_ERR_ALIGN;
+  if (!ws || ws_bytes < ws_bytes_layer(L, 1)) return QMOE_ERR_WORKSPACE;
+  return launch_moe_step(*L, h, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                         static_cast<uint8_t*>(ws), kStepShared, stream);
+}
+
+qmoe_status qmoe_expert_ffn_routed(const qmoe_moe_layer* L, const uint16_t* h, const int32_t* idx,
+                                   const float* w, const int32_t* expert_slot,
+                                   const uint16_t* residual, uint16_t* out, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  qmoe_status s = check_layer(L);
+  if (s != QMOE_OK) return s;
+  if (!h || !idx || !w || !out) return QMOE_ERR_NULL_ARG;
+  if (!al16(h) || (residual && (reinterpret_cast<uintptr_t>(residual) & 1u))) return QMOE_ERR_ALIGN;
+  if (!ws || ws_bytes < ws_bytes_layer(L, 1)) return QMOE_ERR_WORKSPACE;
+  return launch_moe_step(*L, h, idx, w, expert_slot, residual, out, nullptr, nullptr,
+                         static_cast<uint8_t*>(ws), kStepRouted, stream);
+}
+
 qmoe_status qmoe_moe_decode(const qmoe_moe_layer* L, const uint16_t* x, const int32_t* expert_slot,
                             int32_t residual, uint16_t* out, int32_t* idx_out, float* w_out,
                             void* ws, size_t ws_bytes, void* stream) {

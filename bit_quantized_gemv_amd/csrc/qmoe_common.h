@@ -215,6 +215,9 @@ constexpr int kBytes = kCntBase + kNCnt * 64;
 }  // namespace ctl
 constexpr size_t kCtlBytes = (size_t)ctl::kBytes;
 
+// Launch modes of the decode step.
+constexpr int kStepFused = 0, kStepPhased = 1, kStepShared = 2, kStepRouted = 3;
+
 __host__ __device__ inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 struct WsLayout {

@@ -88,6 +88,7 @@ struct DecodeArgs {
   int perG;                 // G blocks per expert
   int role0;                // role index of blockIdx.x == 0
   int nowait;               // 1: producers ran in earlier launches (no waits)
+  int s_done;               // 1: the S blocks ran in an earlier launch
 };
 
 __device__ __forceinline__ uint32_t* ctl_of(const DecodeArgs& a) {
@@ -934,7 +935,7 @@ __device__ void role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
     ssh[m] = ld_sb(a.shd.s, a.shd.b, (int64_t)row * Gs + (c >> 1));
   }
   // 2. shared activations once the S blocks are published, shared part
-  if (!a.nowait && !block_wait_flags(flags, a.nS, epoch, ctlw, 2, sys)) return;
+  if (!a.nowait && !a.s_done && !block_wait_flags(flags, a.nS, epoch, ctlw, 2, sys)) return;
   const float* act = act_of(a, blockIdx.x % ctl::kRep);
   stage_a(act, Is, as_sh, ah_sh, threadIdx.x, kBlock);
   __syncthreads();
@@ -1090,13 +1091,17 @@ static void launch_step(const DecodeArgs& a, int blocks, size_t lds, void* strea
     launch_step_kernel<0, 0, 0, 0>(a, blocks, lds, stream, ev0, ev1);
 }
 
-// phased: 0 = one launch with in-kernel waits; 1 = three ordered launches.
+// mode: kStepFused = one launch with in-kernel waits; kStepPhased = three
+// ordered launches; kStepShared = the shared gate/up blocks only;
+// kStepRouted = routed gate/up, down and combine after a kStepShared launch
+// on the same workspace and stream (the last two need a given routing).
 // ev_start/ev_stop (hipEvent_t or null): recorded at the start of the first
 // and the end of the last kernel of the step.
 qmoe_status launch_moe_step(const qmoe_moe_layer& L, const uint16_t* x, const int32_t* idx_in,
                             const float* w_in, const int32_t* slot, const uint16_t* residual,
-                            uint16_t* out, int32_t* idx_out, float* w_out, uint8_t* ws, int phased,
+                            uint16_t* out, int32_t* idx_out, float* w_out, uint8_t* ws, int mode,
                             void* stream, void* ev_start, void* ev_stop) {
+  const int phased = mode == kStepPhased;
   if (!moe_step_supported(L)) return QMOE_ERR_UNSUPPORTED;
   hipEvent_t e0 = reinterpret_cast<hipEvent_t>(ev_start);
   hipEvent_t e1 = reinterpret_cast<hipEvent_t>(ev_stop);
@@ -1105,14 +1110,17 @@ qmoe_status launch_moe_step(const qmoe_moe_layer& L, const uint16_t* x, const in
   a.router = devq(L.router); a.gate = devq(L.gate); a.up = devq(L.up); a.down = devq(L.down);
   a.shg = devq(L.sh_gate); a.shu = devq(L.sh_up); a.shd = devq(L.sh_down);
   a.x = x;
-  a.gamma = idx_in ? nullptr : L.rms_gamma;
+  // with a given routing (or for the shared blocks alone) x is the expert
+  // input h itself: no router, no normalisation
+  const bool given = idx_in || mode == kStepShared;
+  a.gamma = given ? nullptr : L.rms_gamma;
   a.eps = L.rms_eps;
   a.lbias = L.logit_bias;
   a.idx_in = idx_in; a.w_in = w_in; a.slot = slot; a.residual = residual;
   a.out = out; a.idx_out = idx_out; a.w_out = w_out;
   a.ws = ws;
   a.wl = ws_layout(a.E, a.K, a.I, a.Is, 1);
-  a.nR = idx_in ? 0 : cdiv(a.E, kRowsPerUnit);
+  a.nR = given ? 0 : cdiv(a.E, kRowsPerUnit);
   a.nS = a.Is / kRowsPerUnit;
   a.perG = a.I / kRowsPerUnit;
   a.nG = a.K * a.perG;
@@ -1121,6 +1129,19 @@ qmoe_status launch_moe_step(const qmoe_moe_layer& L, const uint16_t* x, const in
   if (router_lds(a.H) > lds) lds = router_lds(a.H);
   if (down_lds(a.I, a.Is) > lds) lds = down_lds(a.I, a.Is);
   a.nowait = phased;
+  a.s_done = 0;
+  if (mode == kStepShared || mode == kStepRouted) {
+    if (mode == kStepRouted && !idx_in) return QMOE_ERR_NULL_ARG;
+    if (mode == kStepShared) {
+      a.role0 = a.nR;
+      launch_step(a, a.nS, lds, stream, e0, e1);
+    } else {
+      a.s_done = 1;
+      a.role0 = a.nR + a.nS;
+      launch_step(a, a.nG + a.nD, lds, stream, e0, e1);
+    }
+    return hipGetLastError() == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
+  }
   if (!phased) {
     a.role0 = 0;
     launch_step(a, a.nR + a.nS + a.nG + a.nD, lds, stream, e0, e1);

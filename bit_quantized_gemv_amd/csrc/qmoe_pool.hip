@@ -1,0 +1,215 @@
+// qmoe_pool.hip -- host-resident expert pool: per layer, a fixed number of
+// device slots (16 for the model) caches routed-expert blobs; the blobs
+// themselves live in pinned host memory.  Replacement is least frequently
+// used over the whole history of the layer (devtrends.cc "Come eseguire un
+// modello da 26 miliardi…", section "Qual è il trucco principale
+// dell'architettura"; remio.ai "TurboFieldfare esegue Mac Gemma 4 26B in
+// 2 GB…", section "Mac Gemma 4 26B entra nello spazio disponibile…"): misses
+// are copied host -> device on a side stream while the shared expert runs.
+//
+// Policy (one layer; a step is one acquire for that layer):
+//   - every needed expert's use count goes up by one and its last use is the
+//     current step, before anything is placed;
+//   - needed experts already in a slot are hits;
+//   - misses, in rank order, take the lowest free slot, else evict the
+//     resident expert that is not needed in this step with the smallest
+//     (use count, last use, expert id).
+// Counts persist across evictions.  Only host bookkeeping and
+// hipMemcpyAsync: no kernels, no device allocation.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <vector>
+
+#include "qmoe.h"
+
+struct qmoe_pool {
+  int32_t layers, experts, slots;
+  size_t blob_bytes;
+  std::vector<const void*> host_blobs;  // [layers * experts] (empty: planning only)
+  std::vector<void*> arena;             // [layers] device slot arenas
+  struct Layer {
+    std::vector<int64_t> uses, last;    // [experts]
+    std::vector<int32_t> slot_of;       // [experts]: slot or -1
+    std::vector<int32_t> held;          // [slots]: expert or -1
+    int64_t step = 0;
+    int32_t* map_host[2] = {nullptr, nullptr};  // pinned expert -> slot staging
+    hipEvent_t map_done[2] = {nullptr, nullptr};  // its last copy has completed
+    int flip = 0;
+  };
+  std::vector<Layer> L;
+  qmoe_pool_stats st;
+};
+
+namespace {
+
+// One LFU step of layer `ly` for the needed experts `need[0..k)`.
+qmoe_status lfu_step(qmoe_pool* p, int32_t ly, const int32_t* need, int32_t k, int32_t* slot_out,
+                     int32_t* hit_out, int32_t* victim_out) {
+  qmoe_pool::Layer& S = p->L[ly];
+  const int64_t now = S.step++;
+  std::vector<char> wanted(p->experts, 0);
+  for (int32_t j = 0; j < k; ++j) {
+    if (need[j] < 0 || need[j] >= p->experts) return QMOE_ERR_BAD_SHAPE;
+    if (wanted[need[j]]) return QMOE_ERR_BAD_SHAPE;  // ids of one step are distinct
+    wanted[need[j]] = 1;
+  }
+  for (int32_t j = 0; j < k; ++j) {
+    S.uses[need[j]] += 1;
+    S.last[need[j]] = now;
+  }
+  for (int32_t j = 0; j < k; ++j) {
+    const int32_t e = need[j];
+    int32_t victim = -1, s = S.slot_of[e];
+    const bool hit = s >= 0;
+    if (!hit) {
+      for (int32_t i = 0; i < p->slots && s < 0; ++i)
+        if (S.held[i] < 0) s = i;
+      if (s < 0) {
+        // evict: smallest (uses, last, id) among residents not needed now
+        for (int32_t i = 0; i < p->slots; ++i) {
+          const int32_t c = S.held[i];
+          if (wanted[c]) continue;
+          if (s < 0) {
+            s = i;
+            continue;
+          }
+          const int32_t b = S.held[s];
+          const bool less = S.uses[c] != S.uses[b]  ? S.uses[c] < S.uses[b]
+                            : S.last[c] != S.last[b] ? S.last[c] < S.last[b]
+                                                     : c < b;
+          if (less) s = i;
+        }
+        if (s < 0) return QMOE_ERR_UNSUPPORTED;  // unreachable with k <= slots
+        victim = S.held[s];
+        S.slot_of[victim] = -1;
+      }
+      S.held[s] = e;
+      S.slot_of[e] = s;
+    }
+    if (slot_out) slot_out[j] = s;
+    if (hit_out) hit_out[j] = hit ? 1 : 0;
+    if (victim_out) victim_out[j] = victim;
+  }
+  return QMOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qmoe_status qmoe_pool_create(int32_t layers, int32_t experts, int32_t slots, size_t blob_bytes,
+                             const void* const* host_blobs, void* const* dev_slot_arena,
+                             qmoe_pool** out) {
+  if (!out) return QMOE_ERR_NULL_ARG;
+  *out = nullptr;
+  if (layers <= 0 || experts <= 0 || slots <= 0 || slots > experts) return QMOE_ERR_BAD_SHAPE;
+  if ((host_blobs == nullptr) != (dev_slot_arena == nullptr)) return QMOE_ERR_NULL_ARG;
+  if (host_blobs && (blob_bytes == 0 || blob_bytes % 256)) return QMOE_ERR_ALIGN;
+  qmoe_pool* p = new qmoe_pool();
+  p->layers = layers;
+  p->experts = experts;
+  p->slots = slots;
+  p->blob_bytes = blob_bytes;
+  memset(&p->st, 0, sizeof(p->st));
+  p->L.resize(layers);
+  for (auto& S : p->L) {
+    S.uses.assign(experts, 0);
+    S.last.assign(experts, -1);
+    S.slot_of.assign(experts, -1);
+    S.held.assign(slots, -1);
+  }
+  if (host_blobs) {
+    p->host_blobs.assign(host_blobs, host_blobs + (size_t)layers * experts);
+    p->arena.assign(dev_slot_arena, dev_slot_arena + layers);
+    for (auto& S : p->L)
+      for (int i = 0; i < 2; ++i) {
+        void* m = nullptr;
+        if (hipHostMalloc(&m, sizeof(int32_t) * experts, hipHostMallocDefault) != hipSuccess) {
+          qmoe_pool_destroy(p);
+          return QMOE_ERR_HIP;
+        }
+        S.map_host[i] = static_cast<int32_t*>(m);
+        if (hipEventCreateWithFlags(&S.map_done[i], hipEventDisableTiming) != hipSuccess) {
+          qmoe_pool_destroy(p);
+          return QMOE_ERR_HIP;
+        }
+      }
+  }
+  *out = p;
+  return QMOE_OK;
+}
+
+qmoe_status qmoe_pool_plan(qmoe_pool* p, int32_t layer, const int32_t* host_idx, int32_t k,
+                           int32_t* slot_out, int32_t* hit_out, int32_t* victim_out) {
+  if (!p || !host_idx) return QMOE_ERR_NULL_ARG;
+  if (layer < 0 || layer >= p->layers || k <= 0 || k > p->slots) return QMOE_ERR_BAD_SHAPE;
+  return lfu_step(p, layer, host_idx, k, slot_out, hit_out, victim_out);
+}
+
+qmoe_status qmoe_pool_acquire(qmoe_pool* p, int32_t layer, const int32_t* host_idx, int32_t k,
+                              int32_t* dev_expert_slot, void* copy_stream, void* ready,
+                              qmoe_pool_stats* st) {
+  if (!p || !host_idx || !dev_expert_slot) return QMOE_ERR_NULL_ARG;
+  if (p->host_blobs.empty()) return QMOE_ERR_UNSUPPORTED;  // planning-only pool
+  if (layer < 0 || layer >= p->layers || k <= 0 || k > QMOE_MAX_TOP_K || k > p->slots)
+    return QMOE_ERR_BAD_SHAPE;
+  int32_t slot[QMOE_MAX_TOP_K], hit[QMOE_MAX_TOP_K], victim[QMOE_MAX_TOP_K];
+  qmoe_status s = lfu_step(p, layer, host_idx, k, slot, hit, victim);
+  if (s != QMOE_OK) return s;
+  hipStream_t cs = reinterpret_cast<hipStream_t>(copy_stream);
+  qmoe_pool::Layer& S = p->L[layer];
+  int32_t nh = 0, nm = 0;
+  for (int32_t j = 0; j < k; ++j) {
+    if (hit[j]) {
+      ++nh;
+      continue;
+    }
+    ++nm;
+    const void* src = p->host_blobs[(size_t)layer * p->experts + host_idx[j]];
+    void* dst = static_cast<uint8_t*>(p->arena[layer]) + (size_t)slot[j] * p->blob_bytes;
+    if (hipMemcpyAsync(dst, src, p->blob_bytes, hipMemcpyHostToDevice, cs) != hipSuccess)
+      return QMOE_ERR_HIP;
+  }
+  // expert -> slot map of the layer (non-resident experts map to slot 0, a
+  // valid address; the kernels only look up the routed experts)
+  // (the staging buffer is rewritten only after its previous copy is done)
+  const int f = S.flip;
+  S.flip ^= 1;
+  if (hipEventSynchronize(S.map_done[f]) != hipSuccess) return QMOE_ERR_HIP;
+  int32_t* m = S.map_host[f];
+  for (int32_t e = 0; e < p->experts; ++e) m[e] = S.slot_of[e] >= 0 ? S.slot_of[e] : 0;
+  if (hipMemcpyAsync(dev_expert_slot, m, sizeof(int32_t) * p->experts, hipMemcpyHostToDevice, cs) !=
+      hipSuccess)
+    return QMOE_ERR_HIP;
+  if (hipEventRecord(S.map_done[f], cs) != hipSuccess) return QMOE_ERR_HIP;
+  if (ready && hipEventRecord(reinterpret_cast<hipEvent_t>(ready), cs) != hipSuccess)
+    return QMOE_ERR_HIP;
+  p->st.hits += nh;
+  p->st.misses += nm;
+  p->st.h2d_bytes += (int64_t)nm * (int64_t)p->blob_bytes;
+  p->st.last_hits = nh;
+  p->st.last_misses = nm;
+  if (st) *st = p->st;
+  return QMOE_OK;
+}
+
+qmoe_status qmoe_pool_stats_get(const qmoe_pool* p, qmoe_pool_stats* st) {
+  if (!p || !st) return QMOE_ERR_NULL_ARG;
+  *st = p->st;
+  return QMOE_OK;
+}
+
+void qmoe_pool_destroy(qmoe_pool* p) {
+  if (!p) return;
+  for (auto& S : p->L)
+    for (int i = 0; i < 2; ++i) {
+      if (S.map_done[i]) hipEventDestroy(S.map_done[i]);
+      if (S.map_host[i]) hipHostFree(S.map_host[i]);
+    }
+  delete p;
+}
+
+}  // extern "C"

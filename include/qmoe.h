@@ -209,6 +209,78 @@ qmoe_status qmoe_workspace_status(void* ws, size_t ws_bytes, int32_t* device_cod
 
 const char* qmoe_status_string(qmoe_status s);
 
+/* ---------------------------------------------------------------------
+ * Split FFN: the shared expert's gate/up first, the rest after the routed
+ * experts' weights are in place, so that host -> device copies of missing
+ * experts (on another stream) overlap the shared expert (devtrends.cc,
+ * section "Qual è il trucco principale dell'architettura").  Run on one
+ * stream and one workspace, in this order, the pair computes exactly what
+ * qmoe_expert_ffn computes (bitwise).
+ * ------------------------------------------------------------------- */
+qmoe_status qmoe_expert_ffn_shared(const qmoe_moe_layer* L, const uint16_t* h,
+                                   void* ws, size_t ws_bytes, void* stream);
+qmoe_status qmoe_expert_ffn_routed(const qmoe_moe_layer* L, const uint16_t* h,
+                                   const int32_t* idx, const float* w,
+                                   const int32_t* expert_slot,
+                                   const uint16_t* residual, uint16_t* out,
+                                   void* ws, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
+ * Host-resident expert pool (devtrends.cc, section "Qual è il trucco
+ * principale dell'architettura": 16 slots per layer, least frequently
+ * used; remio.ai "TurboFieldfare esegue Mac Gemma 4 26B in 2 GB…", section
+ * "Mac Gemma 4 26B entra nello spazio disponibile…").
+ *
+ * Every routed expert blob of every layer sits in pinned host memory
+ * (host_blobs[layer * experts + e], blob_bytes each, allocated with
+ * hipHostMalloc by the caller).  Each layer has a device arena of `slots`
+ * blobs (dev_slot_arena[layer], caller-owned); the layer's gate/up/down
+ * qmoe_qtensors point into it with expert_stride_bytes = blob_bytes, and
+ * the FFN kernels find an expert through the expert -> slot map that
+ * qmoe_pool_acquire writes.
+ *
+ * Replacement, per layer (one acquire is one step): every needed expert's
+ * use count is incremented and its last use set to the step; needed experts
+ * in a slot are hits; misses, in rank order, take the lowest free slot, or
+ * evict the resident expert not needed in this step with the smallest
+ * (use count, last use, id).  Counts are never reset.
+ * ------------------------------------------------------------------- */
+typedef struct qmoe_pool qmoe_pool;
+typedef struct {
+  int64_t hits, misses;       /* cumulative over every acquire */
+  int64_t h2d_bytes;          /* cumulative host -> device bytes */
+  int32_t last_hits, last_misses;
+} qmoe_pool_stats;
+
+/* host_blobs and dev_slot_arena may both be NULL: a planning-only pool
+ * (bookkeeping without copies, usable without a GPU; see qmoe_pool_plan).
+ * Allocates host memory only (bookkeeping and two pinned expert -> slot
+ * staging maps per layer). */
+qmoe_status qmoe_pool_create(int32_t layers, int32_t experts, int32_t slots,
+                             size_t blob_bytes, const void* const* host_blobs,
+                             void* const* dev_slot_arena, qmoe_pool** out);
+
+/* One replacement step of `layer` for the needed experts host_idx[0..k)
+ * (distinct, host memory), without copies.  slot_out/hit_out/victim_out
+ * ([k], host, each may be NULL): the slot of each needed expert, 1 for a
+ * hit, and the expert evicted to make room (-1: none). */
+qmoe_status qmoe_pool_plan(qmoe_pool* pool, int32_t layer, const int32_t* host_idx,
+                           int32_t k, int32_t* slot_out, int32_t* hit_out,
+                           int32_t* victim_out);
+
+/* One replacement step (as qmoe_pool_plan), then on copy_stream: the
+ * missing blobs host -> device into their slots, the layer's expert -> slot
+ * map into dev_expert_slot (int32 [experts], device), and `ready` (a
+ * hipEvent_t, or NULL) recorded after them.  The compute stream must wait
+ * for `ready` before the routed part of the layer.  Slots are overwritten:
+ * work that read this layer's slots must be complete (or ordered before
+ * copy_stream).  st (or NULL) receives the cumulative statistics. */
+qmoe_status qmoe_pool_acquire(qmoe_pool* pool, int32_t layer, const int32_t* host_idx,
+                              int32_t k, int32_t* dev_expert_slot, void* copy_stream,
+                              void* ready, qmoe_pool_stats* st);
+qmoe_status qmoe_pool_stats_get(const qmoe_pool* pool, qmoe_pool_stats* st);
+void qmoe_pool_destroy(qmoe_pool* pool);
+
 #ifdef __cplusplus
 }
 #endif

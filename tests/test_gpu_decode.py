@@ -326,3 +326,28 @@ def test_moe_decode_timed_equals_untimed(torch_cuda, q, big_layer):
     ms = e0.elapsed_time(e1)
     log(f"  timed step kernel {ms * 1e3:.1f} us")
     assert 0 < ms < 100
+
+
+def test_expert_ffn_split_equals_one_launch(torch_cuda, q, big_layer):
+    """Shared gate/up first, routed part second (same stream and workspace):
+    the same bits as qmoe_expert_ffn, with and without an expert->slot map."""
+    torch = torch_cuda
+    lw, ol, dl = big_layer
+    L = dl.layer
+    X = synth.make_tokens(lw.wl, 2, stream=72)
+    idx, w = synth.dirichlet_routing(lw.wl, 2, stream=7)
+    ws = L.new_workspace(1)
+    for t in range(2):
+        h = _dev_u16(torch, X[t])
+        idx_d = torch.from_numpy(idx[t]).cuda()
+        w_d = torch.from_numpy(w[t]).cuda()
+        ref = _expert_ffn(torch, q, dl, X[t], idx[t], w[t], residual=X[1 - t])
+        out = torch.empty(L.hidden, dtype=torch.int16, device="cuda")
+        q.qmoe_expert_ffn_shared(L, h, ws)
+        q.qmoe_expert_ffn_routed(L, h, idx_d, w_d, None, _dev_u16(torch, X[1 - t]), out, ws)
+        assert np.array_equal(to_u16(out), ref)
+        ident = torch.arange(L.n_experts, dtype=torch.int32, device="cuda")
+        q.qmoe_expert_ffn_shared(L, h, ws)
+        q.qmoe_expert_ffn_routed(L, h, idx_d, w_d, ident, _dev_u16(torch, X[1 - t]), out, ws)
+        assert np.array_equal(to_u16(out), ref)
+    assert q.qmoe_workspace_status(ws) == 0

@@ -1,0 +1,154 @@
+"""GPU check of the host-resident expert pool: a stack streamed through
+16 device slots per layer (pinned host blobs, copies on a side stream
+overlapping the shared expert) gives bit-identical outputs to the same
+kernels on resident weights; the pool's trace equals the oracle's LFU
+replay; outputs match the fp64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+import synth.device
+from tests.helpers import bf16_to_f64, log, rel_l2, to_u16
+
+pytestmark = pytest.mark.gpu
+
+WL = synth.WORKLOADS["tiny_streaming_decode"]
+
+
+@pytest.fixture(scope="module")
+def layers():
+    import torch
+
+    assert torch.cuda.is_available()
+    return [synth.make_layer(WL, l) for l in range(WL.layers)]
+
+
+def _flow(torch, q, dls, X, pool=None, slot_maps=None, trace=None):
+    """RMSNorm -> router -> shared gate/up -> (pool acquire) -> routed part,
+    layer after layer, token after token.  Returns every layer's output."""
+    H, K = WL.hidden, WL.top_k
+    compute = torch.cuda.current_stream()
+    copy = torch.cuda.Stream()
+    ws = dls[0].layer.new_workspace(1)
+    rws = torch.zeros(q.qmoe_router_workspace_bytes(WL.n_experts, 1), dtype=torch.uint8,
+                      device="cuda")
+    idx_d = torch.empty(K, dtype=torch.int32, device="cuda")
+    w_d = torch.empty(K, dtype=torch.float32, device="cuda")
+    idx_h = torch.empty(K, dtype=torch.int32, pin_memory=True)
+    ev_idx = torch.cuda.Event()
+    ready = torch.cuda.Event()
+    ready.record(copy)  # create the event before handing it to the library
+    outs = []
+    for t in range(X.shape[0]):
+        x = torch.from_numpy(np.ascontiguousarray(X[t]).view(np.int16)).cuda()
+        per = []
+        for l, dl in enumerate(dls):
+            L = dl.layer
+            h = torch.empty(H, dtype=torch.int16, device="cuda")
+            q.qmoe_rmsnorm(x, dl.gamma, 1e-6, 1, H, h)
+            q.qmoe_router_topk(L.router, dl.logit_bias, h, 1, K, idx_d, w_d, None, rws)
+            smap = None
+            if pool is not None:
+                idx_h.copy_(idx_d, non_blocking=True)
+                ev_idx.record(compute)
+            q.qmoe_expert_ffn_shared(L, h, ws)
+            if pool is not None:
+                ev_idx.synchronize()
+                smap = slot_maps[l]
+                st = pool.acquire(l, idx_h.data_ptr(), K, smap, copy, ready.cuda_event)
+                compute.wait_event(ready)
+            out = torch.empty(H, dtype=torch.int16, device="cuda")
+            q.qmoe_expert_ffn_routed(L, h, idx_d, w_d, smap, x, out, ws)
+            if trace is not None:
+                torch.cuda.synchronize()
+                trace.append((l, idx_d.cpu().numpy().copy(), w_d.cpu().numpy().copy(),
+                              None if smap is None else smap.cpu().numpy().copy(),
+                              None if pool is None else (st.last_hits, st.last_misses)))
+            per.append(to_u16(out))
+            x = out
+        outs.append(per)
+    torch.cuda.synchronize()
+    return outs
+
+
+def test_pool_streaming_equals_resident_and_oracle(layers):
+    import torch
+
+    import bit_quantized_gemv_amd as q
+
+    E, K, S = WL.n_experts, WL.top_k, WL.slots
+    blob = layers[0].layout.nbytes
+    X = synth.make_tokens(WL, WL.tokens, stream=91)
+    prior = [synth.zipf_prior(WL, l) for l in range(WL.layers)]
+
+    # resident: every expert on the device
+    res_dls = [synth.device.DeviceLayer(lw, logit_bias=prior[l]) for l, lw in enumerate(layers)]
+    res_trace = []
+    ref = _flow(torch, q, res_dls, X, trace=res_trace)
+
+    # streamed: pinned host blobs, 16 device slots per layer
+    host = torch.empty((WL.layers * E, blob), dtype=torch.uint8, pin_memory=True)
+    for l, lw in enumerate(layers):
+        host[l * E:(l + 1) * E].copy_(torch.from_numpy(lw.blobs))
+    arenas = [torch.zeros((S, blob), dtype=torch.uint8, device="cuda") for _ in layers]
+    pool = q.Pool(WL.layers, E, S, blob,
+                  [host[i].data_ptr() for i in range(WL.layers * E)],
+                  [a.data_ptr() for a in arenas])
+    slot_maps = [torch.zeros(E, dtype=torch.int32, device="cuda") for _ in layers]
+    str_dls = [synth.device.DeviceLayer(lw, logit_bias=prior[l], blobs=arenas[l])
+               for l, lw in enumerate(layers)]
+    trace = []
+    got = _flow(torch, q, str_dls, X, pool=pool, slot_maps=slot_maps, trace=trace)
+
+    # 1. bit-identical to the resident run (same kernels, other addresses)
+    for t in range(len(X)):
+        for l in range(WL.layers):
+            assert np.array_equal(got[t][l], ref[t][l]), (t, l)
+
+    # 2. the pool's trace equals the oracle's LFU replay of the same needs
+    st = pool.stats()
+    total_hits = 0
+    for l in range(WL.layers):
+        rows = [tr for tr in trace if tr[0] == l]
+        need = np.stack([r[1] for r in rows])
+        rep = oracle.lfu_replay(need, E, S)
+        for step, r in enumerate(rows):
+            _, idx, _, smap, (hits, misses) = r
+            assert hits == int(rep["hit"][step].sum()), (l, step)
+            assert list(smap[idx]) == list(rep["slot"][step]), (l, step)
+        total_hits += rep["hits"]
+    assert st.hits == total_hits and st.hits + st.misses == WL.tokens * WL.layers * K
+    assert st.h2d_bytes == st.misses * blob
+    log(f"  pool hit rate {st.hits / (st.hits + st.misses):.3f}, "
+        f"{st.h2d_bytes / 1e6:.1f} MB host->device")
+
+    # 3. every layer against the oracle on the device's own layer input
+    worst = 0.0
+    for t in range(len(X)):
+        xin = X[t]
+        for l, lw in enumerate(layers):
+            ol = _oracle_cache(lw, prior[l])
+            r = ol.forward(xin, residual=True)
+            _, gidx, gw, _, _ = trace[t * WL.layers + l]
+            if list(gidx) != list(r["idx"]):
+                lg = r["logits"]
+                gap = max(abs(lg[a] - lg[b]) for a, b in zip(gidx, r["idx"]))
+                assert gap <= 1e-3 * max(1.0, abs(lg).max())
+                r = ol.forward(xin, residual=True, force_idx=gidx, force_w=gw.astype(np.float64))
+            e = rel_l2(bf16_to_f64(got[t][l]), bf16_to_f64(r["out"]))
+            worst = max(worst, e)
+            assert e <= 2e-3, (t, l, e)
+            xin = got[t][l]
+    log(f"  worst layer relL2 vs oracle {worst:.2e}")
+    pool.close()
+
+
+_ORC = {}
+
+
+def _oracle_cache(lw, prior):
+    key = id(lw)
+    if key not in _ORC:
+        _ORC[key] = oracle.OracleLayer(lw, logit_bias=prior)
+    return _ORC[key]
