@@ -115,6 +115,10 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill leg")
+    ap.add_argument("--no-stack", action="store_true", help="skip the 30-layer stack leg")
+    ap.add_argument("--streaming", action="store_true",
+                    help="only the expert-streaming leg (30 layers, pinned host experts, "
+                         "16 device slots per layer); prints its own JSON line")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
     ap.add_argument("--phased", action="store_true",
@@ -130,6 +134,10 @@ def main():
     import bit_quantized_gemv_amd as q
     import synth
     import synth.device as sd
+
+    if args.streaming:
+        print(json.dumps(streaming_leg(torch, q, synth, sd)), flush=True)
+        return
 
     wl = synth.WORKLOADS["layer_decode"]
     log("generating layer weights")
@@ -253,6 +261,10 @@ def main():
     }
     if not args.no_prefill:
         res["prefill"] = prefill_leg(torch, q, synth, sd, lw, layers, wl, sptr)
+    if not args.no_stack:
+        del layers
+        torch.cuda.empty_cache()
+        res["stack"] = stack_leg(torch, q, synth, sd, sptr)
     if args.copy_calibration:
         copy_calibration(torch)
     if not args.no_cpu_baseline:
@@ -315,6 +327,158 @@ def prefill_leg(torch, q, synth, sd, lw, layers, wl, sptr, iters: int = 64):
             "algorithmic_bytes": nbytes, "achieved_GBps": nbytes / (us * 1e-6) / 1e9,
             "flops": flops, "achieved_TFLOPs": flops / (us * 1e-6) / 1e12,
             "mfma_f16_peak_TFLOPs": MFMA_F16_PEAK_TFS}
+
+
+def stack_leg(torch, q, synth, sd, sptr, tokens: int = 256, warmup: int = 8):
+    """The 30-layer decode stack (RMSNorm -> router top-8 -> shared + routed
+    FFN -> residual per layer, independent seeded layers, all resident):
+    each token runs 30 single-launch layer steps; every launch records its
+    kernel's start and end."""
+    import ctypes
+
+    st = synth.WORKLOADS["stack30_decode"]
+    log(f"generating {st.layers} stack layers")
+    dls, nbytes = [], 0
+    for l in range(st.layers):
+        lw = synth.make_layer(st, l)
+        nbytes += lw.algorithmic_bytes_decode() + lw.gamma.nbytes
+        dl = sd.DeviceLayer(lw)
+        dl.lw = None  # keep only the device copy
+        dls.append(dl)
+    X = torch.from_numpy(synth.make_tokens(st, tokens, stream=3).view(np.int16)).cuda()
+    H, K = st.hidden, st.top_k
+    buf = [torch.empty(H, dtype=torch.int16, device="cuda") for _ in range(2)]
+    idx = torch.empty(K, dtype=torch.int32, device="cuda")
+    w = torch.empty(K, dtype=torch.float32, device="cuda")
+    ws = dls[0].layer.new_workspace(1)
+    fn = q.lib().qmoe_moe_decode_timed
+    cl = [ctypes.byref(dl.layer.c()) for dl in dls]
+    bp = [b.data_ptr() for b in buf]
+    wsa = (idx.data_ptr(), w.data_ptr(), ws.data_ptr(), ws.numel())
+    n = st.layers
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n * tokens)]
+    stream = torch.cuda.current_stream()
+    for e in ev:
+        e.record(stream)
+    evh = [e.cuda_event for e in ev]
+
+    def token(t, timed):
+        src = X[t].data_ptr()
+        for l in range(n):
+            dst = bp[l & 1]
+            e0 = evh[2 * (t * n + l)] if timed else None
+            e1 = evh[2 * (t * n + l) + 1] if timed else None
+            rc = fn(cl[l], src, None, 1, dst, wsa[0], wsa[1], wsa[2], wsa[3], sptr, e0, e1)
+            if rc:
+                raise q.QmoeError("qmoe_moe_decode_timed", rc)
+            src = dst
+
+    for t in range(warmup):
+        token(t, False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(tokens):
+        token(t, True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if q.qmoe_workspace_status(ws) != 0:
+        raise SystemExit("device wait failure in the stack leg")
+    kern = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(n * tokens)]) * 1e3
+    kern_token_us = float(kern.sum() / tokens)
+    log(f"stack: {tokens / wall:.0f} tokens/s, layer kernel mean {kern.mean():.2f} us")
+    return {"workload": "30-layer MoE decode stack, batch 1, RMSNorm + residual per layer, "
+                        "independent seeded layers, all experts resident",
+            "tokens_per_s": tokens / wall, "us_per_token": wall * 1e6 / tokens,
+            "layer_kernel_us_mean": float(kern.mean()), "kernel_us_per_token": kern_token_us,
+            "algorithmic_bytes_per_token": nbytes,
+            "achieved_GBps_kernels": nbytes / (kern_token_us * 1e-6) / 1e9,
+            "achieved_GBps_wall": nbytes * tokens / wall / 1e9,
+            "frac_of_hbm_peak_kernels": nbytes / (kern_token_us * 1e-6) / 1e9 / HBM_PEAK_GBS}
+
+
+def streaming_leg(torch, q, synth, sd, steps: int = 512):
+    """Expert-streaming decode: the 30-layer stack with every routed expert
+    in pinned host memory and 16 device slots per layer.  Per layer:
+    RMSNorm, router, routing to the host, shared gate/up while the pool
+    copies the missing experts on a side stream, then the routed part."""
+    st = synth.WORKLOADS["streaming_decode"]
+    L, E, K, H, S = st.layers, st.n_experts, st.top_k, st.hidden, st.slots
+    log(f"generating {L} layers into pinned host memory")
+    lws = []
+    host = None
+    for l in range(L):
+        lw = synth.make_layer(st, l)
+        if host is None:
+            blob = lw.layout.nbytes
+            host = torch.empty((L * E, blob), dtype=torch.uint8, pin_memory=True)
+        host[l * E:(l + 1) * E].copy_(torch.from_numpy(lw.blobs))
+        lw.blobs = lw.blobs[:1]  # the host copy now lives in pinned memory
+        lws.append(lw)
+    arenas = [torch.zeros((S, blob), dtype=torch.uint8, device="cuda") for _ in range(L)]
+    dls = [sd.DeviceLayer(lw, blobs=arenas[l]) for l, lw in enumerate(lws)]
+    pool = q.Pool(L, E, S, blob, [host[i].data_ptr() for i in range(L * E)],
+                  [a.data_ptr() for a in arenas])
+    maps = [torch.zeros(E, dtype=torch.int32, device="cuda") for _ in range(L)]
+    X = torch.from_numpy(synth.make_tokens(st, steps, stream=5).view(np.int16)).cuda()
+    compute = torch.cuda.current_stream()
+    copy = torch.cuda.Stream()
+    ws = dls[0].layer.new_workspace(1)
+    rws = torch.zeros(q.qmoe_router_workspace_bytes(E, 1), dtype=torch.uint8, device="cuda")
+    idx = torch.empty(K, dtype=torch.int32, device="cuda")
+    w = torch.empty(K, dtype=torch.float32, device="cuda")
+    idx_h = torch.empty(K, dtype=torch.int32, pin_memory=True)
+    h = torch.empty(H, dtype=torch.int16, device="cuda")
+    buf = [torch.empty(H, dtype=torch.int16, device="cuda") for _ in range(2)]
+    ev_idx = torch.cuda.Event()
+    ready = torch.cuda.Event()
+    ready.record(copy)
+
+    def token(t):
+        x = X[t]
+        for l, dl in enumerate(dls):
+            Ly = dl.layer
+            q.qmoe_rmsnorm(x, dl.gamma, 1e-6, 1, H, h)
+            q.qmoe_router_topk(Ly.router, dl.logit_bias, h, 1, K, idx, w, None, rws)
+            idx_h.copy_(idx, non_blocking=True)
+            ev_idx.record(compute)
+            q.qmoe_expert_ffn_shared(Ly, h, ws)
+            ev_idx.synchronize()
+            s = pool.acquire(l, idx_h.data_ptr(), K, maps[l], copy, ready.cuda_event)
+            compute.wait_event(ready)
+            out = buf[l & 1]
+            q.qmoe_expert_ffn_routed(Ly, h, idx, w, maps[l], x, out, ws)
+            x = out
+        return s
+
+    t0 = time.perf_counter()
+    last = None
+    for t in range(steps):
+        s = token(t)
+        if t == steps // 2:
+            torch.cuda.synchronize()
+            last = (time.perf_counter(), s.hits, s.misses, s.h2d_bytes)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    s = pool.stats()
+    hits, misses = s.hits, s.misses
+    wh = (s.hits - last[1]) / max(1, (s.hits - last[1]) + (s.misses - last[2]))
+    warm_s = t1 - last[0]
+    warm_tokens = steps - steps // 2 - 1
+    res = {"metric": "expert-streaming stack decode tokens/s (pinned host experts, 16-slot LFU)",
+           "value": steps / (t1 - t0), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
+           "higher_is_better": True, "dtype": "f32", "data": "synthetic (seeded)",
+           "config": {"workload": "30-layer MoE decode stack, batch 1, hidden 2816, 128 experts "
+                                  "per layer in pinned host memory, 16 device slots per layer, "
+                                  "Zipf(1.1) log-prior on the router logits"},
+           "hit_rate": hits / (hits + misses), "hit_rate_second_half": wh,
+           "h2d_bytes": s.h2d_bytes,
+           "h2d_GBps": s.h2d_bytes / (t1 - t0) / 1e9,
+           "tokens_per_s_second_half": warm_tokens / warm_s,
+           "h2d_GBps_second_half": (s.h2d_bytes - last[3]) / warm_s / 1e9}
+    pool.close()
+    log(f"streaming: {res['value']:.1f} tokens/s, hit rate {res['hit_rate']:.3f}, "
+        f"H2D {res['h2d_GBps']:.1f} GB/s")
+    return res
 
 
 def copy_calibration(torch, reps: int = 3):
