@@ -114,13 +114,18 @@ __device__ __forceinline__ float gelu_tanh(float z) {
   return 0.5f * z * (1.0f + tanhf(k0 * fmaf(k1 * z * z, z, z)));
 }
 
+// Weights are read once per step: non-temporal loads, so that they do not
+// displace the kernel's code and the small exchanged data from the caches.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ldg16(const uint8_t* p) {
-  return *reinterpret_cast<const uint4*>(p);
+  u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // Packed (scale | bias << 16) fp16 pair at element offset `off`.
 __device__ __forceinline__ uint32_t ld_sb(const uint16_t* s, const uint16_t* b, int64_t off) {
-  return (uint32_t)s[off] | ((uint32_t)b[off] << 16);
+  return (uint32_t)__builtin_nontemporal_load(s + off) |
+         ((uint32_t)__builtin_nontemporal_load(b + off) << 16);
 }
 
 // ----------------------------------------- device-coherent data exchange

@@ -50,8 +50,6 @@ namespace qmoe {
 
 constexpr int kSP = 11;          // gate/up steps per pass (runtime shapes)
 constexpr int kMaxXW = 2;        // activation words per thread kept in registers
-constexpr int kMS = 6;           // shared-down steps per wave (runtime shapes)
-constexpr int kMR = 4;           // routed-down steps per expert (runtime shapes)
 constexpr int kSR = 8;           // router steps per wave per pass (runtime shapes)
 constexpr uint64_t kWaitTicks = 20000000ull;  // 0.2 s of the 100 MHz clock
 // Blocks whose first weight loads are not on the critical path hold them
@@ -62,7 +60,7 @@ constexpr uint64_t kHoldTicks = 0;
 // LDS "sys" words at the start of every block's LDS
 constexpr int kSysEpoch = 0, kSysOk = 1, kSysIdx = 8, kSysW = 16, kSysRed = 32;
 constexpr int kSysTkIdx = 96, kSysTkW = 160;  // per-wave top-k of the standalone router
-constexpr int kSysBytes = 1024;
+constexpr int kSysBytes = 768;
 
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ inline size_t al16(size_t n) { return (n + 15) & ~(size_t)15; }
@@ -116,21 +114,24 @@ __device__ __forceinline__ uint32_t launch_epoch() {
   return e ? e : 0x80000000u;
 }
 
-// One full wave: wait until flags[0..n) all equal `epoch`.  Polling reads
-// one sentinel (the flag of the last producer, which is usually the last to
-// be raised) until it is set and only then checks all of them, so that
-// waiting blocks add almost no memory traffic.
+// One full wave: wait until flags[0..n) all equal `epoch`.  Every poll reads
+// all n flags at once (a few loads per lane), so the wait ends one round
+// trip after the last flag is raised.
 constexpr int kPollSleep = 6;  // s_sleep units (64 cycles) between polls
 __device__ bool wave_wait_flags(const uint32_t* flags, int n, uint32_t epoch, uint32_t* ctlw,
                                 uint32_t code) {
   const int lane = threadIdx.x & 63;
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  // a polling wave issues ahead of the bulk weight loads of its CU
+  __builtin_amdgcn_s_setprio(2);
   for (int it = 0;; ++it) {
-    uint32_t sent = __builtin_amdgcn_readfirstlane(ld_dev(flags + n - 1));
-    if (sent == epoch) {
+    {
       bool ok = true;
       for (int i = lane; i < n; i += 64) ok = ok && ld_dev(flags + i) == epoch;
-      if (__all(ok)) return true;
+      if (__all(ok)) {
+        __builtin_amdgcn_s_setprio(0);
+        return true;
+      }
     }
     if ((it & 15) == 15) {
       if (ld_dev(ctlw + ctl::kError) != 0) return false;
@@ -148,12 +149,12 @@ __device__ __forceinline__ void hold_until(uint64_t t0, uint64_t ticks) {
   while (__builtin_amdgcn_s_memrealtime() - t0 < ticks) __builtin_amdgcn_s_sleep(1);
 }
 
-// Whole block: wave 0 waits, the others meet it at a barrier.
+// Whole block: wave `pw` waits, the others meet it at a barrier.
 __device__ bool block_wait_flags(const uint32_t* flags, int n, uint32_t epoch, uint32_t* ctlw,
-                                 uint32_t code, uint32_t* sys) {
-  if (threadIdx.x < 64) {
+                                 uint32_t code, uint32_t* sys, int pw = 0) {
+  if ((int)(threadIdx.x >> 6) == pw) {
     bool ok = wave_wait_flags(flags, n, epoch, ctlw, code);
-    if (threadIdx.x == 0) sys[kSysOk] = ok ? 1u : 0u;
+    if ((threadIdx.x & 63) == 0) sys[kSysOk] = ok ? 1u : 0u;
   }
   __syncthreads();
   bool ok = sys[kSysOk] != 0;
@@ -263,8 +264,8 @@ __device__ void wave_topk(const float* lg, int E, int K, int32_t* idx_s, float* 
 
 // One wave: wait until all E tagged logits of one replica carry `epoch`
 // (each is (epoch << 32) | fp32 bits, written with one 64-bit store), then
-// top-k on them.  The poll reads the last expert's tag until it is current,
-// then all of them.  In a launch that follows its producers, no waiting.
+// top-k on them.  Every poll reads all of them.  In a launch that follows
+// its producers, no waiting.
 template <int NV>
 __device__ bool wave_routing(const DecodeArgs& a, uint32_t epoch, int32_t* idx_s, float* w_s,
                              bool write_out) {
@@ -274,26 +275,17 @@ __device__ bool wave_routing(const DecodeArgs& a, uint32_t epoch, int32_t* idx_s
   uint32_t* ctlw = ctl_of(a);
   float v[NV];
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+  __builtin_amdgcn_s_setprio(2);  // issue ahead of the CU's bulk weight loads
   for (int it = 0;; ++it) {
-    bool ready = a.nowait;
-    if (!ready) {
-      uint64_t t = ld_dev(tag + a.E - 1);
-      ready = __builtin_amdgcn_readfirstlane((uint32_t)(t >> 32)) == epoch;
-    }
-    if (ready) {
-      bool ok = true;
+    bool ok = true;
 #pragma unroll
-      for (int m = 0; m < NV; ++m) {
-        int e = lane + 64 * m;
-        v[m] = -INFINITY;
-        if (e < a.E) {
-          uint64_t t = ld_dev(tag + e);
-          v[m] = __uint_as_float((uint32_t)t);
-          ok = ok && (a.nowait || (uint32_t)(t >> 32) == epoch);
-        }
-      }
-      if (__all(ok)) break;
+    for (int m = 0; m < NV; ++m) {
+      const int e = lane + 64 * m;
+      const uint64_t t = ld_dev(tag + min(e, a.E - 1));
+      v[m] = e < a.E ? __uint_as_float((uint32_t)t) : -INFINITY;
+      ok = ok && (a.nowait || (uint32_t)(t >> 32) == epoch);
     }
+    if (__all(ok)) break;
     if ((it & 15) == 15) {
       if (ld_dev(ctlw + ctl::kError) != 0) return false;
       if (__builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
@@ -303,6 +295,7 @@ __device__ bool wave_routing(const DecodeArgs& a, uint32_t epoch, int32_t* idx_s
     }
     __builtin_amdgcn_s_sleep(kPollSleep);
   }
+  __builtin_amdgcn_s_setprio(0);
   wave_topk_vals<NV>(v, a.E, a.K, idx_s, w_s, write_out ? a.idx_out : nullptr,
                      write_out ? a.w_out : nullptr);
   return true;
@@ -590,23 +583,24 @@ __device__ __forceinline__ void rows4_run(const DevQ (&m)[NM], int row0, int row
 }
 
 // LDS carve-ups (bytes).  Gate/up: sys | xs pairs (H*2) | xh (H/32 floats)
-// | per-wave scale tables (4 waves x 8 rows x H/64 words).
+// | per-wave scale tables (4 waves x 16 rows x H/64 words).
 __host__ __device__ inline size_t gu_xh_off(int H) { return kSysBytes + (size_t)H * 2; }
 __host__ __device__ inline size_t gu_sb_off(int H) { return al16(gu_xh_off(H) + (size_t)(H / 32) * 4); }
-__host__ __device__ inline size_t gu_sb_words(int H) { return (size_t)kRowsPerUnit * (H / 64); }
+// (room for two row-blocks: the step's gate/up waves hold 16 rows)
+__host__ __device__ inline size_t gu_sb_words(int H) { return (size_t)2 * kRowsPerUnit * (H / 64); }
 __host__ __device__ inline size_t gu_lds(int H) {
   return gu_sb_off(H) + (size_t)kWavesPerBlock * gu_sb_words(H) * 4;
 }
 __host__ __device__ inline size_t router_lds(int H) {
   return kSysBytes + (size_t)H * 4 + (size_t)(H / 16) * 4;
 }
-// Down: sys | a_s (Is floats) | its chunk sums | per-wave a_k (I floats) + sums
-__host__ __device__ inline size_t down_w_off(int Is) {
-  return al16(kSysBytes + (size_t)Is * 4 + (size_t)(Is / 32) * 4);
+// Down: sys | a_s (Is floats) | a_k (K x I floats) | chunk sums of a_s
+// (Is/32) | chunk sums of a_k (K x I/32): every activation of the step.
+__host__ __device__ inline size_t down_ah_off(int I, int Is, int K) {
+  return kSysBytes + ((size_t)Is + (size_t)K * I) * 4;
 }
-__host__ __device__ inline size_t down_w_stride(int I) { return al16((size_t)I * 4 + (size_t)(I / 32) * 4); }
-__host__ __device__ inline size_t down_lds(int I, int Is) {
-  return down_w_off(Is) + (size_t)kWavesPerBlock * down_w_stride(I);
+__host__ __device__ inline size_t down_lds(int I, int Is, int K) {
+  return down_ah_off(I, Is, K) + ((size_t)Is + (size_t)K * I) / 32 * 4;
 }
 
 // ======================================================= qmoe_gemv_affine4
@@ -785,6 +779,8 @@ constexpr int kSysLg = 64;  // sys words: the router block's 8 logits
 
 template <int HC>
 __device__ void role_router(const DecodeArgs& a, int b, uint8_t* smem, uint32_t epoch) {
+  // the router is on every other block's critical path: its waves issue first
+  __builtin_amdgcn_s_setprio(3);
   uint32_t* sys = reinterpret_cast<uint32_t*>(smem);
   const int H = HC ? HC : a.H;
   float4* xr = reinterpret_cast<float4*>(smem + kSysBytes);
@@ -806,9 +802,21 @@ __device__ void role_router(const DecodeArgs& a, int b, uint8_t* smem, uint32_t 
   }
 }
 
-// Gate/up of one row-block of 8 rows: wave w computes matrix (w & 1: gate,
-// up) over column half (w >> 1); the block sums the halves and applies the
+// Gate/up of 16 rows (two row-blocks of 8): wave w computes matrix (w & 1:
+// gate, up) over column half (w >> 1) for both row-blocks, whose loads are
+// all issued before any math; the block sums the halves and applies the
 // GELU gating.  expert_rank < 0: shared expert.
+constexpr int kGuRows = 2 * kRowsPerUnit;
+
+// The same matrix seen from 8 rows further down.
+__device__ __forceinline__ DevQ rows_below(DevQ m, int H) {
+  const int G = H / 64;
+  m.q += (int64_t)kRowsPerUnit * (H / 2);
+  m.s += (int64_t)kRowsPerUnit * G;
+  m.b += (int64_t)kRowsPerUnit * G;
+  return m;
+}
+
 template <int HC, int NV>
 __device__ void role_gate_up(const DecodeArgs& a, int expert_rank, int rb, int rows,
                              uint8_t* smem, uint32_t epoch, uint64_t t_start) {
@@ -820,18 +828,19 @@ __device__ void role_gate_up(const DecodeArgs& a, int expert_rank, int rb, int r
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int mi = wave & 1, half = wave >> 1;
   uint32_t* sbl = reinterpret_cast<uint32_t*>(smem + gu_sb_off(H)) + wave * gu_sb_words(H);
-  const int row0 = rb * kRowsPerUnit;
+  const int row0 = rb * kGuRows;  // rows is a multiple of 16: both row-blocks are whole
   const int CWh = H / 64;  // chunks per column half
   XRegs X;
   x_load(X, a.x, H);
-  DevQ m[1];
+  DevQ m[2];
   size_t dst;  // element offset inside an activation replica
-  float acc[1];
+  float acc[2];
   if (expert_rank < 0) {
     hold_until(t_start, kHoldTicks);
     m[0] = mi ? a.shu : a.shg;
+    m[1] = rows_below(m[0], H);
     dst = 0;
-    rows4_run<1, HC / 64>(m, row0, rows, H, half * CWh, CWh, xs, xh, sbl,
+    rows4_run<2, HC / 64>(m, row0, rows, H, half * CWh, CWh, xs, xh, sbl,
                           [&] {
                             float inv = a.gamma ? x_inv_rms(X, a.x, H, a.eps, red) : 1.f;
                             x_stage<true>(X, a.x, a.gamma, inv, H, xs, xh);
@@ -847,150 +856,234 @@ __device__ void role_gate_up(const DecodeArgs& a, int expert_rank, int rb, int r
     int e = reinterpret_cast<int32_t*>(sys + kSysIdx)[expert_rank];
     int s = a.slot ? a.slot[e] : e;
     m[0] = devq_at(mi ? a.up : a.gate, s);
+    m[1] = rows_below(m[0], H);
     dst = (size_t)a.Is + (size_t)expert_rank * a.I;
-    rows4_run<1, HC / 64>(m, row0, rows, H, half * CWh, CWh, xs, xh, sbl, [] {}, acc);
+    rows4_run<2, HC / 64>(m, row0, rows, H, half * CWh, CWh, xs, xh, sbl, [] {}, acc);
   }
-  if ((lane >> 3) == 0) red[wave * 8 + (lane & 7)] = acc[0];
+  if ((lane >> 3) == 0) {
+    red[(wave * 2 + 0) * 8 + (lane & 7)] = acc[0];
+    red[(wave * 2 + 1) * 8 + (lane & 7)] = acc[1];
+  }
   __syncthreads();
-  // a = gelu(g) * u for the 8 rows, stored in every activation replica
-  const int t = threadIdx.x & 7, rep = threadIdx.x >> 3;
-  if (rep < ctl::kRep && row0 + t < rows) {
-    float g = red[0 * 8 + t] + red[2 * 8 + t];
-    float u = red[1 * 8 + t] + red[3 * 8 + t];
+  // a = gelu(g) * u for the 16 rows, stored in every activation replica
+  const int t = threadIdx.x & 15, rep = threadIdx.x >> 4;
+  if (rep < ctl::kRep) {
+    const int k = t >> 3, rr = t & 7;
+    float g = red[((0 * 2 + k) * 8) + rr] + red[((2 * 2 + k) * 8) + rr];
+    float u = red[((1 * 2 + k) * 8) + rr] + red[((3 * 2 + k) * 8) + rr];
     st_dev(act_of(a, rep) + dst + row0 + t, gelu_tanh(g) * u);
   }
 }
 
-// fp32 activations a[n] (device-coherent 16-byte reads) -> even/odd LDS
-// layout as[(2j+e)*CH + c], ah[c] = chunk sums.  `nthr` threads from `t`.
-__device__ __forceinline__ void stage_a(const float* a, int n, float4* as, float* ah, int t,
-                                        int nthr) {
-  const int CH = n / 32, Wn = n / 8;
-  for (int v0 = 0; v0 < Wn; v0 += nthr) {
-    int v = v0 + t;
-    bool ok = v < Wn;
-    float4 lo = ld_dev16(a, (uint32_t)n * 4, (uint32_t)v * 32);
-    float4 hi = ld_dev16(a, (uint32_t)n * 4, (uint32_t)v * 32 + 16);
-    float s = ((lo.x + lo.y) + (lo.z + lo.w)) + ((hi.x + hi.y) + (hi.z + hi.w));
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    if (ok) {
-      int c = v >> 2, j = v & 3;
-      as[(2 * j) * CH + c] = make_float4(lo.x, lo.z, hi.x, hi.z);
-      as[(2 * j + 1) * CH + c] = make_float4(lo.y, lo.w, hi.y, hi.w);
-      if (j == 0) ah[c] = s;
+// Activations [off, off + n) of a replica (fp32) -> LDS in one pass: each
+// thread issues all its 16-byte device-coherent loads before it uses any,
+// so a pass costs one round trip.  The run is a sequence of segments of
+// `seg` values (the shared activations, or one expert's): per segment
+// (CH = seg/32 chunks), word v = 4c + j (8 values) goes to the even/odd
+// layout as[(2j+e)*CH + c] and ah[c] is the sum of chunk c.  The caller
+// passes the run's value and chunk-sum bases.
+constexpr int kStageUnroll = 4;  // words (8 floats) per thread per pass
+__device__ __forceinline__ void stage_run(const float* act, int off, int n, int seg, float4* as,
+                                          float* ah) {
+  const int Wn = n / 8, Wseg = seg / 8, CH = seg / 32;
+  const uint32_t nbytes = (uint32_t)(off + n) * 4;
+  for (int v0 = 0; v0 < Wn; v0 += kStageUnroll * kBlock) {
+    float4 lo[kStageUnroll], hi[kStageUnroll];
+#pragma unroll
+    for (int u = 0; u < kStageUnroll; ++u) {
+      const uint32_t v = (uint32_t)(v0 + u * kBlock + threadIdx.x);
+      lo[u] = ld_dev16(act, nbytes, (uint32_t)off * 4 + v * 32);  // past the end: zeros
+      hi[u] = ld_dev16(act, nbytes, (uint32_t)off * 4 + v * 32 + 16);
+    }
+#pragma unroll
+    for (int u = 0; u < kStageUnroll; ++u) {
+      const int v = v0 + u * kBlock + threadIdx.x;
+      float s = ((lo[u].x + lo[u].y) + (lo[u].z + lo[u].w)) +
+                ((hi[u].x + hi[u].y) + (hi[u].z + hi[u].w));
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      if (v < Wn) {
+        const int k = v / Wseg, vl = v - k * Wseg;
+        float4* a4 = as + (size_t)k * seg / 4;
+        const int c = vl >> 2, j = vl & 3;
+        a4[(2 * j) * CH + c] = make_float4(lo[u].x, lo[u].z, hi[u].x, hi[u].z);
+        a4[(2 * j + 1) * CH + c] = make_float4(lo[u].y, lo[u].w, hi[u].y, hi[u].w);
+        if (j == 0) ah[k * CH + c] = s;
+      }
     }
   }
 }
 
-// One down task: chunk c of a row of a 4-bit matrix against staged fp32
-// activations; returns s*sum(q a) + b*sum(a).
-__device__ __forceinline__ float down_chunk(uint4 w, uint32_t sb, const float4* as, const float* ah,
-                                            int CH, int c) {
-  float a0 = 0.f, a1 = 0.f;
-  dot_word4_f32(w.x, as[c], as[CH + c], a0, a1);
-  dot_word4_f32(w.y, as[2 * CH + c], as[3 * CH + c], a0, a1);
-  dot_word4_f32(w.z, as[4 * CH + c], as[5 * CH + c], a0, a1);
-  dot_word4_f32(w.w, as[6 * CH + c], as[7 * CH + c], a0, a1);
-  // the fp8 conversion gave q * 2^-9: fold 2^9 into the scale
-  return fmaf(512.0f * half_to_f32(sb & 0xffffu), a0 + a1, half_to_f32(sb >> 16) * ah[c]);
+// One down task of a lane: chunk c (32 inputs) of the 8 rows [row0, row0+8)
+// of a 4-bit matrix.  The lane reads the chunk's staged activations once
+// and applies them to all 8 rows.
+struct DTask {
+  uint4 w[kRowsPerUnit];
+  uint32_t sb[kRowsPerUnit];
+};
+
+__device__ __forceinline__ void dtask_load(DTask& T, const DevQ& W, int row0, int CH, int c) {
+  const int G = CH / 2;
+#pragma unroll
+  for (int r = 0; r < kRowsPerUnit; ++r) {
+    T.w[r] = ldg16(W.q + ((int64_t)(row0 + r) * CH + c) * 16);
+    T.sb[r] = ld_sb(W.s, W.b, (int64_t)(row0 + r) * G + (c >> 1));
+  }
 }
 
-// Down projections + combine for output rows [8b, 8b+8).  Order: shared
-// weights (held back briefly) -> shared activations once the shared gate/up
-// blocks are done, and the shared part -> routing -> routed weights of this
-// wave's experts -> each expert as soon as its gate/up blocks are done.
-// The shared part comes first so that its waits and activation loads are
-// not queued behind the routed weights.
-// IC/ISC: expert and shared intermediate sizes when known (0: runtime).
+// acc[r] += wgt * (s * sum(q a) + b * sum(a)) over the chunk, for the 8 rows.
+__device__ __forceinline__ void dtask_acc(const DTask& T, const float4* as, const float* ah, int CH,
+                                          int c, float wgt, float (&acc)[kRowsPerUnit]) {
+  float4 x[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x[i] = as[i * CH + c];
+  const float hs = ah[c];
+#pragma unroll
+  for (int r = 0; r < kRowsPerUnit; ++r) {
+    float a0 = 0.f, a1 = 0.f;
+    dot_word4_f32(T.w[r].x, x[0], x[1], a0, a1);
+    dot_word4_f32(T.w[r].y, x[2], x[3], a0, a1);
+    dot_word4_f32(T.w[r].z, x[4], x[5], a0, a1);
+    dot_word4_f32(T.w[r].w, x[6], x[7], a0, a1);
+    // the fp8 conversion gave q * 2^-9: fold 2^9 into the scale
+    float v = fmaf(512.0f * half_to_f32(T.sb[r] & 0xffffu), a0 + a1,
+                   half_to_f32(T.sb[r] >> 16) * hs);
+    acc[r] = fmaf(wgt, v, acc[r]);
+  }
+}
+
+// Sum acc[0..8) of every lane of the block, per row; threads 0..7 return
+// rows 0..7 (fixed order: a reduce-scatter over the wave, then the waves
+// in turn).
+__device__ float rows8_block_sum(float (&acc)[kRowsPerUnit], float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float v4[4], v2[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool hi = lane & 32;
+    float send = hi ? acc[i] : acc[4 + i];
+    float keep = hi ? acc[4 + i] : acc[i];
+    v4[i] = keep + __shfl_xor(send, 32);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const bool hi = lane & 16;
+    float send = hi ? v4[i] : v4[2 + i];
+    float keep = hi ? v4[2 + i] : v4[i];
+    v2[i] = keep + __shfl_xor(send, 16);
+  }
+  float v;
+  {
+    const bool hi = lane & 8;
+    float send = hi ? v2[0] : v2[1];
+    float keep = hi ? v2[1] : v2[0];
+    v = keep + __shfl_xor(send, 8);
+  }
+  // lane l now holds row (l >> 3) & 7 over 8 of the lanes; finish the wave
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 1);
+  __syncthreads();
+  if ((lane & 7) == 0) red[wave * 8 + (lane >> 3)] = v;
+  __syncthreads();
+  float s = 0.f;
+  if (threadIdx.x < kRowsPerUnit)
+    for (int w = 0; w < kWavesPerBlock; ++w) s += red[w * 8 + threadIdx.x];
+  return s;
+}
+
+// Down projections + combine for output rows [8b, 8b+8).  The block's 256
+// lanes own chunk tasks of all 8 rows: task t < K*CHk is routed (expert
+// rank k = t / CHk, chunk c), the next CHs tasks are the shared chunks.
+// Order: shared-down weights -> routing -> at once the routed-down weights
+// (they stream while the gate/up blocks work) -> shared activations once
+// the shared gate/up blocks are done, shared part -> one wait for the
+// gate/up blocks of all experts, their activations in one pass, routed part
+// -> combine.  Under the load of the weight streams a dependent memory
+// access takes microseconds, so the routing is fetched before the stream
+// starts, the waits are polled by the last wave (its tasks are shared ones,
+// loaded early) and every staging is one round trip.  IC/ISC: expert and
+// shared intermediate sizes when known (0: runtime).
 template <int IC, int ISC, int NV>
 __device__ void role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t epoch,
                           uint64_t t_start) {
   uint32_t* sys = reinterpret_cast<uint32_t*>(smem);
   const int K = a.K;
   const int I = IC ? IC : a.I, Is = ISC ? ISC : a.Is;
-  const int CHk = I / 32, CHs = Is / 32, Gk = I / 64, Gs = Is / 64;
-  const int Sk = cdiv(CHk, kSlots);
-  constexpr int MS = ISC ? cdiv(cdiv(ISC / 32, kSlots), kWavesPerBlock) : kMS;
-  constexpr int MR = IC ? cdiv(IC / 32, kSlots) : kMR;
+  const int CHk = I / 32, CHs = Is / 32;
+  // tasks per lane: one pass with all loads issued at once when the shapes
+  // are known and fit; otherwise pass by pass
+  constexpr bool kOnePass = IC && ISC && QMOE_MAX_TOP_K * (IC / 32) + ISC / 32 <= kBlock;
   float4* as_sh = reinterpret_cast<float4*>(smem + kSysBytes);
-  float* ah_sh = reinterpret_cast<float*>(as_sh + Is / 4);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 7, p = lane >> 3;
-  float4* as_w = reinterpret_cast<float4*>(smem + down_w_off(Is) + (size_t)wave * down_w_stride(I));
-  float* ah_w = reinterpret_cast<float*>(as_w + I / 4);
+  float* ah_sh = reinterpret_cast<float*>(smem + down_ah_off(I, Is, K));
+  const float4* ask = as_sh + Is / 4;
+  const float* ahk = ah_sh + Is / 32;
+  constexpr int kPollWave = kWavesPerBlock - 1;
   float* red = reinterpret_cast<float*>(sys + kSysRed);
   uint32_t* ctlw = ctl_of(a);
   const uint32_t* flags =
       reinterpret_cast<const uint32_t*>(rep_of(a, ctl::kFlagBase, blockIdx.x % ctl::kRep));
-  const int row = b * kRowsPerUnit + r;  // H is a multiple of 64: always valid
+  const int row0 = b * kRowsPerUnit;  // H is a multiple of 64: all 8 rows exist
+  const int nrt = K * CHk, ntask = nrt + CHs;
+  const int t = threadIdx.x;
+  const bool routed = t < nrt;
+  float acc[kRowsPerUnit];
+#pragma unroll
+  for (int r = 0; r < kRowsPerUnit; ++r) acc[r] = 0.f;
+  DTask T;
 
-  // 1. shared-down weights: wave w takes steps w, w+4, ...
+  // 1. shared-down weights
   hold_until(t_start, kHoldTicks);
-  uint4 wsh[MS];
-  uint32_t ssh[MS];
-#pragma unroll
-  for (int m = 0; m < MS; ++m) {
-    int c = min((wave + m * kWavesPerBlock) * kSlots + p, CHs - 1);
-    wsh[m] = ldg16(a.shd.q + ((int64_t)row * CHs + c) * 16);
-    ssh[m] = ld_sb(a.shd.s, a.shd.b, (int64_t)row * Gs + (c >> 1));
-  }
-  // 2. shared activations once the S blocks are published, shared part
-  if (!a.nowait && !a.s_done && !block_wait_flags(flags, a.nS, epoch, ctlw, 2, sys)) return;
-  const float* act = act_of(a, blockIdx.x % ctl::kRep);
-  stage_a(act, Is, as_sh, ah_sh, threadIdx.x, kBlock);
-  __syncthreads();
-  float acc = 0.f;
-#pragma unroll
-  for (int m = 0; m < MS; ++m) {
-    int c = (wave + m * kWavesPerBlock) * kSlots + p;
-    if (c < CHs) acc += down_chunk(wsh[m], ssh[m], as_sh, ah_sh, CHs, c);
-  }
-  // 3. routing, then the routed-down weights of this wave's experts (k, k+4)
+  if (kOnePass && !routed) dtask_load(T, a.shd, row0, CHs, min(t - nrt, CHs - 1));
+  // 2. routing, then at once the routed-down weights
   if (!block_routing<NV>(a, epoch, sys, b == 0)) return;
   const int32_t* idx_s = reinterpret_cast<const int32_t*>(sys + kSysIdx);
   const float* w_s = reinterpret_cast<const float*>(sys + kSysW);
-  uint4 wrt[2][MR];
-  uint32_t srt[2][MR];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    int k = min(wave + j * kWavesPerBlock, K - 1);
-    int e = idx_s[k];
-    DevQ d = devq_at(a.down, a.slot ? a.slot[e] : e);
-#pragma unroll
-    for (int i = 0; i < MR; ++i) {
-      int c = min(min(i, Sk - 1) * kSlots + p, CHk - 1);
-      wrt[j][i] = ldg16(d.q + ((int64_t)row * CHk + c) * 16);
-      srt[j][i] = ld_sb(d.s, d.b, (int64_t)row * Gk + (c >> 1));
+  if (kOnePass && routed) {
+    const int k = t / CHk, c = t - k * CHk;
+    const int e = idx_s[k];
+    dtask_load(T, devq_at(a.down, a.slot ? a.slot[e] : e), row0, CHk, c);
+  }
+  // 3. shared activations once the S blocks are published, shared part
+  if (!a.nowait && !a.s_done &&
+      !block_wait_flags(flags, a.nS, epoch, ctlw, 2, sys, kPollWave))
+    return;
+  stage_run(act_of(a, blockIdx.x % ctl::kRep), 0, Is, Is, as_sh, ah_sh);
+  __syncthreads();
+  if (kOnePass) {
+    if (!routed && t < ntask) dtask_acc(T, as_sh, ah_sh, CHs, t - nrt, 1.0f, acc);
+  } else {
+    for (int c = t; c < CHs; c += kBlock) {
+      DTask U;
+      dtask_load(U, a.shd, row0, CHs, c);
+      dtask_acc(U, as_sh, ah_sh, CHs, c, 1.0f, acc);
     }
   }
-  // 4. each wave: its experts in turn, as soon as their G blocks are done
-  bool ok = true;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    int k = wave + j * kWavesPerBlock;
-    if (k < K && ok) {
-      if (!a.nowait) ok = wave_wait_flags(flags + a.nS + k * a.perG, a.perG, epoch, ctlw, 3);
-      if (ok) {
-        stage_a(act + Is + (size_t)k * I, I, as_w, ah_w, lane, 64);
-        float part = 0.f;
-#pragma unroll
-        for (int i = 0; i < MR; ++i) {
-          int c = i * kSlots + p;
-          if (i < Sk && c < CHk) part += down_chunk(wrt[j][i], srt[j][i], as_w, ah_w, CHk, c);
-        }
-        acc = fmaf(w_s[k], part, acc);
-      }
+  // 4. one wait for the G blocks of all K experts, their activations in one
+  //    pass, routed part
+  if (!a.nowait &&
+      !block_wait_flags(flags + a.nS, K * a.perG, epoch, ctlw, 3, sys, kPollWave))
+    return;
+  stage_run(act_of(a, blockIdx.x % ctl::kRep), Is, K * I, I, as_sh + Is / 4, ah_sh + Is / 32);
+  __syncthreads();
+  if (kOnePass) {
+    if (routed) {
+      const int k = t / CHk, c = t - k * CHk;
+      dtask_acc(T, ask + (size_t)k * I / 4, ahk + k * CHk, CHk, c, w_s[k], acc);
+    }
+  } else {
+    for (int u = t; u < nrt; u += kBlock) {
+      const int k = u / CHk, c = u - k * CHk;
+      const int e = idx_s[k];
+      DTask U;
+      dtask_load(U, devq_at(a.down, a.slot ? a.slot[e] : e), row0, CHk, c);
+      dtask_acc(U, ask + (size_t)k * I / 4, ahk + k * CHk, CHk, c, w_s[k], acc);
     }
   }
-  // 5. combine: row sums, then the 4 waves in order, residual, bf16
-  acc = rowblock_sum(acc);
-  __syncthreads();
-  if (p == 0) red[wave * 8 + r] = acc;
-  __syncthreads();
-  if (threadIdx.x < 8) {
-    int rr = b * kRowsPerUnit + threadIdx.x;
-    float s = 0.f;
-    for (int w = 0; w < kWavesPerBlock; ++w) s += red[w * 8 + threadIdx.x];
+  // 5. combine: rows over the block, residual, bf16
+  float s = rows8_block_sum(acc, red);
+  if (threadIdx.x < kRowsPerUnit) {
+    const int rr = row0 + threadIdx.x;
     if (a.residual) s += bf16_to_f32(a.residual[rr]);
     a.out[rr] = f32_to_bf16(s);
   }
@@ -1061,11 +1154,11 @@ qmoe_status launch_router(const qmoe_qtensor& Wr, const float* lbias, const uint
 }
 
 bool moe_step_supported(const qmoe_moe_layer& L) {
-  const int Ss = cdiv(L.shared_inter / 32, kSlots), Sk = cdiv(L.inter / 32, kSlots);
   const int nR = cdiv(L.n_experts, kRowsPerUnit);
-  const int perG = L.inter / kRowsPerUnit;
-  const int nS = L.shared_inter / kRowsPerUnit;
-  return Ss <= kMS * kWavesPerBlock && Sk <= kMR && L.hidden / 8 <= kMaxXW * kBlock && nR <= 64 &&
+  const int perG = L.inter / kGuRows;
+  const int nS = L.shared_inter / kGuRows;
+  return L.hidden / 8 <= kMaxXW * kBlock && nR <= 64 &&
+         down_lds(L.inter, L.shared_inter, L.top_k) <= 65536 &&
          L.n_experts * 8 <= ctl::kRepStride && nS + L.top_k * perG <= ctl::kMaxFlags;
 }
 
@@ -1121,13 +1214,13 @@ qmoe_status launch_moe_step(const qmoe_moe_layer& L, const uint16_t* x, const in
   a.ws = ws;
   a.wl = ws_layout(a.E, a.K, a.I, a.Is, 1);
   a.nR = given ? 0 : cdiv(a.E, kRowsPerUnit);
-  a.nS = a.Is / kRowsPerUnit;
-  a.perG = a.I / kRowsPerUnit;
+  a.nS = a.Is / kGuRows;
+  a.perG = a.I / kGuRows;
   a.nG = a.K * a.perG;
   a.nD = a.H / kRowsPerUnit;
   size_t lds = gu_lds(a.H);
   if (router_lds(a.H) > lds) lds = router_lds(a.H);
-  if (down_lds(a.I, a.Is) > lds) lds = down_lds(a.I, a.Is);
+  if (down_lds(a.I, a.Is, a.K) > lds) lds = down_lds(a.I, a.Is, a.K);
   a.nowait = phased;
   a.s_done = 0;
   if (mode == kStepShared || mode == kStepRouted) {
