@@ -30,7 +30,7 @@ typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kPfRows = 64;   // weight rows (output features) per block
-constexpr int kPfMaxM = 128;  // rows per expert (tokens) per block
+constexpr int kPfMaxM = 64;   // A rows (an expert's tokens) per pass of a block
 constexpr int kPfMSub = kPfMaxM / 16;
 
 struct PfLayout {
@@ -131,20 +131,25 @@ __global__ __launch_bounds__(kBlock) void k_pf_prep(const uint16_t* X, int n8, _
 }
 
 // ================================================================= GEMMs
-// B operands of one 16-row slice for a 128-code block: lane (n = l%16,
-// j = l/16) holds codes [32j, 32j+32) of its row as 4 words; word m feeds
-// MFMA m (K slots 8 codes each).  Dequantized to fp16 in the order
-// (q0,q2,q4,q6,q1,q3,q5,q7) of the word.
+// One block: 64 weight rows (wave w: rows n0 + 16w + l%16) of NM matrices
+// against up to 128 rows of A (an expert's tokens), K in steps of 128
+// codes.  Per step the block stages its A rows (fp16, prepared layout) in
+// LDS once for all four waves, while every lane holds the next two steps
+// of its weights in registers: lane (n = l%16, j = l/16) holds codes
+// [128kb + 32j, +32) of its row as 4 words; word t feeds MFMA t (K slots
+// 8j..8j+7), dequantized to fp16 in the order (q0,q2,q4,q6,q1,q3,q5,q7).
 __device__ __forceinline__ h8_t dequant_word(uint32_t v, h2_t s2, h2_t b2) {
   const uint32_t lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;
   h2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false);  // q0, q2
   h2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, true);   // q4, q6
   h2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, false);  // q1, q3
   h2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 512.0f, true);   // q5, q7
-  p0 = p0 * s2 + b2;
-  p1 = p1 * s2 + b2;
-  p2 = p2 * s2 + b2;
-  p3 = p3 * s2 + b2;
+  // one rounding each (an explicit fused multiply-add, the same in every
+  // instantiation)
+  p0 = __builtin_elementwise_fma(p0, s2, b2);
+  p1 = __builtin_elementwise_fma(p1, s2, b2);
+  p2 = __builtin_elementwise_fma(p2, s2, b2);
+  p3 = __builtin_elementwise_fma(p3, s2, b2);
   h8_t o;
   o[0] = p0.x; o[1] = p0.y; o[2] = p1.x; o[3] = p1.y;
   o[4] = p2.x; o[5] = p2.y; o[6] = p3.x; o[7] = p3.y;
@@ -165,58 +170,132 @@ struct PfArgs {
   float* y_sh;          // [T][H]
 };
 
-// C[m][n] over rows m < M of A (fp16 prepared rows, given by `arow`) and
-// NM weight matrices (rows n0 + 16*wave + n, K columns).  acc[ms][k] is the
-// 16x16 tile of M-slice ms and matrix k: lane l holds rows
-// 16ms + 4(l/16) + r and column l%16.
+constexpr int kPfAStride = 136;  // fp16 per staged A row: 128 + 8 (conflict-free reads)
+
+typedef unsigned int u4v_t __attribute__((ext_vector_type(4)));
+
+struct PfShared {
+  _Float16 a[kPfMaxM * kPfAStride];
+  int32_t rows[kPfMaxM];  // element offset of each A row from the A base
+};
+
 template <int NM>
-__device__ __forceinline__ void pf_tile(const DevQ (&W)[NM], int n_row, int K, int M,
-                                        const _Float16* const* arow, f4_t (&acc)[kPfMSub][NM]) {
-  const int lane = threadIdx.x & 63, j = lane >> 4;
+struct PfW {
+  u4v_t q[NM];
+  uint32_t sb[NM];
+};
+
+// Weights of step kb (clamped to a valid address past the end).
+template <int NM>
+__device__ __forceinline__ void pf_load_w(PfW<NM>& B, const DevQ (&W)[NM], int n_row, int K,
+                                          int kb) {
+  const int j = (threadIdx.x & 63) >> 4;
+  const int c = min(128 * kb + 32 * j, K - 32);
   const int G = K / 64;
-  const int nms = (M + 15) / 16;
 #pragma unroll
-  for (int ms = 0; ms < kPfMSub; ++ms)
+  for (int k = 0; k < NM; ++k) {
+    B.q[k] = __builtin_nontemporal_load(
+        reinterpret_cast<const u4v_t*>(W[k].q + (int64_t)n_row * (K / 2) + c / 2));
+    B.sb[k] = ld_sb(W[k].s, W[k].b, (int64_t)n_row * G + c / 64);
+  }
+}
+
+// A rows of step kb: thread (r0 = tid/16, seg = tid%16) loads 16 bytes of
+// rows r0 + 16i, i < NMS.  Rows past Mc re-read row Mc-1 (zeroed at store).
+template <int NMS>
+struct PfA {
+  u4v_t v[NMS];
+};
+template <int NMS>
+__device__ __forceinline__ void pf_load_a(PfA<NMS>& A, const _Float16* abase, const PfShared& sh,
+                                          int Mc, int K, int kb) {
+  const int seg = threadIdx.x & 15, r0 = threadIdx.x >> 4;
+  const int col = min(128 * kb + 8 * seg, K - 8);
+#pragma unroll
+  for (int i = 0; i < NMS; ++i)
+    A.v[i] = *reinterpret_cast<const u4v_t*>(abase + sh.rows[min(r0 + 16 * i, Mc - 1)] + col);
+}
+template <int NMS>
+__device__ __forceinline__ void pf_store_a(const PfA<NMS>& A, PfShared& sh, int Mc, int K, int kb) {
+  const int seg = threadIdx.x & 15, r0 = threadIdx.x >> 4;
+  const bool colok = 128 * kb + 8 * seg < K;
+#pragma unroll
+  for (int i = 0; i < NMS; ++i) {
+    const int m = r0 + 16 * i;
+    const u4v_t z = {0u, 0u, 0u, 0u};
+    *reinterpret_cast<u4v_t*>(sh.a + m * kPfAStride + 8 * seg) = (colok && m < Mc) ? A.v[i] : z;
+  }
+}
+
+template <int NM, int NMS>
+__device__ __forceinline__ void pf_mma(const PfW<NM>& B, int K, int kb, const PfShared& sh,
+                                       f4_t (&acc)[NMS][NM]) {
+  const int lane = threadIdx.x & 63, m = lane & 15, j = lane >> 4;
+  const bool kok = 128 * kb + 32 * j < K;
+  h8_t Bf[NM][4];
+#pragma unroll
+  for (int k = 0; k < NM; ++k) {
+    _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)(B.sb[k] & 0xffffu));
+    _Float16 bv = __builtin_bit_cast(_Float16, (uint16_t)(B.sb[k] >> 16));
+    if (!kok) sv = bv = (_Float16)0.f;
+    const h2_t s2 = {sv, sv}, b2 = {bv, bv};
+    const u4v_t z = {0u, 0u, 0u, 0u};
+    const u4v_t q = kok ? B.q[k] : z;
+    Bf[k][0] = dequant_word(q.x, s2, b2);
+    Bf[k][1] = dequant_word(q.y, s2, b2);
+    Bf[k][2] = dequant_word(q.z, s2, b2);
+    Bf[k][3] = dequant_word(q.w, s2, b2);
+  }
+#pragma unroll
+  for (int ms = 0; ms < NMS; ++ms) {
+    const h8_t* ap = reinterpret_cast<const h8_t*>(sh.a + (ms * 16 + m) * kPfAStride + 32 * j);
+    const h8_t A0 = ap[0], A1 = ap[1], A2 = ap[2], A3 = ap[3];
+#pragma unroll
+    for (int k = 0; k < NM; ++k) {
+      acc[ms][k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, Bf[k][0], acc[ms][k], 0, 0, 0);
+      acc[ms][k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, Bf[k][1], acc[ms][k], 0, 0, 0);
+      acc[ms][k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A2, Bf[k][2], acc[ms][k], 0, 0, 0);
+      acc[ms][k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A3, Bf[k][3], acc[ms][k], 0, 0, 0);
+    }
+    // keep each subtile's fragment reads next to its MFMAs (bounded registers)
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// C = A W^T over one pass of Mc <= 64 A rows (sh.rows[0..Mc) set), K
+// columns; acc[ms][k]: lane l holds rows 16ms + 4(l/16) + r, column l%16.
+// Weights run two steps ahead; A one step ahead (loaded during the
+// previous step's math, stored to LDS between two barriers).
+template <int NM, int NMS>
+__device__ __forceinline__ void pf_pass(const DevQ (&W)[NM], int n_row, int K, int Mc,
+                                        const _Float16* abase, PfShared& sh,
+                                        f4_t (&acc)[NMS][NM]) {
+#pragma unroll
+  for (int ms = 0; ms < NMS; ++ms)
 #pragma unroll
     for (int k = 0; k < NM; ++k) acc[ms][k] = f4_t{0.f, 0.f, 0.f, 0.f};
   const int nkb = (K + 127) / 128;
-  for (int kb = 0; kb < nkb; ++kb) {
-    const int c0 = 128 * kb + 32 * j;  // first code of this lane group
-    const bool kok = c0 < K;
-    const int cc = kok ? c0 : 0;
-    h8_t B[NM][4];
-#pragma unroll
-    for (int k = 0; k < NM; ++k) {
-      uint4 wq = *reinterpret_cast<const uint4*>(W[k].q + ((int64_t)n_row * (K / 2) + cc / 2));
-      const int g = cc / 64;
-      _Float16 sv = __builtin_bit_cast(_Float16, W[k].s[(int64_t)n_row * G + g]);
-      _Float16 bv = __builtin_bit_cast(_Float16, W[k].b[(int64_t)n_row * G + g]);
-      if (!kok) sv = bv = (_Float16)0.f;
-      h2_t s2 = {sv, sv}, b2 = {bv, bv};
-      B[k][0] = dequant_word(kok ? wq.x : 0u, s2, b2);
-      B[k][1] = dequant_word(kok ? wq.y : 0u, s2, b2);
-      B[k][2] = dequant_word(kok ? wq.z : 0u, s2, b2);
-      B[k][3] = dequant_word(kok ? wq.w : 0u, s2, b2);
-    }
-#pragma unroll
-    for (int ms = 0; ms < kPfMSub; ++ms) {
-      if (ms < nms) {
-        const int m = ms * 16 + (lane & 15);
-        h8_t A[4];
-        if (m < M && kok) {
-          const h8_t* ap = reinterpret_cast<const h8_t*>(arow[ms] + cc);
-          A[0] = ap[0]; A[1] = ap[1]; A[2] = ap[2]; A[3] = ap[3];
-        } else {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) A[t] = h8_t{0, 0, 0, 0, 0, 0, 0, 0};
-        }
-#pragma unroll
-        for (int k = 0; k < NM; ++k)
-#pragma unroll
-          for (int t = 0; t < 4; ++t)
-            acc[ms][k] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[t], B[k][t], acc[ms][k], 0, 0, 0);
-      }
-    }
+  PfW<NM> B0, B1;
+  PfA<NMS> A;
+  pf_load_w<NM>(B0, W, n_row, K, 0);
+  pf_load_a<NMS>(A, abase, sh, Mc, K, 0);
+  pf_load_w<NM>(B1, W, n_row, K, 1);
+  pf_store_a<NMS>(A, sh, Mc, K, 0);
+  __syncthreads();
+  for (int kb = 0; kb < nkb; kb += 2) {
+    pf_load_a<NMS>(A, abase, sh, Mc, K, min(kb + 1, nkb - 1));
+    pf_mma<NM, NMS>(B0, K, kb, sh, acc);
+    pf_load_w<NM>(B0, W, n_row, K, kb + 2);
+    __syncthreads();
+    if (kb + 1 >= nkb) break;
+    pf_store_a<NMS>(A, sh, Mc, K, kb + 1);
+    __syncthreads();
+    pf_load_a<NMS>(A, abase, sh, Mc, K, min(kb + 2, nkb - 1));
+    pf_mma<NM, NMS>(B1, K, kb + 1, sh, acc);
+    pf_load_w<NM>(B1, W, n_row, K, kb + 3);
+    __syncthreads();
+    if (kb + 2 < nkb) pf_store_a<NMS>(A, sh, Mc, K, kb + 2);
+    __syncthreads();
   }
 }
 
@@ -227,13 +306,46 @@ __device__ __forceinline__ int prep_col(int n) {
   return (n & ~7) | ((v & 1) ? 4 + (v >> 1) : (v >> 1));
 }
 
-// gate/up: grid (tiles of 64 rows over max(I, Is), E + 1); y = E: shared.
-// An expert's rows are taken kPfMaxM at a time (more than T only when the
-// caller repeats an expert within a token).
-__global__ __launch_bounds__(kBlock) void k_pf_gu(PfArgs a) {
-  __shared__ const _Float16* rows_s[kPfMaxM];
-  const int e = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const bool shared = e == a.E;
+template <int NMS>
+__device__ __forceinline__ void pf_gu_store(const f4_t (&acc)[NMS][2], _Float16* out, int ld, int base, int Mc,
+                            int n) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int ms = 0; ms < NMS; ++ms)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = ms * 16 + 4 * (lane >> 4) + r;
+      if (m < Mc) {
+        float v = gelu_tanh(acc[ms][0][r]) * acc[ms][1][r];
+        // the product is rounded to fp32, then to fp16, in every copy of
+        // this code (the backend would otherwise fuse the multiply with the
+        // conversion in some copies only: other bits, other signs of zero)
+        asm volatile("" : "+v"(v));
+        out[(size_t)(base + m) * ld + prep_col(n)] = (_Float16)v;
+      }
+    }
+}
+template <int NMS>
+__device__ __forceinline__ void pf_down_store(const f4_t (&acc)[NMS][1], float* out, int ld, int base, int Mc,
+                              int n) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int ms = 0; ms < NMS; ++ms)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int m = ms * 16 + 4 * (lane >> 4) + r;
+      if (m < Mc) out[(size_t)(base + m) * ld + n] = acc[ms][0][r];
+    }
+}
+
+// gate/up: grid (tiles of 64 rows over max(I, Is), E + 1); y = 0: the
+// shared expert (largest, started first), y = e + 1: expert e.  An
+// expert's rows are taken 64 at a time.
+__global__ __launch_bounds__(kBlock, 2) void k_pf_gu(PfArgs a) {
+  __shared__ PfShared sh;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool shared = blockIdx.y == 0;
+  const int e = blockIdx.y - 1;
   const int N = shared ? a.Is : a.I;
   const int n0 = blockIdx.x * kPfRows;
   if (n0 >= N) return;
@@ -256,32 +368,31 @@ __global__ __launch_bounds__(kBlock) void k_pf_gu(PfArgs a) {
     __syncthreads();
     for (int m = threadIdx.x; m < Mc; m += kBlock) {
       int t = shared ? mc + m : a.perm[base + mc + m] / a.K;
-      rows_s[m] = a.xh + (size_t)t * a.H;
+      sh.rows[m] = t * a.H;
     }
     __syncthreads();
-    const _Float16* arow[kPfMSub];
-#pragma unroll
-    for (int ms = 0; ms < kPfMSub; ++ms) arow[ms] = rows_s[min(ms * 16 + (lane & 15), Mc - 1)];
-    f4_t acc[kPfMSub][2];
-    pf_tile<2>(W, n, a.H, Mc, arow, acc);
-#pragma unroll
-    for (int ms = 0; ms < kPfMSub; ++ms) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = ms * 16 + 4 * (lane >> 4) + r;
-        if (m < Mc) {
-          float v = gelu_tanh(acc[ms][0][r]) * acc[ms][1][r];
-          out[(size_t)(base + mc + m) * ld + prep_col(n)] = (_Float16)v;
-        }
-      }
+    if (Mc <= 16) {
+      f4_t acc[1][2];
+      pf_pass<2, 1>(W, n, a.H, Mc, a.xh, sh, acc);
+      pf_gu_store<1>(acc, out, ld, base + mc, Mc, n);
+    } else if (Mc <= 32) {
+      f4_t acc[2][2];
+      pf_pass<2, 2>(W, n, a.H, Mc, a.xh, sh, acc);
+      pf_gu_store<2>(acc, out, ld, base + mc, Mc, n);
+    } else {
+      f4_t acc[4][2];
+      pf_pass<2, 4>(W, n, a.H, Mc, a.xh, sh, acc);
+      pf_gu_store<4>(acc, out, ld, base + mc, Mc, n);
     }
   }
 }
 
-// down: grid (tiles of 64 rows over H, E + 1); y = E: shared.
-__global__ __launch_bounds__(kBlock) void k_pf_down(PfArgs a) {
-  const int e = blockIdx.y, wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const bool shared = e == a.E;
+// down: grid (tiles of 64 rows over H, E + 1); y = 0: shared, y = e + 1.
+__global__ __launch_bounds__(kBlock, 3) void k_pf_down(PfArgs a) {
+  __shared__ PfShared sh;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const bool shared = blockIdx.y == 0;
+  const int e = blockIdx.y - 1;
   const int n0 = blockIdx.x * kPfRows;
   const int M = shared ? a.T : a.counts[e];
   const int base = shared ? 0 : a.offsets[e];
@@ -298,19 +409,21 @@ __global__ __launch_bounds__(kBlock) void k_pf_down(PfArgs a) {
   float* out = shared ? a.y_sh : a.y;
   for (int mc = 0; mc < M; mc += kPfMaxM) {
     const int Mc = min(M - mc, kPfMaxM);
-    const _Float16* arow[kPfMSub];
-#pragma unroll
-    for (int ms = 0; ms < kPfMSub; ++ms)
-      arow[ms] = src + (size_t)(base + mc + min(ms * 16 + (lane & 15), Mc - 1)) * Kd;
-    f4_t acc[kPfMSub][1];
-    pf_tile<1>(W, n, Kd, Mc, arow, acc);
-#pragma unroll
-    for (int ms = 0; ms < kPfMSub; ++ms) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = ms * 16 + 4 * (lane >> 4) + r;
-        if (m < Mc) out[(size_t)(base + mc + m) * a.H + n] = acc[ms][0][r];
-      }
+    __syncthreads();
+    for (int m = threadIdx.x; m < Mc; m += kBlock) sh.rows[m] = (base + mc + m) * Kd;
+    __syncthreads();
+    if (Mc <= 16) {
+      f4_t acc[1][1];
+      pf_pass<1, 1>(W, n, Kd, Mc, src, sh, acc);
+      pf_down_store<1>(acc, out, a.H, base + mc, Mc, n);
+    } else if (Mc <= 32) {
+      f4_t acc[2][1];
+      pf_pass<1, 2>(W, n, Kd, Mc, src, sh, acc);
+      pf_down_store<2>(acc, out, a.H, base + mc, Mc, n);
+    } else {
+      f4_t acc[4][1];
+      pf_pass<1, 4>(W, n, Kd, Mc, src, sh, acc);
+      pf_down_store<4>(acc, out, a.H, base + mc, Mc, n);
     }
   }
 }
