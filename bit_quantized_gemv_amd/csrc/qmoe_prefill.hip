@@ -32,6 +32,7 @@ typedef float f4_t __attribute__((ext_vector_type(4)));
 constexpr int kPfRows = 64;   // weight rows (output features) per block
 constexpr int kPfMaxM = 64;   // A rows (an expert's tokens) per pass of a block
 constexpr int kPfMSub = kPfMaxM / 16;
+constexpr int kPfMChunks = 2; // row chunks of one expert handled by separate blocks
 
 struct PfLayout {
   size_t counts, offsets, perm, pos, xh, act, act_sh, y, y_sh, total;
@@ -175,7 +176,7 @@ constexpr int kPfAStride = 136;  // fp16 per staged A row: 128 + 8 (conflict-fre
 typedef unsigned int u4v_t __attribute__((ext_vector_type(4)));
 
 struct PfShared {
-  _Float16 a[kPfMaxM * kPfAStride];
+  _Float16 a[2][kPfMaxM * kPfAStride];  // A rows of two K-steps (double buffer)
   int32_t rows[kPfMaxM];  // element offset of each A row from the A base
 };
 
@@ -194,9 +195,11 @@ __device__ __forceinline__ void pf_load_w(PfW<NM>& B, const DevQ (&W)[NM], int n
   const int G = K / 64;
 #pragma unroll
   for (int k = 0; k < NM; ++k) {
-    B.q[k] = __builtin_nontemporal_load(
-        reinterpret_cast<const u4v_t*>(W[k].q + (int64_t)n_row * (K / 2) + c / 2));
-    B.sb[k] = ld_sb(W[k].s, W[k].b, (int64_t)n_row * G + c / 64);
+    // cached loads: a step reads half of each 128-byte line, the next step
+    // the other half
+    B.q[k] = *reinterpret_cast<const u4v_t*>(W[k].q + (int64_t)n_row * (K / 2) + c / 2);
+    B.sb[k] = (uint32_t)W[k].s[(int64_t)n_row * G + c / 64] |
+              ((uint32_t)W[k].b[(int64_t)n_row * G + c / 64] << 16);
   }
 }
 
@@ -216,19 +219,19 @@ __device__ __forceinline__ void pf_load_a(PfA<NMS>& A, const _Float16* abase, co
     A.v[i] = *reinterpret_cast<const u4v_t*>(abase + sh.rows[min(r0 + 16 * i, Mc - 1)] + col);
 }
 template <int NMS>
-__device__ __forceinline__ void pf_store_a(const PfA<NMS>& A, PfShared& sh, int Mc, int K, int kb) {
+__device__ __forceinline__ void pf_store_a(const PfA<NMS>& A, _Float16* buf, int Mc, int K, int kb) {
   const int seg = threadIdx.x & 15, r0 = threadIdx.x >> 4;
   const bool colok = 128 * kb + 8 * seg < K;
 #pragma unroll
   for (int i = 0; i < NMS; ++i) {
     const int m = r0 + 16 * i;
     const u4v_t z = {0u, 0u, 0u, 0u};
-    *reinterpret_cast<u4v_t*>(sh.a + m * kPfAStride + 8 * seg) = (colok && m < Mc) ? A.v[i] : z;
+    *reinterpret_cast<u4v_t*>(buf + m * kPfAStride + 8 * seg) = (colok && m < Mc) ? A.v[i] : z;
   }
 }
 
 template <int NM, int NMS>
-__device__ __forceinline__ void pf_mma(const PfW<NM>& B, int K, int kb, const PfShared& sh,
+__device__ __forceinline__ void pf_mma(const PfW<NM>& B, int K, int kb, const _Float16* buf,
                                        f4_t (&acc)[NMS][NM]) {
   const int lane = threadIdx.x & 63, m = lane & 15, j = lane >> 4;
   const bool kok = 128 * kb + 32 * j < K;
@@ -248,7 +251,7 @@ __device__ __forceinline__ void pf_mma(const PfW<NM>& B, int K, int kb, const Pf
   }
 #pragma unroll
   for (int ms = 0; ms < NMS; ++ms) {
-    const h8_t* ap = reinterpret_cast<const h8_t*>(sh.a + (ms * 16 + m) * kPfAStride + 32 * j);
+    const h8_t* ap = reinterpret_cast<const h8_t*>(buf + (ms * 16 + m) * kPfAStride + 32 * j);
     const h8_t A0 = ap[0], A1 = ap[1], A2 = ap[2], A3 = ap[3];
 #pragma unroll
     for (int k = 0; k < NM; ++k) {
@@ -264,8 +267,9 @@ __device__ __forceinline__ void pf_mma(const PfW<NM>& B, int K, int kb, const Pf
 
 // C = A W^T over one pass of Mc <= 64 A rows (sh.rows[0..Mc) set), K
 // columns; acc[ms][k]: lane l holds rows 16ms + 4(l/16) + r, column l%16.
-// Weights run two steps ahead; A one step ahead (loaded during the
-// previous step's math, stored to LDS between two barriers).
+// Weights run two steps ahead in registers; A rows are loaded two steps
+// ahead into registers (two alternating sets) and stored to the LDS buffer
+// of the next step (two alternating buffers, one barrier per step).
 template <int NM, int NMS>
 __device__ __forceinline__ void pf_pass(const DevQ (&W)[NM], int n_row, int K, int Mc,
                                         const _Float16* abase, PfShared& sh,
@@ -276,27 +280,30 @@ __device__ __forceinline__ void pf_pass(const DevQ (&W)[NM], int n_row, int K, i
     for (int k = 0; k < NM; ++k) acc[ms][k] = f4_t{0.f, 0.f, 0.f, 0.f};
   const int nkb = (K + 127) / 128;
   PfW<NM> B0, B1;
-  PfA<NMS> A;
+  PfA<NMS> Aa, Ab;
   pf_load_w<NM>(B0, W, n_row, K, 0);
-  pf_load_a<NMS>(A, abase, sh, Mc, K, 0);
+  pf_load_a<NMS>(Aa, abase, sh, Mc, K, 0);
   pf_load_w<NM>(B1, W, n_row, K, 1);
-  pf_store_a<NMS>(A, sh, Mc, K, 0);
+  pf_load_a<NMS>(Ab, abase, sh, Mc, K, min(1, nkb - 1));
+  pf_store_a<NMS>(Aa, sh.a[0], Mc, K, 0);
   __syncthreads();
   for (int kb = 0; kb < nkb; kb += 2) {
-    pf_load_a<NMS>(A, abase, sh, Mc, K, min(kb + 1, nkb - 1));
-    pf_mma<NM, NMS>(B0, K, kb, sh, acc);
+    // step kb: buffer 0 holds A(kb); Ab holds A(kb + 1)
+    pf_load_a<NMS>(Aa, abase, sh, Mc, K, min(kb + 2, nkb - 1));
+    pf_mma<NM, NMS>(B0, K, kb, sh.a[0], acc);
     pf_load_w<NM>(B0, W, n_row, K, kb + 2);
-    __syncthreads();
     if (kb + 1 >= nkb) break;
-    pf_store_a<NMS>(A, sh, Mc, K, kb + 1);
+    pf_store_a<NMS>(Ab, sh.a[1], Mc, K, kb + 1);
     __syncthreads();
-    pf_load_a<NMS>(A, abase, sh, Mc, K, min(kb + 2, nkb - 1));
-    pf_mma<NM, NMS>(B1, K, kb + 1, sh, acc);
+    // step kb + 1: buffer 1 holds A(kb + 1); Aa holds A(kb + 2)
+    pf_load_a<NMS>(Ab, abase, sh, Mc, K, min(kb + 3, nkb - 1));
+    pf_mma<NM, NMS>(B1, K, kb + 1, sh.a[1], acc);
     pf_load_w<NM>(B1, W, n_row, K, kb + 3);
-    __syncthreads();
-    if (kb + 2 < nkb) pf_store_a<NMS>(A, sh, Mc, K, kb + 2);
+    if (kb + 2 >= nkb) break;
+    pf_store_a<NMS>(Aa, sh.a[0], Mc, K, kb + 2);
     __syncthreads();
   }
+  __syncthreads();  // the LDS is free for the next pass
 }
 
 // Column position of output feature n inside its group of 8 in the prepared
@@ -338,9 +345,10 @@ __device__ __forceinline__ void pf_down_store(const f4_t (&acc)[NMS][1], float* 
     }
 }
 
-// gate/up: grid (tiles of 64 rows over max(I, Is), E + 1); y = 0: the
-// shared expert (largest, started first), y = e + 1: expert e.  An
-// expert's rows are taken 64 at a time.
+// gate/up: grid (tiles of 64 rows over max(I, Is), E + 1, kPfMChunks);
+// y = 0: the shared expert (largest, started first), y = e + 1: expert e;
+// z: which 64-row chunks of the expert's rows (z, z + gridDim.z, ...), so
+// that the chunks of the shared and the busiest experts run side by side.
 __global__ __launch_bounds__(kBlock, 2) void k_pf_gu(PfArgs a) {
   __shared__ PfShared sh;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -363,7 +371,7 @@ __global__ __launch_bounds__(kBlock, 2) void k_pf_gu(PfArgs a) {
   const int n = n0 + 16 * wave + (lane & 15);  // N is a multiple of 64
   _Float16* out = shared ? a.act_sh : a.act;
   const int ld = shared ? a.Is : a.I;
-  for (int mc = 0; mc < M; mc += kPfMaxM) {
+  for (int mc = blockIdx.z * kPfMaxM; mc < M; mc += gridDim.z * kPfMaxM) {
     const int Mc = min(M - mc, kPfMaxM);
     __syncthreads();
     for (int m = threadIdx.x; m < Mc; m += kBlock) {
@@ -387,7 +395,8 @@ __global__ __launch_bounds__(kBlock, 2) void k_pf_gu(PfArgs a) {
   }
 }
 
-// down: grid (tiles of 64 rows over H, E + 1); y = 0: shared, y = e + 1.
+// down: grid (tiles of 64 rows over H, E + 1, kPfMChunks); y and z as for
+// gate/up.
 __global__ __launch_bounds__(kBlock, 3) void k_pf_down(PfArgs a) {
   __shared__ PfShared sh;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -407,7 +416,7 @@ __global__ __launch_bounds__(kBlock, 3) void k_pf_down(PfArgs a) {
   }
   const int n = n0 + 16 * wave + (lane & 15);  // H is a multiple of 64
   float* out = shared ? a.y_sh : a.y;
-  for (int mc = 0; mc < M; mc += kPfMaxM) {
+  for (int mc = blockIdx.z * kPfMaxM; mc < M; mc += gridDim.z * kPfMaxM) {
     const int Mc = min(M - mc, kPfMaxM);
     __syncthreads();
     for (int m = threadIdx.x; m < Mc; m += kBlock) sh.rows[m] = (base + mc + m) * Kd;
@@ -500,8 +509,8 @@ qmoe_status launch_prefill(const qmoe_moe_layer& L, const uint16_t* X, int T, co
   hipLaunchKernelGGL(k_pf_prep, dim3((n8 + kBlock - 1) / kBlock), dim3(kBlock), 0, S(stream), X, n8,
                      const_cast<_Float16*>(a.xh));
   const int ngu = ((I > Is ? I : Is) + kPfRows - 1) / kPfRows;
-  hipLaunchKernelGGL(k_pf_gu, dim3(ngu, E + 1), dim3(kBlock), 0, S(stream), a);
-  hipLaunchKernelGGL(k_pf_down, dim3(H / kPfRows, E + 1), dim3(kBlock), 0, S(stream), a);
+  hipLaunchKernelGGL(k_pf_gu, dim3(ngu, E + 1, kPfMChunks), dim3(kBlock), 0, S(stream), a);
+  hipLaunchKernelGGL(k_pf_down, dim3(H / kPfRows, E + 1, kPfMChunks), dim3(kBlock), 0, S(stream), a);
   hipLaunchKernelGGL(k_pf_combine, dim3((H / 8 + kBlock - 1) / kBlock, T), dim3(kBlock), 0,
                      S(stream), K, H, w, pos_of, a.y, a.y_sh, residual, out);
   return hipGetLastError() == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
