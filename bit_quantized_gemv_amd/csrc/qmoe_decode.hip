@@ -746,14 +746,32 @@ __global__ __launch_bounds__(kBlock) void k_router(DevQ Wr, const float* lbias, 
   float* red = reinterpret_cast<float*>(sys + kSysRed);
   const int row0 = blockIdx.x * kRowsPerUnit;
   const int t0 = blockIdx.y * kTokTile, t1 = min(T, t0 + kTokTile);
-  for (int t = t0; t < t1; ++t) {
-    float s = router_token<H8C>(Wr, row0, E, H, x + (size_t)t * H, nullptr, 0.f, xr, xh, red);
+  auto put = [&](int t, float s) {
     if (threadIdx.x < 8 && row0 + (int)threadIdx.x < E) {
       int e = row0 + threadIdx.x;
       if (lbias) s += lbias[e];
       st_dev(logits_ws + (size_t)t * E + e, s);
       if (logits_out) logits_out[(size_t)t * E + e] = s;
     }
+  };
+  if (H8C) {
+    // the block's 8 router rows stay in registers for all tokens of the
+    // tile; the next token's activations load while this one is computed
+    constexpr int SR = H8C ? cdiv(cdiv(H8C, kSlots), kWavesPerBlock) : 1;
+    RRegs<SR> R;
+    router_load<SR>(R, Wr, row0, E, H, 0);
+    XRegs X;
+    x_load(X, x + (size_t)t0 * H, H);
+    for (int t = t0; t < t1; ++t) {
+      __syncthreads();  // the previous token's staged values are consumed
+      x_stage<false>(X, x + (size_t)t * H, nullptr, 1.f, H, xr, xh);
+      __syncthreads();
+      if (t + 1 < t1) x_load(X, x + (size_t)(t + 1) * H, H);
+      put(t, router_finish(router_compute<SR>(R, H, 0, xr, xh, 0.f), red));
+    }
+  } else {
+    for (int t = t0; t < t1; ++t)
+      put(t, router_token<H8C>(Wr, row0, E, H, x + (size_t)t * H, nullptr, 0.f, xr, xh, red));
   }
   wait_vm();
   __syncthreads();
