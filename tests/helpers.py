@@ -50,11 +50,12 @@ def codes_of(m) -> np.ndarray:
 
 def gemv4_bound(m, x: np.ndarray) -> np.ndarray:
     """Per-row forward error bound of the 4-bit GEMV as the kernels compute
-    it: per 32-column chunk D = sum (1 + q/16) x on the dot2 unit, then
-    acc += 16 s D + (b - 16 s) X with X the chunk sum of x; chunk partials
-    are summed by each lane and across 8 lanes.  Every term passes through at
-    most n = 64 + cols/32 roundings, so |err| <= gamma_n * M with
-    M = sum_c (16|s| + |s| q_c + |b - 16 s|) |x_c|."""
+    it: per 32-column chunk D = sum q x on the dot2 unit (exact products),
+    then acc += s D + b X with X the chunk sum of x; chunk partials are
+    summed by each lane and across 8 lanes.  Every term passes through at
+    most n = 64 + cols/32 roundings, so |err| <= gamma_n * M for any
+    M >= sum_c (|s| q_c + |b|) |x_c|; the M used here,
+    sum_c (16|s| + |s| q_c + |b - 16 s|) |x_c|, is larger (|b| <= |b - 16 s| + 16|s|)."""
     q = codes_of(m)
     s = np.repeat(m.s.view(np.float16).astype(np.float64), 64, axis=1)
     b = np.repeat(m.b.view(np.float16).astype(np.float64), 64, axis=1)
