@@ -7,7 +7,8 @@ package without it raises ImportError (there is no fallback path).
 
 Names mirror the C entry points: ``qmoe_gemv_affine4``, ``qmoe_router_topk``,
 ``qmoe_expert_ffn``, ``qmoe_moe_decode``, ``qmoe_prefill_grouped``,
-``qmoe_rmsnorm``, ``qmoe_workspace_bytes``, ``qmoe_workspace_status``.
+``qmoe_rmsnorm``, ``qmoe_workspace_bytes``, ``qmoe_workspace_status``,
+``qmoe_stack_decode`` (with ``Stack``, a table and workspace holder).
 Tensor arguments are torch tensors on the GPU; bf16/fp16 data may be given as
 ``torch.bfloat16`` / ``torch.float16`` or as 16-bit integer bit patterns.
 """
@@ -95,11 +96,19 @@ _lib.qmoe_workspace_bytes.argtypes = [C.POINTER(_Layer), C.c_int32]
 _lib.qmoe_router_workspace_bytes.restype = C.c_size_t
 _lib.qmoe_router_workspace_bytes.argtypes = [C.c_int32, C.c_int32]
 _lib.qmoe_workspace_status.argtypes = [_vp, C.c_size_t, C.POINTER(C.c_int32), _vp]
+_lib.qmoe_stack_table_bytes.restype = C.c_size_t
+_lib.qmoe_stack_table_bytes.argtypes = [C.c_int32]
+_lib.qmoe_stack_table_init.argtypes = [C.POINTER(_Layer), C.c_int32, _vp, C.c_size_t, _vp]
+_lib.qmoe_stack_workspace_bytes.restype = C.c_size_t
+_lib.qmoe_stack_workspace_bytes.argtypes = [C.POINTER(_Layer)]
+_lib.qmoe_stack_decode.argtypes = [C.POINTER(_Layer), _vp, C.c_int32, _vp, _vp, _vp, _vp, _vp,
+                                   _vp, C.c_size_t, _vp]
 for _f in ("qmoe_gemv_affine4", "qmoe_router_topk", "qmoe_expert_ffn", "qmoe_moe_decode",
            "qmoe_moe_decode_phased", "qmoe_prefill_grouped", "qmoe_rmsnorm",
            "qmoe_workspace_status", "qmoe_prefill_dispatch_offsets", "qmoe_moe_decode_timed",
            "qmoe_expert_ffn_shared", "qmoe_expert_ffn_routed", "qmoe_pool_create",
-           "qmoe_pool_plan", "qmoe_pool_acquire", "qmoe_pool_stats_get"):
+           "qmoe_pool_plan", "qmoe_pool_acquire", "qmoe_pool_stats_get",
+           "qmoe_stack_table_init", "qmoe_stack_decode"):
     getattr(_lib, _f).restype = C.c_int
 
 
@@ -331,6 +340,55 @@ def qmoe_rmsnorm(x, gamma, eps: float, T: int, H: int, out, stream=None) -> None
                                              _stream(stream)))
 
 
+def qmoe_stack_table_bytes(n_layers: int) -> int:
+    return int(_lib.qmoe_stack_table_bytes(n_layers))
+
+
+def qmoe_stack_table_init(layers, table, stream=None) -> None:
+    """Device layer table of ``layers`` (MoeLayer list, one shape) into the
+    uint8 device tensor ``table``; waits for the copy."""
+    arr = (_Layer * len(layers))(*[l.c() for l in layers])
+    _check("qmoe_stack_table_init", _lib.qmoe_stack_table_init(
+        arr, len(layers), _ptr(table), table.numel() * table.element_size(), _stream(stream)))
+
+
+def qmoe_stack_workspace_bytes(layer: MoeLayer) -> int:
+    return int(_lib.qmoe_stack_workspace_bytes(C.byref(layer.c())))
+
+
+def qmoe_stack_decode(shape: MoeLayer, table, n_layers: int, x, out, layer_out, idx_out, w_out,
+                      ws, stream=None) -> None:
+    _check("qmoe_stack_decode", _lib.qmoe_stack_decode(
+        C.byref(shape.c()), _ptr(table), n_layers, _ptr(x), _ptr(out), _ptr(layer_out),
+        _ptr(idx_out), _ptr(w_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+class Stack:
+    """A decode stack on the device: the layers (kept alive), their device
+    table and a workspace for qmoe_stack_decode."""
+
+    def __init__(self, layers, device="cuda"):
+        import torch
+
+        self.layers = list(layers)
+        self.shape = self.layers[0]
+        n = qmoe_stack_table_bytes(len(self.layers))
+        if n == 0:
+            raise QmoeError("qmoe_stack_table_bytes", 2)
+        self.table = torch.zeros(n, dtype=torch.uint8, device=device)
+        qmoe_stack_table_init(self.layers, self.table)
+        wsn = qmoe_stack_workspace_bytes(self.shape)
+        if wsn == 0:
+            raise QmoeError("qmoe_stack_workspace_bytes", 2)
+        self.ws = torch.zeros(wsn, dtype=torch.uint8, device=device)
+
+    def decode(self, x, out, layer_out=None, idx_out=None, w_out=None, n_layers=None,
+               stream=None) -> None:
+        qmoe_stack_decode(self.shape, self.table,
+                          len(self.layers) if n_layers is None else n_layers, x, out,
+                          layer_out, idx_out, w_out, self.ws, stream)
+
+
 def qmoe_workspace_status(ws, stream=None) -> int:
     """Device error word of a workspace (0 = every in-kernel wait completed);
     synchronises the stream and clears the word."""
@@ -350,4 +408,6 @@ __all__ = [
     "qmoe_rmsnorm",
     "qmoe_workspace_bytes",
     "qmoe_router_workspace_bytes", "qmoe_workspace_status",
+    "qmoe_stack_table_bytes", "qmoe_stack_table_init", "qmoe_stack_workspace_bytes",
+    "qmoe_stack_decode", "Stack",
 ]

@@ -26,6 +26,9 @@ size_t prefill_ws_bytes(const qmoe_moe_layer& L, int T);
 void prefill_dispatch_offsets(const qmoe_moe_layer& L, int T, size_t* counts, size_t* offsets,
                               size_t* perm);
 bool moe_step_supported(const qmoe_moe_layer& L);
+qmoe_status launch_moe_stack(const qmoe_moe_layer& L, const void* table, int n_layers,
+                             const uint16_t* x, uint16_t* out, uint16_t* lout, int32_t* idx_out,
+                             float* w_out, uint8_t* ws, uint16_t* xb, void* stream);
 
 static bool al16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -69,6 +72,18 @@ static size_t ws_bytes_layer(const qmoe_moe_layer* L, int T) {
   size_t d = wl.total;
   size_t p = wl.pf + prefill_ws_bytes(*L, T);
   return p > d ? p : d;
+}
+
+// Stack workspace: the one-token layer workspace, then the two layer-input
+// buffers.
+static size_t stack_xb_offset(const qmoe_moe_layer* L) { return align256(ws_bytes_layer(L, 1)); }
+static size_t stack_ws_bytes(const qmoe_moe_layer* L) {
+  return stack_xb_offset(L) + align256((size_t)2 * L->hidden * 2);
+}
+
+static bool same_shape(const qmoe_moe_layer& a, const qmoe_moe_layer& b) {
+  return a.hidden == b.hidden && a.n_experts == b.n_experts && a.top_k == b.top_k &&
+         a.inter == b.inter && a.shared_inter == b.shared_inter && a.rms_eps == b.rms_eps;
 }
 }  // namespace qmoe
 
@@ -216,8 +231,9 @@ qmoe_status qmoe_workspace_status(void* ws, size_t ws_bytes, int32_t* device_cod
   if (hipStreamSynchronize(st) != hipSuccess) return QMOE_ERR_HIP;
   *device_code = (int32_t)v;
   if (v != 0) {
-    uint32_t zero = 0;
-    if (hipMemcpyAsync(word, &zero, 4, hipMemcpyHostToDevice, st) != hipSuccess) return QMOE_ERR_HIP;
+    // a wait gave up: flags, tags and counters may hold values of the
+    // unfinished call; start the control area afresh
+    if (hipMemsetAsync(ws, 0, kCtlBytes, st) != hipSuccess) return QMOE_ERR_HIP;
     if (hipStreamSynchronize(st) != hipSuccess) return QMOE_ERR_HIP;
     return QMOE_ERR_DEVICE;
   }
@@ -250,6 +266,64 @@ qmoe_status qmoe_moe_decode_phased(const qmoe_moe_layer* L, const uint16_t* x,
   if (!ws || ws_bytes < ws_bytes_layer(L, 1)) return QMOE_ERR_WORKSPACE;
   return launch_moe_step(*L, x, nullptr, nullptr, expert_slot, residual ? x : nullptr, out,
                          idx_out, w_out, static_cast<uint8_t*>(ws), 1, stream);
+}
+
+size_t qmoe_stack_table_bytes(int32_t n_layers) {
+  if (n_layers < 1 || n_layers > QMOE_MAX_LAYERS) return 0;
+  return sizeof(StackLayerDev) * (size_t)n_layers;
+}
+
+qmoe_status qmoe_stack_table_init(const qmoe_moe_layer* layers, int32_t n_layers, void* table,
+                                  size_t table_bytes, void* stream) {
+  if (!layers || !table) return QMOE_ERR_NULL_ARG;
+  if (n_layers < 1 || n_layers > QMOE_MAX_LAYERS) return QMOE_ERR_BAD_SHAPE;
+  if (!al16(table)) return QMOE_ERR_ALIGN;
+  if (table_bytes < qmoe_stack_table_bytes(n_layers)) return QMOE_ERR_WORKSPACE;
+  StackLayerDev* host = new StackLayerDev[n_layers];
+  for (int l = 0; l < n_layers; ++l) {
+    const qmoe_moe_layer& L = layers[l];
+    qmoe_status s = check_layer(&L);
+    if (s == QMOE_OK && !same_shape(L, layers[0])) s = QMOE_ERR_BAD_SHAPE;
+    if (s != QMOE_OK) {
+      delete[] host;
+      return s;
+    }
+    StackLayerDev& d = host[l];
+    d.router = devq(L.router); d.gate = devq(L.gate); d.up = devq(L.up); d.down = devq(L.down);
+    d.shg = devq(L.sh_gate); d.shu = devq(L.sh_up); d.shd = devq(L.sh_down);
+    d.gamma = L.rms_gamma;
+    d.lbias = L.logit_bias;
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  qmoe_status r = QMOE_OK;
+  if (hipMemcpyAsync(table, host, sizeof(StackLayerDev) * n_layers, hipMemcpyHostToDevice, st) !=
+          hipSuccess ||
+      hipStreamSynchronize(st) != hipSuccess)
+    r = QMOE_ERR_HIP;
+  delete[] host;
+  return r;
+}
+
+size_t qmoe_stack_workspace_bytes(const qmoe_moe_layer* L) {
+  if (check_layer(L) != QMOE_OK) return 0;
+  return stack_ws_bytes(L);
+}
+
+qmoe_status qmoe_stack_decode(const qmoe_moe_layer* L, const void* table, int32_t n_layers,
+                              const uint16_t* x, uint16_t* out, uint16_t* layer_out,
+                              int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
+                              void* stream) {
+  qmoe_status s = check_layer(L);
+  if (s != QMOE_OK) return s;
+  if (!table || !x || !out) return QMOE_ERR_NULL_ARG;
+  if (n_layers < 1 || n_layers > QMOE_MAX_LAYERS) return QMOE_ERR_BAD_SHAPE;
+  if (!al16(table) || !al16(x) || !al16(out) || (layer_out && !al16(layer_out)))
+    return QMOE_ERR_ALIGN;
+  if (x == out) return QMOE_ERR_BAD_SHAPE;
+  if (!ws || ws_bytes < stack_ws_bytes(L)) return QMOE_ERR_WORKSPACE;
+  uint8_t* w8 = static_cast<uint8_t*>(ws);
+  return launch_moe_stack(*L, table, n_layers, x, out, layer_out, idx_out, w_out, w8,
+                          reinterpret_cast<uint16_t*>(w8 + stack_xb_offset(L)), stream);
 }
 
 }  // extern "C"

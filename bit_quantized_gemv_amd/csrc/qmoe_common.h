@@ -215,10 +215,19 @@ constexpr int kFlagBase = kTagBase + kRep * kRepStride;   // per-block flag repl
 constexpr int kMaxFlags = kRepStride / 4;
 constexpr int kCntBase = kFlagBase + kRep * kRepStride;   // counters, 64 B apart
 constexpr int kCntRouterTile = 0;     // [16] standalone router: per token tile
-constexpr int kNCnt = kCntRouterTile + 16;
+constexpr int kCntStack = 16;         // layer stack: output blocks done with the last layer
+constexpr int kNCnt = kCntStack + 1;
 constexpr int kBytes = kCntBase + kNCnt * 64;
 }  // namespace ctl
 constexpr size_t kCtlBytes = (size_t)ctl::kBytes;
+
+// Device form of one layer of a decode stack (the pointers of
+// qmoe_moe_layer that change from layer to layer).
+struct StackLayerDev {
+  DevQ router, gate, up, down, shg, shu, shd;
+  const uint16_t* gamma;
+  const float* lbias;
+};
 
 // Launch modes of the decode step.
 constexpr int kStepFused = 0, kStepPhased = 1, kStepShared = 2, kStepRouted = 3;

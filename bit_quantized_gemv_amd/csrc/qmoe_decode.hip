@@ -43,6 +43,7 @@
 // waits for each load just before its first use, so the math of the first
 // chunks overlaps the transfer of the last ones.
 #include <hip/hip_ext.h>
+#include <string.h>
 
 #include "qmoe_common.h"
 
@@ -60,6 +61,8 @@ constexpr uint64_t kHoldTicks = 0;
 // LDS "sys" words at the start of every block's LDS
 constexpr int kSysEpoch = 0, kSysOk = 1, kSysIdx = 8, kSysW = 16, kSysRed = 32;
 constexpr int kSysTkIdx = 96, kSysTkW = 160;  // per-wave top-k of the standalone router
+constexpr int kSysXch = 96;    // top-k exchange slots (2k 64-bit words) of the step roles
+constexpr int kSysWait = 184;  // stack kernel: 64-bit length of the last wait for a layer input
 constexpr int kSysBytes = 768;
 
 __host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
@@ -87,6 +90,8 @@ struct DecodeArgs {
   int role0;                // role index of blockIdx.x == 0
   int nowait;               // 1: producers ran in earlier launches (no waits)
   int s_done;               // 1: the S blocks ran in an earlier launch
+  int dwait;                // stack: output blocks of the previous layer to wait for
+  uint32_t dtag;            // stack: their flag value
 };
 
 __device__ __forceinline__ uint32_t* ctl_of(const DecodeArgs& a) {
@@ -105,22 +110,27 @@ __device__ __forceinline__ float* act_of(const DecodeArgs& a, int r) {
 }
 
 // --------------------------------------------------------------- waits
-// The epoch of this call: every launch is a new packet of its queue, so the
-// packet's address differs from the previous launch's and is the same for
-// all of the launch's blocks.  Every flag and tag is rewritten by every
-// call, so only the previous call's values can be present when one starts.
+// The epoch of a one-layer call: every launch is a new packet of its queue,
+// so the packet's address differs from the previous launch's and is the
+// same for all of the launch's blocks.  Every flag and tag is rewritten by
+// every call, so only the previous call's values can be present when one
+// starts.  Epochs are odd; the layers of a stack call use even tags.
 __device__ __forceinline__ uint32_t launch_epoch() {
-  uint32_t e = (uint32_t)(reinterpret_cast<uintptr_t>(__builtin_amdgcn_dispatch_ptr()) >> 6);
-  return e ? e : 0x80000000u;
+  return ((uint32_t)(reinterpret_cast<uintptr_t>(__builtin_amdgcn_dispatch_ptr()) >> 6) << 1) | 1u;
 }
+
+// Tag of layer l of a stack call: even and nonzero.  A stack call leaves
+// every flag and tag at zero when it completes, so the tags of its layers
+// only have to differ from each other and from the odd one-layer epochs.
+__device__ __forceinline__ uint32_t stack_tag(int l) { return 2u * (uint32_t)(l + 1); }
 
 // One full wave: wait until flags[0..n) all equal `epoch`.  Every poll reads
 // all n flags at once (a few loads per lane), so the wait ends one round
 // trip after the last flag is raised.
 constexpr int kPollSleep = 6;  // s_sleep units (64 cycles) between polls
 __device__ bool wave_wait_flags(const uint32_t* flags, int n, uint32_t epoch, uint32_t* ctlw,
-                                uint32_t code) {
-  const int lane = threadIdx.x & 63;
+                                uint32_t code, int tid = threadIdx.x) {
+  const int lane = tid & 63;
   const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
   // a polling wave issues ahead of the bulk weight loads of its CU
   __builtin_amdgcn_s_setprio(2);
@@ -151,10 +161,10 @@ __device__ __forceinline__ void hold_until(uint64_t t0, uint64_t ticks) {
 
 // Whole block: wave `pw` waits, the others meet it at a barrier.
 __device__ bool block_wait_flags(const uint32_t* flags, int n, uint32_t epoch, uint32_t* ctlw,
-                                 uint32_t code, uint32_t* sys, int pw = 0) {
-  if ((int)(threadIdx.x >> 6) == pw) {
-    bool ok = wave_wait_flags(flags, n, epoch, ctlw, code);
-    if ((threadIdx.x & 63) == 0) sys[kSysOk] = ok ? 1u : 0u;
+                                 uint32_t code, uint32_t* sys, int pw = 0, int tid = threadIdx.x) {
+  if ((int)(tid >> 6) == pw) {
+    bool ok = wave_wait_flags(flags, n, epoch, ctlw, code, tid);
+    if ((tid & 63) == 0) sys[kSysOk] = ok ? 1u : 0u;
   }
   __syncthreads();
   bool ok = sys[kSysOk] != 0;
@@ -164,12 +174,56 @@ __device__ bool block_wait_flags(const uint32_t* flags, int n, uint32_t epoch, u
 
 // This block's device stores are complete: raise its flag (word `flag` of
 // every flag replica).
-__device__ void block_publish(const DecodeArgs& a, int flag, uint32_t epoch) {
+__device__ void block_publish(const DecodeArgs& a, int flag, uint32_t epoch, int tid = threadIdx.x) {
   wait_vm();
   __syncthreads();
-  if (threadIdx.x < ctl::kRep)
-    st_dev(reinterpret_cast<uint32_t*>(rep_of(a, ctl::kFlagBase, threadIdx.x)) + flag, epoch);
+  if (tid < ctl::kRep)
+    st_dev(reinterpret_cast<uint32_t*>(rep_of(a, ctl::kFlagBase, tid)) + flag, epoch);
 }
+
+// Stack layers: the whole block waits until every output block of the
+// previous layer has published (its rows of this layer's input are then
+// readable device-coherently).  Wave `pw` polls, but only after three
+// quarters of its previous wait for a layer input have passed: the flags
+// cannot rise much sooner, and the polls of several hundred waiting blocks
+// would otherwise load the memory system while the output blocks stage
+// their activations.
+__device__ bool wait_prev_layer(const DecodeArgs& a, uint32_t* sys, int pw, int tid = threadIdx.x) {
+  if (!a.dwait) return true;
+  const uint32_t* flags =
+      reinterpret_cast<const uint32_t*>(rep_of(a, ctl::kFlagBase, blockIdx.x % ctl::kRep)) +
+      a.nS + a.nG;
+  if ((int)(tid >> 6) == pw) {
+    uint64_t* last = reinterpret_cast<uint64_t*>(sys + kSysWait);
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    hold_until(t0, *last / 4 * 3);
+    bool ok = wave_wait_flags(flags, a.dwait, a.dtag, ctl_of(a), 4, tid);
+    if ((tid & 63) == 0) {
+      *last = __builtin_amdgcn_s_memrealtime() - t0;
+      sys[kSysOk] = ok ? 1u : 0u;
+    }
+  }
+  __syncthreads();
+  bool ok = sys[kSysOk] != 0;
+  __syncthreads();
+  return ok;
+}
+
+// Values made opaque to the compiler where they are used inside the layer
+// loop of the stack kernel, so that address arithmetic derived from them is
+// recomputed per layer instead of being hoisted out of the loop and held in
+// registers across it.
+__device__ __forceinline__ void opaque_s(int& v) { asm volatile("" : "+s"(v)); }
+__device__ __forceinline__ void opaque_v(int& v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ int opaque_tid() {
+  int t = threadIdx.x;
+  opaque_v(t);
+  return t;
+}
+
+struct NoPre {
+  __device__ void operator()() const {}
+};
 
 // ------------------------------------------------------------ reductions
 template <int CTRL>
@@ -191,11 +245,11 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 
 // Block-wide sum of one float per thread (fixed order; same bits everywhere).
-__device__ float block_sum(float v, float* red) {
+__device__ float block_sum(float v, float* red, int tid = threadIdx.x) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  int wave = threadIdx.x >> 6;
+  int wave = tid >> 6;
   __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[wave] = v;
+  if ((tid & 63) == 0) red[wave] = v;
   __syncthreads();
   float s = 0.f;
   for (int i = 0; i < kWavesPerBlock; ++i) s += red[i];
@@ -209,8 +263,8 @@ __device__ float block_sum(float v, float* red) {
 // (LDS) and, optionally, to idx2/w2.
 template <int NV>
 __device__ void wave_topk_vals(const float (&v)[NV], int E, int K, int32_t* idx_s, float* w_s,
-                               int32_t* idx2, float* w2) {
-  const int lane = threadIdx.x & 63;
+                               int32_t* idx2, float* w2, int tid = threadIdx.x) {
+  const int lane = tid & 63;
   uint32_t live = 0;
 #pragma unroll
   for (int m = 0; m < NV; ++m)
@@ -262,14 +316,96 @@ __device__ void wave_topk(const float* lg, int E, int K, int32_t* idx_s, float* 
   wave_topk_vals<QMOE_MAX_EXPERTS / 64>(v, E, K, idx_s, w_s, idx2, w2);
 }
 
+// Order value of a logit: an unsigned integer that increases with the
+// fp32 value (-0 counts as +0), and back.
+__device__ __forceinline__ uint32_t topk_ord(float f) {
+  const uint32_t b = __float_as_uint(f + 0.0f);
+  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+}
+__device__ __forceinline__ float topk_value(uint32_t u) {
+  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+}
+
+// One wave: the same top-k and softmax as wave_topk_vals (descending
+// logits, equal logits by lower index; p_j = exp(l_j - l_max), w_j = p_j /
+// sum(p) summed in rank order), with a short dependency chain:
+//   1. T = the k-th largest order value, bit by bit from the top: keep a
+//      bit when at least k order values are >= the prefix with it (one
+//      ballot count per value slot and bit);
+//   2. the k selected are the values above T and, in index order, the
+//      first k - #(above T) of those equal to T (ballot prefix counts);
+//   3. they are gathered into k slots of `xch` (LDS, 2k words of 8 bytes)
+//      as (order value, complemented index) keys, and lane j < k ranks
+//      slot j against the k keys;
+//   4. lane j takes rank j for the softmax.
+template <int NV>
+__device__ void wave_topk_radix(const float (&v)[NV], int E, int K, int32_t* idx_s, float* w_s,
+                                int32_t* idx2, float* w2, uint64_t* xch, int tid = threadIdx.x) {
+  const int lane = tid & 63;
+  const uint64_t below = (1ull << lane) - 1ull;
+  uint32_t o[NV];
+#pragma unroll
+  for (int m = 0; m < NV; ++m) o[m] = lane + 64 * m < E ? topk_ord(v[m]) : 0u;  // 0: no expert
+  uint32_t T = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = T | (1u << b);
+    uint32_t n = 0;
+#pragma unroll
+    for (int m = 0; m < NV; ++m) n += (uint32_t)__popcll(__ballot(o[m] >= c));
+    if (n >= (uint32_t)K) T = c;
+  }
+  uint32_t above = 0;
+#pragma unroll
+  for (int m = 0; m < NV; ++m) above += (uint32_t)__popcll(__ballot(o[m] > T));
+  const uint32_t need = (uint32_t)K - above;
+  uint32_t ties = 0, base = 0;
+#pragma unroll
+  for (int m = 0; m < NV; ++m) {
+    const uint64_t tie = __ballot(o[m] == T);
+    const bool take =
+        o[m] > T || (o[m] == T && ties + (uint32_t)__popcll(tie & below) < need);
+    ties += (uint32_t)__popcll(tie);
+    const uint64_t sel = __ballot(take);
+    if (take)
+      xch[base + (uint32_t)__popcll(sel & below)] =
+          ((uint64_t)o[m] << 32) | (uint32_t)~(lane + 64 * m);
+    base += (uint32_t)__popcll(sel);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  if (lane < K) {
+    const uint64_t kj = xch[lane];
+    uint32_t r = 0;
+    for (int j = 0; j < K; ++j) r += xch[j] > kj ? 1u : 0u;
+    xch[K + r] = kj;
+  }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  float p = 0.f;
+  int e = 0;
+  if (lane < K) {
+    const uint64_t kr = xch[K + lane];
+    e = (int)~(uint32_t)kr;
+    p = expf(topk_value((uint32_t)(kr >> 32)) - topk_value((uint32_t)(xch[K] >> 32)));
+  }
+  float sum = 0.f;
+  for (int j = 0; j < K; ++j)
+    sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), j));
+  if (lane < K) {
+    const float wj = p / sum;
+    idx_s[lane] = e;
+    w_s[lane] = wj;
+    if (idx2) idx2[lane] = e;
+    if (w2) w2[lane] = wj;
+  }
+}
+
 // One wave: wait until all E tagged logits of one replica carry `epoch`
 // (each is (epoch << 32) | fp32 bits, written with one 64-bit store), then
 // top-k on them.  Every poll reads all of them.  In a launch that follows
 // its producers, no waiting.
 template <int NV>
 __device__ bool wave_routing(const DecodeArgs& a, uint32_t epoch, int32_t* idx_s, float* w_s,
-                             bool write_out) {
-  const int lane = threadIdx.x & 63;
+                             bool write_out, uint64_t* xch, int tid = threadIdx.x) {
+  const int lane = tid & 63;
   const uint64_t* tag = reinterpret_cast<const uint64_t*>(
       rep_of(a, ctl::kTagBase, blockIdx.x % ctl::kRep));
   uint32_t* ctlw = ctl_of(a);
@@ -282,7 +418,7 @@ __device__ bool wave_routing(const DecodeArgs& a, uint32_t epoch, int32_t* idx_s
     for (int m = 0; m < NV; ++m) {
       const int e = lane + 64 * m;
       const uint64_t t = ld_dev(tag + min(e, a.E - 1));
-      v[m] = e < a.E ? __uint_as_float((uint32_t)t) : -INFINITY;
+      v[m] = __uint_as_float((uint32_t)t);
       ok = ok && (a.nowait || (uint32_t)(t >> 32) == epoch);
     }
     if (__all(ok)) break;
@@ -295,29 +431,33 @@ __device__ bool wave_routing(const DecodeArgs& a, uint32_t epoch, int32_t* idx_s
     }
     __builtin_amdgcn_s_sleep(kPollSleep);
   }
+  // the selection runs at the polling priority: it is on every consumer's
+  // critical path
+  wave_topk_radix<NV>(v, a.E, a.K, idx_s, w_s, write_out ? a.idx_out : nullptr,
+                      write_out ? a.w_out : nullptr, xch, tid);
   __builtin_amdgcn_s_setprio(0);
-  wave_topk_vals<NV>(v, a.E, a.K, idx_s, w_s, write_out ? a.idx_out : nullptr,
-                     write_out ? a.w_out : nullptr);
   return true;
 }
 
 // Routing for a consumer block: from the caller's arrays, or from the
 // router blocks' published logits.  Leaves idx/w in sys LDS.
 template <int NV>
-__device__ bool block_routing(const DecodeArgs& a, uint32_t epoch, uint32_t* sys, bool write_out) {
+__device__ bool block_routing(const DecodeArgs& a, uint32_t epoch, uint32_t* sys, bool write_out,
+                              int tid = threadIdx.x) {
   int32_t* idx_s = reinterpret_cast<int32_t*>(sys + kSysIdx);
   float* w_s = reinterpret_cast<float*>(sys + kSysW);
   if (a.idx_in) {
-    if (threadIdx.x < a.K) {
-      idx_s[threadIdx.x] = a.idx_in[threadIdx.x];
-      w_s[threadIdx.x] = a.w_in[threadIdx.x];
+    if (tid < a.K) {
+      idx_s[tid] = a.idx_in[tid];
+      w_s[tid] = a.w_in[tid];
     }
     __syncthreads();
     return true;
   }
-  if (threadIdx.x < 64) {
-    bool ok = wave_routing<NV>(a, epoch, idx_s, w_s, write_out);
-    if (threadIdx.x == 0) sys[kSysOk] = ok ? 1u : 0u;
+  if (tid < 64) {
+    bool ok = wave_routing<NV>(a, epoch, idx_s, w_s, write_out,
+                               reinterpret_cast<uint64_t*>(sys + kSysXch), tid);
+    if (tid == 0) sys[kSysOk] = ok ? 1u : 0u;
   }
   __syncthreads();
   bool ok = sys[kSysOk] != 0;
@@ -346,19 +486,31 @@ __device__ __forceinline__ uint4 norm_word(uint4 r, const uint16_t* gamma, float
 struct XRegs {
   uint4 w[kMaxXW];
 };
-__device__ __forceinline__ void x_load(XRegs& X, const uint16_t* x, int H) {
+__device__ __forceinline__ void x_load(XRegs& X, const uint16_t* x, int H, int tid = threadIdx.x) {
   const uint4* x4 = reinterpret_cast<const uint4*>(x);
   const int Wn = H / 8;
 #pragma unroll
-  for (int i = 0; i < kMaxXW; ++i) X.w[i] = x4[min((int)threadIdx.x + i * kBlock, Wn - 1)];
+  for (int i = 0; i < kMaxXW; ++i) X.w[i] = x4[min(tid + i * kBlock, Wn - 1)];
 }
 
-__device__ float x_inv_rms(const XRegs& X, const uint16_t* x, int H, float eps, float* red) {
+// The same words read device-coherently: the layer input of a stack layer
+// was written by other blocks of the launch.
+__device__ __forceinline__ void x_load_dev(XRegs& X, const uint16_t* x, int H, int tid = threadIdx.x) {
+  const float* xf = reinterpret_cast<const float*>(x);
+  const int Wn = H / 8;
+#pragma unroll
+  for (int i = 0; i < kMaxXW; ++i) {
+    const uint32_t v = (uint32_t)min(tid + i * kBlock, Wn - 1);
+    X.w[i] = __builtin_bit_cast(uint4, ld_dev16(xf, (uint32_t)H * 2, v * 16));
+  }
+}
+
+__device__ float x_inv_rms(const XRegs& X, const uint16_t* x, int H, float eps, float* red, int tid = threadIdx.x) {
   float ss = 0.f;
   const int Wn = H / 8;
   const uint4* x4 = reinterpret_cast<const uint4*>(x);
   for (int i = 0; i * kBlock < Wn; ++i) {
-    int v = threadIdx.x + i * kBlock;
+    int v = tid + i * kBlock;
     if (v >= Wn) break;
     uint4 w;
     if (i < kMaxXW) {
@@ -377,7 +529,7 @@ __device__ float x_inv_rms(const XRegs& X, const uint16_t* x, int H, float eps, 
       ss = fmaf(hi, hi, ss);
     }
   }
-  ss = block_sum(ss, red);
+  ss = block_sum(ss, red, tid);
   return 1.0f / sqrtf(ss / (float)H + eps);
 }
 
@@ -422,13 +574,13 @@ __device__ __forceinline__ void put_f32(uint4 r, int v, bool ok, int CH8, float4
 // words held in X are used; words beyond kMaxXW per thread are loaded here.
 template <bool PAIRS>
 __device__ void x_stage(const XRegs& X, const uint16_t* x, const uint16_t* gamma, float inv, int H,
-                        void* dst, float* xh) {
+                        void* dst, float* xh, int tid = threadIdx.x) {
   const int Wn = H / 8;
   const uint4* x4 = reinterpret_cast<const uint4*>(x);
 #pragma unroll
   for (int i = 0; i < kMaxXW; ++i) {
     if (i * kBlock < Wn) {
-      int v = threadIdx.x + i * kBlock;
+      int v = tid + i * kBlock;
       bool ok = v < Wn;
       uint4 r = ok ? norm_word(X.w[i], gamma, inv, v) : make_uint4(0, 0, 0, 0);
       if (PAIRS)
@@ -438,7 +590,7 @@ __device__ void x_stage(const XRegs& X, const uint16_t* x, const uint16_t* gamma
     }
   }
   for (int i = kMaxXW; i * kBlock < Wn; ++i) {
-    int v = threadIdx.x + i * kBlock;
+    int v = tid + i * kBlock;
     bool ok = v < Wn;
     uint4 r = ok ? norm_word(x4[v], gamma, inv, v) : make_uint4(0, 0, 0, 0);
     if (PAIRS)
@@ -465,8 +617,8 @@ struct Rows4 {
 // lanes past the row-block's units re-read its last one.
 template <int NM, int SP>
 __device__ __forceinline__ void rows4_load_sb(Rows4<NM, SP>& R, const DevQ (&m)[NM], int row0,
-                                              int rows, int G) {
-  const int lane = threadIdx.x & 63;
+                                              int rows, int G, int tid = threadIdx.x) {
+  const int lane = tid & 63;
   const int64_t total = (int64_t)rows * G / 8;          // whole units in the array
   const int64_t first = (int64_t)min(row0, rows - 1) * G / 8;
   const int64_t u = min(first + min(lane, G - 1), total - 1);
@@ -495,8 +647,8 @@ __device__ __forceinline__ void put_sb8(uint4 sv, uint4 bv, uint32_t* dst) {
 // G <= 64 (one unit per lane); otherwise pairs are copied one by one.
 template <int NM, int SP>
 __device__ __forceinline__ void rows4_put_sb(const Rows4<NM, SP>& R, const DevQ (&m)[NM], int row0,
-                                             int rows, int G, uint32_t* sbl) {
-  const int lane = threadIdx.x & 63;
+                                             int rows, int G, uint32_t* sbl, int tid = threadIdx.x) {
+  const int lane = tid & 63;
   const int nr = max(0, min(kRowsPerUnit, rows - row0));
   const bool fast = nr == kRowsPerUnit && G <= 64;
 #pragma unroll
@@ -558,18 +710,18 @@ __device__ __forceinline__ void rows4_compute(const Rows4<NM, SP>& R, const uint
 template <int NM, int CWC, typename StageFn>
 __device__ __forceinline__ void rows4_run(const DevQ (&m)[NM], int row0, int rows, int H, int c0,
                                           int CW_rt, const uint4* xs, const float* xh,
-                                          uint32_t* sbl, StageFn stage, float (&acc)[NM]) {
+                                          uint32_t* sbl, StageFn stage, float (&acc)[NM], int tid = threadIdx.x) {
   constexpr int SP = CWC ? cdiv(CWC, kSlots) : kSP;
   const int CW = CWC ? CWC : CW_rt;
   const int CH = H / 32, G = CH / 2, nsteps = cdiv(CW, kSlots);
-  const int lane = threadIdx.x & 63, r = lane & 7, p = lane >> 3;
+  const int lane = tid & 63, r = lane & 7, p = lane >> 3;
   const int row = min(row0 + r, rows - 1);
   Rows4<NM, SP> R;
 #pragma unroll
   for (int k = 0; k < NM; ++k) acc[k] = 0.f;
-  rows4_load_sb<NM, SP>(R, m, row0, rows, G);
+  rows4_load_sb<NM, SP>(R, m, row0, rows, G, tid);
   rows4_load<NM, SP>(R, m, row, CH, c0, CW, 0, p);
-  rows4_put_sb<NM, SP>(R, m, row0, rows, G, sbl);
+  rows4_put_sb<NM, SP>(R, m, row0, rows, G, sbl, tid);
   stage();
   rows4_compute<NM, SP>(R, xs, xh, sbl, r, G, CH, c0, CW, 0, p, acc);
   if (!CWC) {
@@ -659,8 +811,8 @@ struct RRegs {
 };
 template <int SR>
 __device__ __forceinline__ void router_load(RRegs<SR>& R, const DevQ& Wr, int row0, int E, int H,
-                                            int s0) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 7, p = lane >> 3;
+                                            int s0, int tid = threadIdx.x) {
+  const int wave = tid >> 6, lane = tid & 63, r = lane & 7, p = lane >> 3;
   const int CH8 = H / 16, G = H / 64, row = min(row0 + r, E - 1);
 #pragma unroll
   for (int i = 0; i < SR; ++i) {
@@ -671,8 +823,8 @@ __device__ __forceinline__ void router_load(RRegs<SR>& R, const DevQ& Wr, int ro
 }
 template <int SR>
 __device__ __forceinline__ float router_compute(const RRegs<SR>& R, int H, int s0,
-                                                const float4* xr, const float* xh, float acc) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, p = lane >> 3;
+                                                const float4* xr, const float* xh, float acc, int tid = threadIdx.x) {
+  const int wave = tid >> 6, lane = tid & 63, p = lane >> 3;
   const int CH8 = H / 16;
 #pragma unroll
   for (int i = 0; i < SR; ++i) {
@@ -690,45 +842,52 @@ __device__ __forceinline__ float router_compute(const RRegs<SR>& R, int H, int s
   return acc;
 }
 // Sum the 4 waves' row partials: returns the logit in threads 0..7.
-__device__ float router_finish(float acc, float* red) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+__device__ float router_finish(float acc, float* red, int tid = threadIdx.x) {
+  const int wave = tid >> 6, lane = tid & 63;
   acc = rowblock_sum(acc);
   if ((lane >> 3) == 0) red[wave * 8 + (lane & 7)] = acc;
   __syncthreads();
   float s = 0.f;
-  if (threadIdx.x < 8)
-    for (int w = 0; w < kWavesPerBlock; ++w) s += red[w * 8 + threadIdx.x];
+  if (tid < 8)
+    for (int w = 0; w < kWavesPerBlock; ++w) s += red[w * 8 + tid];
   __syncthreads();
   return s;
 }
 
 // One token's logits for rows [row0, row0+8) (threads 0..7 hold them).
-// H8C: H/16 when known at compile time (0: runtime).
-template <int H8C>
+// H8C: H/16 when known at compile time (0: runtime).  XDEV: the input is
+// read device-coherently after the first weight loads are issued and
+// `pre` (a whole-block wait) has returned.
+template <int H8C, bool XDEV = false, typename Pre = NoPre>
 __device__ float router_token(const DevQ& Wr, int row0, int E, int H_rt, const uint16_t* x,
-                              const uint16_t* gamma, float eps, float4* xr, float* xh, float* red) {
+                              const uint16_t* gamma, float eps, float4* xr, float* xh, float* red,
+                              Pre pre = Pre(), int tid = threadIdx.x) {
   constexpr int SR = H8C ? cdiv(cdiv(H8C, kSlots), kWavesPerBlock) : kSR;
   const int H = H8C ? H8C * 16 : H_rt;
   const int nsteps = cdiv(H / 16, kSlots);
   XRegs X;
-  x_load(X, x, H);
+  if constexpr (!XDEV) x_load(X, x, H, tid);
   float acc = 0.f;
   {
     RRegs<SR> R;
-    router_load<SR>(R, Wr, row0, E, H, 0);
-    float inv = gamma ? x_inv_rms(X, x, H, eps, red) : 1.f;
-    x_stage<false>(X, x, gamma, inv, H, xr, xh);
+    router_load<SR>(R, Wr, row0, E, H, 0, tid);
+    if constexpr (XDEV) {
+      pre();
+      x_load_dev(X, x, H, tid);
+    }
+    float inv = gamma ? x_inv_rms(X, x, H, eps, red, tid) : 1.f;
+    x_stage<false>(X, x, gamma, inv, H, xr, xh, tid);
     __syncthreads();
-    acc = router_compute<SR>(R, H, 0, xr, xh, acc);
+    acc = router_compute<SR>(R, H, 0, xr, xh, acc, tid);
   }
   if (!H8C) {
     for (int s0 = SR * kWavesPerBlock; s0 < nsteps; s0 += SR * kWavesPerBlock) {
       RRegs<SR> R;
-      router_load<SR>(R, Wr, row0, E, H, s0);
-      acc = router_compute<SR>(R, H, s0, xr, xh, acc);
+      router_load<SR>(R, Wr, row0, E, H, s0, tid);
+      acc = router_compute<SR>(R, H, s0, xr, xh, acc, tid);
     }
   }
-  return router_finish(acc, red);
+  return router_finish(acc, red, tid);
 }
 
 // Standalone router for T tokens: grid (ceil(E/8), ceil(T/kTokTile)); the
@@ -795,29 +954,46 @@ __global__ __launch_bounds__(kBlock) void k_router(DevQ Wr, const float* lbias, 
 // ========================================================= MoE FFN step
 constexpr int kSysLg = 64;  // sys words: the router block's 8 logits
 
-template <int HC>
-__device__ void role_router(const DecodeArgs& a, int b, uint8_t* smem, uint32_t epoch) {
+// STK: a stack layer (router weights issued, then the wait for the layer
+// input).  Returns false when a wait gave up.
+template <int HC, bool STK>
+__device__ bool role_router(const DecodeArgs& a, int b, uint8_t* smem, uint32_t epoch) {
   // the router is on every other block's critical path: its waves issue first
   __builtin_amdgcn_s_setprio(3);
   uint32_t* sys = reinterpret_cast<uint32_t*>(smem);
+  int tid = threadIdx.x;
+  if constexpr (STK) opaque_v(tid);
   const int H = HC ? HC : a.H;
   float4* xr = reinterpret_cast<float4*>(smem + kSysBytes);
   float* xh = reinterpret_cast<float*>(smem + kSysBytes + (size_t)H * 4);
   float* red = reinterpret_cast<float*>(sys + kSysRed);
   const int row0 = b * kRowsPerUnit;
-  float s = router_token<HC / 16>(a.router, row0, a.E, H, a.x, a.gamma, a.eps, xr, xh, red);
-  if (threadIdx.x < 8) {
-    int e = min(row0 + (int)threadIdx.x, a.E - 1);
+  bool ok = true;
+  float s;
+  if constexpr (STK) {
+    s = router_token<HC / 16, true>(a.router, row0, a.E, H, a.x, a.gamma, a.eps, xr, xh, red,
+                                    [&] {
+                                      ok = wait_prev_layer(a, sys, 0, tid);
+                                      __builtin_amdgcn_s_setprio(3);
+                                    },
+                                    tid);
+    if (!ok) return false;
+  } else {
+    s = router_token<HC / 16>(a.router, row0, a.E, H, a.x, a.gamma, a.eps, xr, xh, red);
+  }
+  if (tid < 8) {
+    int e = min(row0 + tid, a.E - 1);
     if (a.lbias) s += a.lbias[e];
-    reinterpret_cast<float*>(sys + kSysLg)[threadIdx.x] = s;
+    reinterpret_cast<float*>(sys + kSysLg)[tid] = s;
   }
   __syncthreads();
   // publish (epoch, logit) pairs in every replica: one 64-bit store each
-  const int j = threadIdx.x & 7, rep = threadIdx.x >> 3;
+  const int j = tid & 7, rep = tid >> 3;
   if (rep < ctl::kRep && row0 + j < a.E) {
     uint64_t v = ((uint64_t)epoch << 32) | __float_as_uint(reinterpret_cast<float*>(sys + kSysLg)[j]);
     st_dev(reinterpret_cast<uint64_t*>(rep_of(a, ctl::kTagBase, rep)) + row0 + j, v);
   }
+  return true;
 }
 
 // Gate/up of 16 rows (two row-blocks of 8): wave w computes matrix (w & 1:
@@ -835,21 +1011,26 @@ __device__ __forceinline__ DevQ rows_below(DevQ m, int H) {
   return m;
 }
 
-template <int HC, int NV>
-__device__ void role_gate_up(const DecodeArgs& a, int expert_rank, int rb, int rows,
+// STK: a stack layer; the layer input is read device-coherently after the
+// wait for the previous layer (the shared expert's weights are issued
+// before it).  Returns false when a wait gave up.
+template <int HC, int NV, bool STK>
+__device__ bool role_gate_up(const DecodeArgs& a, int expert_rank, int rb, int rows,
                              uint8_t* smem, uint32_t epoch, uint64_t t_start) {
   uint32_t* sys = reinterpret_cast<uint32_t*>(smem);
+  int tid = threadIdx.x;
+  if constexpr (STK) opaque_v(tid);
   const int H = HC ? HC : a.H;
   uint4* xs = reinterpret_cast<uint4*>(smem + kSysBytes);
   float* xh = reinterpret_cast<float*>(smem + gu_xh_off(H));
   float* red = reinterpret_cast<float*>(sys + kSysRed);
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wave = tid >> 6, lane = tid & 63;
   const int mi = wave & 1, half = wave >> 1;
   uint32_t* sbl = reinterpret_cast<uint32_t*>(smem + gu_sb_off(H)) + wave * gu_sb_words(H);
   const int row0 = rb * kGuRows;  // rows is a multiple of 16: both row-blocks are whole
   const int CWh = H / 64;  // chunks per column half
   XRegs X;
-  x_load(X, a.x, H);
+  if constexpr (!STK) x_load(X, a.x, H, tid);
   DevQ m[2];
   size_t dst;  // element offset inside an activation replica
   float acc[2];
@@ -858,25 +1039,35 @@ __device__ void role_gate_up(const DecodeArgs& a, int expert_rank, int rb, int r
     m[0] = mi ? a.shu : a.shg;
     m[1] = rows_below(m[0], H);
     dst = 0;
+    bool ok = true;
     rows4_run<2, HC / 64>(m, row0, rows, H, half * CWh, CWh, xs, xh, sbl,
                           [&] {
-                            float inv = a.gamma ? x_inv_rms(X, a.x, H, a.eps, red) : 1.f;
-                            x_stage<true>(X, a.x, a.gamma, inv, H, xs, xh);
+                            if constexpr (STK) {
+                              ok = wait_prev_layer(a, sys, 0, tid);
+                              x_load_dev(X, a.x, H, tid);
+                            }
+                            float inv = a.gamma ? x_inv_rms(X, a.x, H, a.eps, red, tid) : 1.f;
+                            x_stage<true>(X, a.x, a.gamma, inv, H, xs, xh, tid);
                             __syncthreads();
                           },
-                          acc);
+                          acc, tid);
+    if (!ok) return false;
   } else {
+    if constexpr (STK) {
+      if (!wait_prev_layer(a, sys, 0, tid)) return false;
+      x_load_dev(X, a.x, H, tid);
+    }
     // stage h while the router finishes, then resolve the expert
-    float inv = a.gamma ? x_inv_rms(X, a.x, H, a.eps, red) : 1.f;
-    x_stage<true>(X, a.x, a.gamma, inv, H, xs, xh);
+    float inv = a.gamma ? x_inv_rms(X, a.x, H, a.eps, red, tid) : 1.f;
+    x_stage<true>(X, a.x, a.gamma, inv, H, xs, xh, tid);
     __syncthreads();
-    if (!block_routing<NV>(a, epoch, sys, false)) return;
+    if (!block_routing<NV>(a, epoch, sys, false, tid)) return false;
     int e = reinterpret_cast<int32_t*>(sys + kSysIdx)[expert_rank];
     int s = a.slot ? a.slot[e] : e;
     m[0] = devq_at(mi ? a.up : a.gate, s);
     m[1] = rows_below(m[0], H);
     dst = (size_t)a.Is + (size_t)expert_rank * a.I;
-    rows4_run<2, HC / 64>(m, row0, rows, H, half * CWh, CWh, xs, xh, sbl, [] {}, acc);
+    rows4_run<2, HC / 64>(m, row0, rows, H, half * CWh, CWh, xs, xh, sbl, [] {}, acc, tid);
   }
   if ((lane >> 3) == 0) {
     red[(wave * 2 + 0) * 8 + (lane & 7)] = acc[0];
@@ -884,13 +1075,14 @@ __device__ void role_gate_up(const DecodeArgs& a, int expert_rank, int rb, int r
   }
   __syncthreads();
   // a = gelu(g) * u for the 16 rows, stored in every activation replica
-  const int t = threadIdx.x & 15, rep = threadIdx.x >> 4;
+  const int t = tid & 15, rep = tid >> 4;
   if (rep < ctl::kRep) {
     const int k = t >> 3, rr = t & 7;
     float g = red[((0 * 2 + k) * 8) + rr] + red[((2 * 2 + k) * 8) + rr];
     float u = red[((1 * 2 + k) * 8) + rr] + red[((3 * 2 + k) * 8) + rr];
     st_dev(act_of(a, rep) + dst + row0 + t, gelu_tanh(g) * u);
   }
+  return true;
 }
 
 // Activations [off, off + n) of a replica (fp32) -> LDS in one pass: each
@@ -899,23 +1091,23 @@ __device__ void role_gate_up(const DecodeArgs& a, int expert_rank, int rb, int r
 // `seg` values (the shared activations, or one expert's): per segment
 // (CH = seg/32 chunks), word v = 4c + j (8 values) goes to the even/odd
 // layout as[(2j+e)*CH + c] and ah[c] is the sum of chunk c.  The caller
-// passes the run's value and chunk-sum bases.
+// passes the run's value and chunk-sum bases; tid is threadIdx.x.
 constexpr int kStageUnroll = 4;  // words (8 floats) per thread per pass
 __device__ __forceinline__ void stage_run(const float* act, int off, int n, int seg, float4* as,
-                                          float* ah) {
+                                          float* ah, int tid) {
   const int Wn = n / 8, Wseg = seg / 8, CH = seg / 32;
   const uint32_t nbytes = (uint32_t)(off + n) * 4;
   for (int v0 = 0; v0 < Wn; v0 += kStageUnroll * kBlock) {
     float4 lo[kStageUnroll], hi[kStageUnroll];
 #pragma unroll
     for (int u = 0; u < kStageUnroll; ++u) {
-      const uint32_t v = (uint32_t)(v0 + u * kBlock + threadIdx.x);
+      const uint32_t v = (uint32_t)(v0 + u * kBlock + tid);
       lo[u] = ld_dev16(act, nbytes, (uint32_t)off * 4 + v * 32);  // past the end: zeros
       hi[u] = ld_dev16(act, nbytes, (uint32_t)off * 4 + v * 32 + 16);
     }
 #pragma unroll
     for (int u = 0; u < kStageUnroll; ++u) {
-      const int v = v0 + u * kBlock + threadIdx.x;
+      const int v = v0 + u * kBlock + tid;
       float s = ((lo[u].x + lo[u].y) + (lo[u].z + lo[u].w)) +
                 ((hi[u].x + hi[u].y) + (hi[u].z + hi[u].w));
       s += __shfl_xor(s, 1);
@@ -973,8 +1165,8 @@ __device__ __forceinline__ void dtask_acc(const DTask& T, const float4* as, cons
 // Sum acc[0..8) of every lane of the block, per row; threads 0..7 return
 // rows 0..7 (fixed order: a reduce-scatter over the wave, then the waves
 // in turn).
-__device__ float rows8_block_sum(float (&acc)[kRowsPerUnit], float* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+__device__ float rows8_block_sum(float (&acc)[kRowsPerUnit], float* red, int tid = threadIdx.x) {
+  const int lane = tid & 63, wave = tid >> 6;
   float v4[4], v2[2];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -1005,8 +1197,8 @@ __device__ float rows8_block_sum(float (&acc)[kRowsPerUnit], float* red) {
   if ((lane & 7) == 0) red[wave * 8 + (lane >> 3)] = v;
   __syncthreads();
   float s = 0.f;
-  if (threadIdx.x < kRowsPerUnit)
-    for (int w = 0; w < kWavesPerBlock; ++w) s += red[w * 8 + threadIdx.x];
+  if (tid < kRowsPerUnit)
+    for (int w = 0; w < kWavesPerBlock; ++w) s += red[w * 8 + tid];
   return s;
 }
 
@@ -1022,9 +1214,13 @@ __device__ float rows8_block_sum(float (&acc)[kRowsPerUnit], float* red) {
 // starts, the waits are polled by the last wave (its tasks are shared ones,
 // loaded early) and every staging is one round trip.  IC/ISC: expert and
 // shared intermediate sizes when known (0: runtime).
-template <int IC, int ISC, int NV>
-__device__ void role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t epoch,
-                          uint64_t t_start) {
+// STK: a stack layer.  The residual is the block's own output rows of the
+// previous layer, kept in `held` (threads 0..7; a.residual for the first
+// layer); the output goes device-coherently to a.out (the next layer's
+// input) and, if given, to `lout`.  Returns false when a wait gave up.
+template <int IC, int ISC, int NV, bool STK>
+__device__ bool role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t epoch,
+                          uint64_t t_start, uint32_t& held, uint16_t* lout) {
   uint32_t* sys = reinterpret_cast<uint32_t*>(smem);
   const int K = a.K;
   const int I = IC ? IC : a.I, Is = ISC ? ISC : a.Is;
@@ -1043,7 +1239,8 @@ __device__ void role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
       reinterpret_cast<const uint32_t*>(rep_of(a, ctl::kFlagBase, blockIdx.x % ctl::kRep));
   const int row0 = b * kRowsPerUnit;  // H is a multiple of 64: all 8 rows exist
   const int nrt = K * CHk, ntask = nrt + CHs;
-  const int t = threadIdx.x;
+  int t = threadIdx.x;
+  if constexpr (STK) opaque_v(t);
   const bool routed = t < nrt;
   float acc[kRowsPerUnit];
 #pragma unroll
@@ -1054,7 +1251,7 @@ __device__ void role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
   hold_until(t_start, kHoldTicks);
   if (kOnePass && !routed) dtask_load(T, a.shd, row0, CHs, min(t - nrt, CHs - 1));
   // 2. routing, then at once the routed-down weights
-  if (!block_routing<NV>(a, epoch, sys, b == 0)) return;
+  if (!block_routing<NV>(a, epoch, sys, b == 0, t)) return false;
   const int32_t* idx_s = reinterpret_cast<const int32_t*>(sys + kSysIdx);
   const float* w_s = reinterpret_cast<const float*>(sys + kSysW);
   if (kOnePass && routed) {
@@ -1064,9 +1261,9 @@ __device__ void role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
   }
   // 3. shared activations once the S blocks are published, shared part
   if (!a.nowait && !a.s_done &&
-      !block_wait_flags(flags, a.nS, epoch, ctlw, 2, sys, kPollWave))
-    return;
-  stage_run(act_of(a, blockIdx.x % ctl::kRep), 0, Is, Is, as_sh, ah_sh);
+      !block_wait_flags(flags, a.nS, epoch, ctlw, 2, sys, kPollWave, t))
+    return false;
+  stage_run(act_of(a, blockIdx.x % ctl::kRep), 0, Is, Is, as_sh, ah_sh, t);
   __syncthreads();
   if (kOnePass) {
     if (!routed && t < ntask) dtask_acc(T, as_sh, ah_sh, CHs, t - nrt, 1.0f, acc);
@@ -1080,9 +1277,9 @@ __device__ void role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
   // 4. one wait for the G blocks of all K experts, their activations in one
   //    pass, routed part
   if (!a.nowait &&
-      !block_wait_flags(flags + a.nS, K * a.perG, epoch, ctlw, 3, sys, kPollWave))
-    return;
-  stage_run(act_of(a, blockIdx.x % ctl::kRep), Is, K * I, I, as_sh + Is / 4, ah_sh + Is / 32);
+      !block_wait_flags(flags + a.nS, K * a.perG, epoch, ctlw, 3, sys, kPollWave, t))
+    return false;
+  stage_run(act_of(a, blockIdx.x % ctl::kRep), Is, K * I, I, as_sh + Is / 4, ah_sh + Is / 32, t);
   __syncthreads();
   if (kOnePass) {
     if (routed) {
@@ -1099,12 +1296,28 @@ __device__ void role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
     }
   }
   // 5. combine: rows over the block, residual, bf16
-  float s = rows8_block_sum(acc, red);
-  if (threadIdx.x < kRowsPerUnit) {
-    const int rr = row0 + threadIdx.x;
-    if (a.residual) s += bf16_to_f32(a.residual[rr]);
-    a.out[rr] = f32_to_bf16(s);
+  float s = rows8_block_sum(acc, red, t);
+  if constexpr (STK) {
+    uint32_t o = 0;
+    if (t < kRowsPerUnit) {
+      const int rr = row0 + t;
+      s += bf16_to_f32(a.residual ? (uint32_t)a.residual[rr] : held);
+      o = f32_to_bf16(s);
+      held = o;
+      if (lout) lout[rr] = (uint16_t)o;
+    }
+    // rows in pairs: one 32-bit device-coherent store per two rows
+    const uint32_t nb = (uint32_t)__shfl_down((int)o, 1);
+    if (t < kRowsPerUnit && !(t & 1))
+      st_dev(reinterpret_cast<uint32_t*>(a.out + row0 + t), o | (nb << 16));
+  } else {
+    if (threadIdx.x < kRowsPerUnit) {
+      const int rr = row0 + threadIdx.x;
+      if (a.residual) s += bf16_to_f32(a.residual[rr]);
+      a.out[rr] = f32_to_bf16(s);
+    }
   }
+  return true;
 }
 
 // EC: number of experts when known at compile time (0: up to 512).
@@ -1116,18 +1329,135 @@ __global__ __launch_bounds__(kBlock) void k_moe_step(DecodeArgs a) {
   const uint32_t epoch = launch_epoch();
   const int rb = a.role0 + blockIdx.x;
   if (rb < a.nR) {
-    role_router<HC>(a, rb, smem, epoch);
+    role_router<HC, false>(a, rb, smem, epoch);
   } else if (rb < a.nR + a.nS) {
     const int s = rb - a.nR;
-    role_gate_up<HC, NV>(a, -1, s, ISC ? ISC : a.Is, smem, epoch, t_start);
+    role_gate_up<HC, NV, false>(a, -1, s, ISC ? ISC : a.Is, smem, epoch, t_start);
     block_publish(a, s, epoch);
   } else if (rb < a.nR + a.nS + a.nG) {
     const int gb = rb - a.nR - a.nS;
-    role_gate_up<HC, NV>(a, gb / a.perG, gb % a.perG, IC ? IC : a.I, smem, epoch, t_start);
+    role_gate_up<HC, NV, false>(a, gb / a.perG, gb % a.perG, IC ? IC : a.I, smem, epoch, t_start);
     block_publish(a, a.nS + gb, epoch);
   } else {
-    role_down<IC, ISC, NV>(a, rb - a.nR - a.nS - a.nG, smem, epoch, t_start);
+    uint32_t held = 0;
+    role_down<IC, ISC, NV, false>(a, rb - a.nR - a.nS - a.nG, smem, epoch, t_start, held, nullptr);
   }
+}
+
+// ============================================================ layer stack
+// One decode token through L layers in one launch (a cooperative launch:
+// every block is resident, which the waits on later blocks need).  Each
+// block keeps its role for all layers, so its code stays in the
+// instruction cache, and before waiting for a layer's input it issues the
+// loads that do not depend on it (router and shared-expert weights; the
+// output blocks' shared-down weights).  Layer l's input is the caller's x
+// (l = 0) or the previous layer's output, ping-ponged through two buffers
+// of the workspace; the router, shared and routed gate/up blocks wait for
+// every output block of the previous layer, which also guarantees that
+// nothing still reads the buffers, activations or tags they overwrite.
+// The last layer's output goes to `out`; the last output block to finish
+// (a counter) clears every flag and tag, so the next call starts from zero.
+// Layer l's arguments: the table's pointers, the layer's input and output
+// buffers, the tags.
+__device__ __forceinline__ void stack_layer_args(DecodeArgs& a, const DecodeArgs& a0,
+                                                 const StackLayerDev* tab, int l, int L,
+                                                 uint16_t* xb, int H) {
+  a = a0;
+  const StackLayerDev& T = tab[l];
+  a.router = T.router; a.gate = T.gate; a.up = T.up; a.down = T.down;
+  a.shg = T.shg; a.shu = T.shu; a.shd = T.shd;
+  a.gamma = T.gamma; a.lbias = T.lbias;
+  a.x = l ? xb + (size_t)((l - 1) & 1) * H : a0.x;
+  a.out = l == L - 1 ? a0.out : xb + (size_t)(l & 1) * H;
+  a.residual = l ? nullptr : a0.x;
+  a.idx_out = a0.idx_out ? a0.idx_out + (size_t)l * a0.K : nullptr;
+  a.w_out = a0.w_out ? a0.w_out + (size_t)l * a0.K : nullptr;
+  a.dwait = l ? a0.nD : 0;
+  a.dtag = stack_tag(l - 1);
+}
+
+template <int HC, int IC, int ISC, int EC>
+__global__ __launch_bounds__(kBlock, 4) void k_moe_stack(DecodeArgs a0, const StackLayerDev* tab,
+                                                      int L, uint16_t* xb, uint16_t* lout) {
+  constexpr int NV = EC ? cdiv(EC, 64) : QMOE_MAX_EXPERTS / 64;
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint32_t* sys = reinterpret_cast<uint32_t*>(smem);
+  const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
+  const int rb = blockIdx.x;
+  const int H = HC ? HC : a0.H;
+  const int nRSG = a0.nR + a0.nS + a0.nG;
+  if (threadIdx.x == 0) *reinterpret_cast<uint64_t*>(sys + kSysWait) = 0;
+  DecodeArgs a;
+  // every role runs its own loop over the layers
+  if (rb < a0.nR) {
+    for (int l = 0; l < L; ++l) {
+      stack_layer_args(a, a0, tab, l, L, xb, H);
+      __syncthreads();  // the previous layer's LDS contents are consumed
+      int b = rb;
+      opaque_s(b);
+      if (!role_router<HC, true>(a, b, smem, stack_tag(l))) return;
+    }
+    return;
+  }
+  if (rb < a0.nR + a0.nS) {
+    const int sb = rb - a0.nR;
+    for (int l = 0; l < L; ++l) {
+      stack_layer_args(a, a0, tab, l, L, xb, H);
+      __syncthreads();
+      int b = sb;
+      opaque_s(b);
+      if (!role_gate_up<HC, NV, true>(a, -1, b, ISC ? ISC : a.Is, smem, stack_tag(l), t_start))
+        return;
+      block_publish(a, sb, stack_tag(l), opaque_tid());
+    }
+    return;
+  }
+  if (rb < nRSG) {
+    const int gb = rb - a0.nR - a0.nS;
+    for (int l = 0; l < L; ++l) {
+      stack_layer_args(a, a0, tab, l, L, xb, H);
+      __syncthreads();
+      int b = gb;
+      opaque_s(b);
+      if (!role_gate_up<HC, NV, true>(a, b / a.perG, b % a.perG, IC ? IC : a.I, smem,
+                                      stack_tag(l), t_start))
+        return;
+      block_publish(a, a.nS + gb, stack_tag(l), opaque_tid());
+    }
+    return;
+  }
+  const int d = rb - nRSG;
+  uint32_t held = 0;
+  for (int l = 0; l < L; ++l) {
+    stack_layer_args(a, a0, tab, l, L, xb, H);
+    __syncthreads();
+    int b = d;
+    opaque_s(b);
+    if (!role_down<IC, ISC, NV, true>(a, b, smem, stack_tag(l), t_start, held,
+                                      lout ? lout + (size_t)l * H : nullptr))
+      return;
+    // the last layer's outputs have no reader inside the launch
+    if (l < L - 1) block_publish(a, a.nS + a.nG + d, stack_tag(l), opaque_tid());
+  }
+  // output blocks: count the finished ones; the last clears the control area
+  wait_vm();
+  __syncthreads();
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(a0.ws + a0.wl.ctl + ctl::kCntBase +
+                                              64 * ctl::kCntStack);
+  if (threadIdx.x == 0) {
+    const uint32_t prev = add_dev(cnt, 1u);
+    sys[kSysOk] = prev == (uint32_t)a0.nD - 1;
+  }
+  __syncthreads();
+  if (!sys[kSysOk]) return;
+  const int nflag = a0.nS + a0.nG + a0.nD;
+  for (int r = 0; r < ctl::kRep; ++r) {
+    uint64_t* tg = reinterpret_cast<uint64_t*>(rep_of(a0, ctl::kTagBase, r));
+    uint32_t* fl = reinterpret_cast<uint32_t*>(rep_of(a0, ctl::kFlagBase, r));
+    for (int i = threadIdx.x; i < a0.E; i += kBlock) st_dev(tg + i, (uint64_t)0);
+    for (int i = threadIdx.x; i < nflag; i += kBlock) st_dev(fl + i, 0u);
+  }
+  if (threadIdx.x == 0) st_dev(cnt, 0u);
 }
 
 // ======================================================== host launchers
@@ -1171,12 +1501,21 @@ qmoe_status launch_router(const qmoe_qtensor& Wr, const float* lbias, const uint
   return hipGetLastError() == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
 }
 
+// Dynamic LDS of the step and stack kernels: the largest role.
+static size_t step_lds(int H, int E, int I, int Is, int K) {
+  (void)E;
+  size_t lds = gu_lds(H);
+  if (router_lds(H) > lds) lds = router_lds(H);
+  if (down_lds(I, Is, K) > lds) lds = down_lds(I, Is, K);
+  return lds;
+}
+
 bool moe_step_supported(const qmoe_moe_layer& L) {
   const int nR = cdiv(L.n_experts, kRowsPerUnit);
   const int perG = L.inter / kGuRows;
   const int nS = L.shared_inter / kGuRows;
   return L.hidden / 8 <= kMaxXW * kBlock && nR <= 64 &&
-         down_lds(L.inter, L.shared_inter, L.top_k) <= 65536 &&
+         step_lds(L.hidden, L.n_experts, L.inter, L.shared_inter, L.top_k) <= 65536 &&
          L.n_experts * 8 <= ctl::kRepStride && nS + L.top_k * perG <= ctl::kMaxFlags;
 }
 
@@ -1236,9 +1575,7 @@ qmoe_status launch_moe_step(const qmoe_moe_layer& L, const uint16_t* x, const in
   a.perG = a.I / kGuRows;
   a.nG = a.K * a.perG;
   a.nD = a.H / kRowsPerUnit;
-  size_t lds = gu_lds(a.H);
-  if (router_lds(a.H) > lds) lds = router_lds(a.H);
-  if (down_lds(a.I, a.Is, a.K) > lds) lds = down_lds(a.I, a.Is, a.K);
+  const size_t lds = step_lds(a.H, a.E, a.I, a.Is, a.K);
   a.nowait = phased;
   a.s_done = 0;
   if (mode == kStepShared || mode == kStepRouted) {
@@ -1269,6 +1606,51 @@ qmoe_status launch_moe_step(const qmoe_moe_layer& L, const uint16_t* x, const in
   a.role0 = a.nR + a.nS + a.nG;
   launch_step(a, a.nD, lds, stream, nullptr, e1);
   return hipGetLastError() == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
+}
+
+template <int HC, int IC, int ISC, int EC>
+static hipError_t launch_stack_kernel(DecodeArgs a, const StackLayerDev* tab, int L,
+                                      uint16_t* xb, uint16_t* lout, int blocks, size_t lds,
+                                      void* stream) {
+  void* args[] = {&a, &tab, &L, &xb, &lout};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_moe_stack<HC, IC, ISC, EC>),
+                                    dim3(blocks), dim3(kBlock), args, (unsigned)lds, S(stream));
+}
+
+// n_layers layers of shape L (weights from the device table) for one token.
+// xb: two bf16 [H] buffers inside the workspace.
+qmoe_status launch_moe_stack(const qmoe_moe_layer& L, const void* table, int n_layers,
+                             const uint16_t* x, uint16_t* out, uint16_t* lout, int32_t* idx_out,
+                             float* w_out, uint8_t* ws, uint16_t* xb, void* stream) {
+  if (!moe_step_supported(L)) return QMOE_ERR_UNSUPPORTED;
+  DecodeArgs a;
+  memset(&a, 0, sizeof(a));
+  a.H = L.hidden; a.E = L.n_experts; a.K = L.top_k; a.I = L.inter; a.Is = L.shared_inter;
+  a.eps = L.rms_eps;
+  a.x = x; a.out = out; a.idx_out = idx_out; a.w_out = w_out;
+  a.ws = ws;
+  a.wl = ws_layout(a.E, a.K, a.I, a.Is, 1);
+  a.nR = cdiv(a.E, kRowsPerUnit);
+  a.nS = a.Is / kGuRows;
+  a.perG = a.I / kGuRows;
+  a.nG = a.K * a.perG;
+  a.nD = a.H / kRowsPerUnit;
+  if (a.nS + a.nG + a.nD > ctl::kMaxFlags) return QMOE_ERR_UNSUPPORTED;
+  const size_t lds = step_lds(a.H, a.E, a.I, a.Is, a.K);
+  const int blocks = a.nR + a.nS + a.nG + a.nD;
+  const StackLayerDev* tab = static_cast<const StackLayerDev*>(table);
+  hipError_t e;
+  if (a.H == 2816 && a.I == 704 && a.Is == 2112 && a.E == 128)
+    e = launch_stack_kernel<2816, 704, 2112, 128>(a, tab, n_layers, xb, lout, blocks, lds, stream);
+  else if (a.H == 512 && a.I == 256 && a.Is == 512 && a.E == 32)
+    e = launch_stack_kernel<512, 256, 512, 32>(a, tab, n_layers, xb, lout, blocks, lds, stream);
+  else
+    e = launch_stack_kernel<0, 0, 0, 0>(a, tab, n_layers, xb, lout, blocks, lds, stream);
+  if (e == hipErrorCooperativeLaunchTooLarge) {
+    (void)hipGetLastError();
+    return QMOE_ERR_UNSUPPORTED;
+  }
+  return e == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
 }
 
 }  // namespace qmoe

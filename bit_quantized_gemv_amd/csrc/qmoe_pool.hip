@@ -206,8 +206,8 @@ void qmoe_pool_destroy(qmoe_pool* p) {
   if (!p) return;
   for (auto& S : p->L)
     for (int i = 0; i < 2; ++i) {
-      if (S.map_done[i]) hipEventDestroy(S.map_done[i]);
-      if (S.map_host[i]) hipHostFree(S.map_host[i]);
+      if (S.map_done[i]) (void)hipEventDestroy(S.map_done[i]);
+      if (S.map_host[i]) (void)hipHostFree(S.map_host[i]);
     }
   delete p;
 }

@@ -102,6 +102,7 @@ typedef struct {
 #define QMOE_MAX_EXPERTS 512
 #define QMOE_MAX_HIDDEN 16384
 #define QMOE_MAX_TOKENS 128
+#define QMOE_MAX_LAYERS 128
 
 /* y[r] = sum_c W[r][c] x[c] for a 4-bit affine matrix (the quantized GEMV).
  * W: bits=4, group=64, expert_stride_bytes ignored.  x: bf16 [cols].
@@ -203,11 +204,58 @@ size_t qmoe_router_workspace_bytes(int32_t n_experts, int32_t T);
 /* Reads (synchronising `stream`) and clears the device error word of a
  * workspace.  *device_code receives 0 when every in-kernel wait completed,
  * nonzero when one gave up (the outputs of that call are then undefined).
+ * In that case the whole control area (flags, tags, counters) is zeroed as
+ * well, so the workspace is ready again.
  * Returns QMOE_OK, QMOE_ERR_DEVICE when the word was nonzero, or an error. */
 qmoe_status qmoe_workspace_status(void* ws, size_t ws_bytes, int32_t* device_code,
                                   void* stream);
 
 const char* qmoe_status_string(qmoe_status s);
+
+/* ---------------------------------------------------------------------
+ * Decode through a stack of layers in one launch (remio.ai "TurboFieldfare
+ * esegue Mac Gemma 4 26B in 2 GB…", section "L'affermazione dei 2 GB
+ * trasforma la larghezza di banda dell'SSD nel nuovo vincolo": the step
+ * repeats in each of the model's 30 layers for every generated token).
+ * Layer l maps x_l to x_{l+1} exactly as qmoe_moe_decode with residual = 1
+ * (RMSNorm with the layer's rms_gamma, router top-k, shared and routed
+ * FFN, combine, residual add, one bf16 rounding); the results are bitwise
+ * those of n_layers ordered qmoe_moe_decode calls.  Weights are resident
+ * (no expert -> slot map).
+ * ------------------------------------------------------------------- */
+
+/* Bytes of the device layer table for n_layers layers (0 when n_layers is
+ * outside [1, QMOE_MAX_LAYERS]). */
+size_t qmoe_stack_table_bytes(int32_t n_layers);
+
+/* Writes the device form of layers[0..n_layers) (host array) into `table`
+ * (device memory, caller-owned, 16-byte aligned, table_bytes >=
+ * qmoe_stack_table_bytes(n_layers)).  Every layer must be valid and have the
+ * sizes and rms_eps of layers[0].  Set-up, not the hot path: the copy is
+ * enqueued on `stream` and the call waits for it.  The table holds the
+ * layers' device pointers, so it stays valid while their weights do. */
+qmoe_status qmoe_stack_table_init(const qmoe_moe_layer* layers, int32_t n_layers,
+                                  void* table, size_t table_bytes, void* stream);
+
+/* Workspace of qmoe_stack_decode for layers of this shape (0 if invalid):
+ * the one-layer workspace plus two bf16 [hidden] buffers for the layer
+ * inputs. */
+size_t qmoe_stack_workspace_bytes(const qmoe_moe_layer* shape);
+
+/* x_0 = x; x_{l+1} = layer l applied to x_l; out = x_{n_layers}.
+ * shape: any layer of the stack (sizes, rms_eps; its pointers are not
+ * used).  table: from qmoe_stack_table_init with at least n_layers layers
+ * of that shape (not checked: the table is device memory).
+ * x, out: bf16 [H], 16-byte aligned (out must not alias x).
+ * layer_out: bf16 [n_layers][H] or NULL; receives every x_{l+1}.
+ * idx_out/w_out: int32/fp32 [n_layers][top_k] or NULL; every layer's routing.
+ * One cooperative launch: QMOE_ERR_UNSUPPORTED when the device cannot hold
+ * all of its blocks at once.  Waits inside the launch are bounded as in
+ * qmoe_moe_decode (see qmoe_workspace_status). */
+qmoe_status qmoe_stack_decode(const qmoe_moe_layer* shape, const void* table,
+                              int32_t n_layers, const uint16_t* x, uint16_t* out,
+                              uint16_t* layer_out, int32_t* idx_out, float* w_out,
+                              void* ws, size_t ws_bytes, void* stream);
 
 /* ---------------------------------------------------------------------
  * Split FFN: the shared expert's gate/up first, the rest after the routed

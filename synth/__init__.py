@@ -77,6 +77,12 @@ WORKLOADS: Dict[str, Workload] = {
     # small-shape version of the streaming stack, for parity tests
     "tiny_streaming_decode": Workload(6, "tiny_streaming_decode", 512, 32, 8, 256, 512,
                                       layers=3, tokens=12, rmsnorm=True, zipf=True, slots=16),
+    # small stacks for parity tests of the one-launch stack decode: the
+    # small shapes, and shapes with no compile-time specialisation
+    "tiny_stack_decode": Workload(7, "tiny_stack_decode", 512, 32, 8, 256, 512,
+                                  layers=5, tokens=3, rmsnorm=True),
+    "odd_stack_decode": Workload(8, "odd_stack_decode", 1024, 64, 4, 128, 256,
+                                 layers=4, tokens=2, rmsnorm=True),
 }
 
 

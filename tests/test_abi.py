@@ -81,3 +81,40 @@ def test_layer_validation_and_workspace_size():
     assert lib.qmoe_workspace_bytes(C.byref(bad), 1) == 0
     assert lib.qmoe_moe_decode(C.byref(bad), 0x3000, None, 0, 0x6000, None, None, 0x7000, 1 << 24,
                                None) == 3   # top_k above the kernels' limit of 8
+
+
+def test_stack_sizes_and_validation_before_launch():
+    """The stack entry points size their buffers and reject bad arguments on
+    the host, before any HIP call (no GPU needed)."""
+    import bit_quantized_gemv_amd as q
+
+    lib = q.lib()
+    assert lib.qmoe_stack_table_bytes(0) == 0
+    assert lib.qmoe_stack_table_bytes(129) == 0
+    one = lib.qmoe_stack_table_bytes(1)
+    assert one > 0 and lib.qmoe_stack_table_bytes(30) == 30 * one
+    L = _layer(q)
+    wsn = lib.qmoe_stack_workspace_bytes(C.byref(L))
+    # the one-layer workspace plus two bf16 [H] input buffers
+    assert wsn >= lib.qmoe_workspace_bytes(C.byref(L), 1) + 2 * 512 * 2
+    bad = _layer(q, K=9)
+    assert lib.qmoe_stack_workspace_bytes(C.byref(bad)) == 0
+    tab, x, out, ws = 0x10000, 0x20000, 0x30000, 0x40000
+
+    def dec(layer=L, table=tab, n=3, xx=x, oo=out, nbytes=wsn):
+        return lib.qmoe_stack_decode(C.byref(layer), table, n, xx, oo, None, None, None, ws,
+                                     nbytes, None)
+
+    assert dec(table=None) == 1
+    assert dec(n=0) == 2 and dec(n=129) == 2
+    assert dec(oo=x) == 2                    # output may not alias the input
+    assert dec(xx=x + 2) == 5                # alignment
+    assert dec(nbytes=wsn - 1) == 4
+    assert dec(layer=bad) == 3
+    # table set-up: every layer must have the first one's shape
+    arr = (q._Layer * 2)(_layer(q), _layer(q, I=512))
+    assert lib.qmoe_stack_table_init(arr, 2, tab, 2 * one, None) == 2
+    arr = (q._Layer * 2)(_layer(q), _layer(q))
+    assert lib.qmoe_stack_table_init(arr, 2, tab, 2 * one - 1, None) == 4
+    assert lib.qmoe_stack_table_init(arr, 0, tab, 2 * one, None) == 2
+    assert lib.qmoe_stack_table_init(arr, 2, None, 2 * one, None) == 1

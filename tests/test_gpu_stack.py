@@ -1,6 +1,7 @@
 """GPU parity of the 30-layer decode stack (RMSNorm -> router top-8 ->
 shared + routed FFN -> residual per layer, independent seeded layers)
-against the fp64 oracle: teacher-forced per layer, then free-running."""
+against the fp64 oracle: teacher-forced per layer, then free-running.  The
+one-launch stack decode must reproduce the one-layer launches bit for bit."""
 import numpy as np
 import pytest
 
@@ -28,6 +29,13 @@ def stack():
     return layers
 
 
+@pytest.fixture(scope="module")
+def stack_kernel(stack):
+    import bit_quantized_gemv_amd as q
+
+    return q.Stack([dl.layer for _, _, dl in stack])
+
+
 def _near_tie(lg, a, b):
     gap = max(abs(lg[i] - lg[j]) for i, j in zip(a, b))
     return gap <= 1e-3 * max(1.0, abs(lg).max())
@@ -51,7 +59,19 @@ def _run_gpu(torch, q, layers, x):
     return xs, idxs
 
 
-def test_stack_teacher_forced_and_free_running(stack):
+def _run_stack_kernel(torch, stk, x):
+    """The same token through the one-launch stack decode."""
+    n, H, K = STACK.layers, STACK.hidden, STACK.top_k
+    lo = torch.empty(n, H, dtype=torch.int16, device="cuda")
+    idx = torch.empty(n, K, dtype=torch.int32, device="cuda")
+    w = torch.empty(n, K, dtype=torch.float32, device="cuda")
+    out = torch.empty(H, dtype=torch.int16, device="cuda")
+    stk.decode(torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda(), out, lo, idx, w)
+    torch.cuda.synchronize()
+    return to_u16(lo), idx.cpu().numpy(), w.cpu().numpy(), to_u16(out)
+
+
+def test_stack_teacher_forced_and_free_running(stack, stack_kernel):
     import torch
     from concurrent.futures import ThreadPoolExecutor
 
@@ -62,6 +82,15 @@ def test_stack_teacher_forced_and_free_running(stack):
     for t in range(N_TOKENS):
         log(f"stack token {t}: 30 layers on the device")
         runs.append(_run_gpu(torch, q, stack, X[t]))
+        log(f"stack token {t}: one-launch stack decode")
+        lo, idx, w, out = _run_stack_kernel(torch, stack_kernel, X[t])
+        xs, routing = runs[-1]
+        for l in range(STACK.layers):
+            assert np.array_equal(lo[l], xs[l + 1]), (t, l, "layer output differs")
+            assert np.array_equal(idx[l], routing[l][0]), (t, l)
+            assert np.array_equal(w[l].view(np.uint32), routing[l][1].view(np.uint32)), (t, l)
+        assert np.array_equal(out, xs[-1])
+    assert q.qmoe_workspace_status(stack_kernel.ws) == 0
 
     # teacher-forced: the oracle's layer l on the device's input to layer l
     flips = 0
