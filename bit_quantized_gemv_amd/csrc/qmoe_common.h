@@ -114,18 +114,35 @@ __device__ __forceinline__ float gelu_tanh(float z) {
   return 0.5f * z * (1.0f + tanhf(k0 * fmaf(k1 * z * z, z, z)));
 }
 
+// Loads through these pointers are global-memory loads.  Pointers that the
+// compiler cannot trace to a kernel argument (read from a table in device
+// memory) would otherwise become flat loads, which also count as LDS
+// operations: every wait for an LDS result or barrier would then wait for
+// all weight loads in flight.
+#define QMOE_GLOBAL __attribute__((address_space(1)))
+template <typename T>
+__device__ __forceinline__ const QMOE_GLOBAL T* gptr(const T* p) {
+  return (const QMOE_GLOBAL T*)p;
+}
+
 // Weights are read once per step: non-temporal loads, so that they do not
 // displace the kernel's code and the small exchanged data from the caches.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ldg16(const uint8_t* p) {
-  u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
+  u32x4_t v = __builtin_nontemporal_load(gptr(reinterpret_cast<const u32x4_t*>(p)));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// 16 bytes at p + 16 i through the cache (a global-memory load).
+__device__ __forceinline__ uint4 ld_g16(const void* p, int64_t i) {
+  u32x4_t v = gptr(reinterpret_cast<const u32x4_t*>(p))[i];
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // Packed (scale | bias << 16) fp16 pair at element offset `off`.
 __device__ __forceinline__ uint32_t ld_sb(const uint16_t* s, const uint16_t* b, int64_t off) {
-  return (uint32_t)__builtin_nontemporal_load(s + off) |
-         ((uint32_t)__builtin_nontemporal_load(b + off) << 16);
+  return (uint32_t)__builtin_nontemporal_load(gptr(s + off)) |
+         ((uint32_t)__builtin_nontemporal_load(gptr(b + off)) << 16);
 }
 
 // ----------------------------------------- device-coherent data exchange

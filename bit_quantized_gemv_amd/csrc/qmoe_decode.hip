@@ -60,6 +60,7 @@ constexpr uint64_t kHoldTicks = 0;
 
 // LDS "sys" words at the start of every block's LDS
 constexpr int kSysEpoch = 0, kSysOk = 1, kSysIdx = 8, kSysW = 16, kSysRed = 32;
+constexpr int kSysSlot = 24;  // stacked position of each routed expert
 constexpr int kSysTkIdx = 96, kSysTkW = 160;  // per-wave top-k of the standalone router
 constexpr int kSysXch = 96;    // top-k exchange slots (2k 64-bit words) of the step roles
 constexpr int kSysWait = 184;  // stack kernel: 64-bit length of the last wait for a layer input
@@ -440,16 +441,21 @@ __device__ bool wave_routing(const DecodeArgs& a, uint32_t epoch, int32_t* idx_s
 }
 
 // Routing for a consumer block: from the caller's arrays, or from the
-// router blocks' published logits.  Leaves idx/w in sys LDS.
+// router blocks' published logits.  Leaves idx/w in sys LDS, and each
+// routed expert's stacked position (through the expert -> slot map, if
+// any) in sys[kSysSlot + j], so that no consumer waits on that lookup.
 template <int NV>
 __device__ bool block_routing(const DecodeArgs& a, uint32_t epoch, uint32_t* sys, bool write_out,
                               int tid = threadIdx.x) {
   int32_t* idx_s = reinterpret_cast<int32_t*>(sys + kSysIdx);
   float* w_s = reinterpret_cast<float*>(sys + kSysW);
+  int32_t* slot_s = reinterpret_cast<int32_t*>(sys + kSysSlot);
   if (a.idx_in) {
     if (tid < a.K) {
-      idx_s[tid] = a.idx_in[tid];
-      w_s[tid] = a.w_in[tid];
+      const int e = gptr(a.idx_in)[tid];
+      idx_s[tid] = e;
+      w_s[tid] = gptr(a.w_in)[tid];
+      slot_s[tid] = a.slot ? gptr(a.slot)[e] : e;
     }
     __syncthreads();
     return true;
@@ -457,6 +463,10 @@ __device__ bool block_routing(const DecodeArgs& a, uint32_t epoch, uint32_t* sys
   if (tid < 64) {
     bool ok = wave_routing<NV>(a, epoch, idx_s, w_s, write_out,
                                reinterpret_cast<uint64_t*>(sys + kSysXch), tid);
+    if (ok && tid < a.K) {
+      const int e = idx_s[tid];
+      slot_s[tid] = a.slot ? gptr(a.slot)[e] : e;
+    }
     if (tid == 0) sys[kSysOk] = ok ? 1u : 0u;
   }
   __syncthreads();
@@ -470,7 +480,7 @@ __device__ bool block_routing(const DecodeArgs& a, uint32_t epoch, uint32_t* sys
 // bf16(x * inv * gamma).
 __device__ __forceinline__ uint4 norm_word(uint4 r, const uint16_t* gamma, float inv, int v) {
   if (!gamma) return r;
-  uint4 g = reinterpret_cast<const uint4*>(gamma)[v];
+  uint4 g = ld_g16(gamma, v);
   uint32_t xr[4] = {r.x, r.y, r.z, r.w}, gr[4] = {g.x, g.y, g.z, g.w}, o[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -487,10 +497,9 @@ struct XRegs {
   uint4 w[kMaxXW];
 };
 __device__ __forceinline__ void x_load(XRegs& X, const uint16_t* x, int H, int tid = threadIdx.x) {
-  const uint4* x4 = reinterpret_cast<const uint4*>(x);
   const int Wn = H / 8;
 #pragma unroll
-  for (int i = 0; i < kMaxXW; ++i) X.w[i] = x4[min(tid + i * kBlock, Wn - 1)];
+  for (int i = 0; i < kMaxXW; ++i) X.w[i] = ld_g16(x, min(tid + i * kBlock, Wn - 1));
 }
 
 // The same words read device-coherently: the layer input of a stack layer
@@ -508,7 +517,6 @@ __device__ __forceinline__ void x_load_dev(XRegs& X, const uint16_t* x, int H, i
 __device__ float x_inv_rms(const XRegs& X, const uint16_t* x, int H, float eps, float* red, int tid = threadIdx.x) {
   float ss = 0.f;
   const int Wn = H / 8;
-  const uint4* x4 = reinterpret_cast<const uint4*>(x);
   for (int i = 0; i * kBlock < Wn; ++i) {
     int v = tid + i * kBlock;
     if (v >= Wn) break;
@@ -519,7 +527,7 @@ __device__ float x_inv_rms(const XRegs& X, const uint16_t* x, int H, float eps, 
       for (int k = 1; k < kMaxXW; ++k)
         if (i == k) w = X.w[k];
     } else {
-      w = x4[v];
+      w = ld_g16(x, v);
     }
     uint32_t r[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
@@ -576,7 +584,6 @@ template <bool PAIRS>
 __device__ void x_stage(const XRegs& X, const uint16_t* x, const uint16_t* gamma, float inv, int H,
                         void* dst, float* xh, int tid = threadIdx.x) {
   const int Wn = H / 8;
-  const uint4* x4 = reinterpret_cast<const uint4*>(x);
 #pragma unroll
   for (int i = 0; i < kMaxXW; ++i) {
     if (i * kBlock < Wn) {
@@ -592,7 +599,7 @@ __device__ void x_stage(const XRegs& X, const uint16_t* x, const uint16_t* gamma
   for (int i = kMaxXW; i * kBlock < Wn; ++i) {
     int v = tid + i * kBlock;
     bool ok = v < Wn;
-    uint4 r = ok ? norm_word(x4[v], gamma, inv, v) : make_uint4(0, 0, 0, 0);
+    uint4 r = ok ? norm_word(ld_g16(x, v), gamma, inv, v) : make_uint4(0, 0, 0, 0);
     if (PAIRS)
       put_pairs(r, v, ok, H / 32, reinterpret_cast<uint4*>(dst), xh);
     else
@@ -624,8 +631,8 @@ __device__ __forceinline__ void rows4_load_sb(Rows4<NM, SP>& R, const DevQ (&m)[
   const int64_t u = min(first + min(lane, G - 1), total - 1);
 #pragma unroll
   for (int k = 0; k < NM; ++k) {
-    R.sv[k] = reinterpret_cast<const uint4*>(m[k].s)[u];
-    R.bv[k] = reinterpret_cast<const uint4*>(m[k].b)[u];
+    R.sv[k] = ld_g16(m[k].s, u);
+    R.bv[k] = ld_g16(m[k].b, u);
   }
 }
 
@@ -657,8 +664,8 @@ __device__ __forceinline__ void rows4_put_sb(const Rows4<NM, SP>& R, const DevQ 
     if (fast) {
       if (lane < G) put_sb8(R.sv[k], R.bv[k], t + 8 * lane);
     } else {
-      const uint16_t* s = m[k].s + (int64_t)row0 * G;
-      const uint16_t* b = m[k].b + (int64_t)row0 * G;
+      const QMOE_GLOBAL uint16_t* s = gptr(m[k].s + (int64_t)row0 * G);
+      const QMOE_GLOBAL uint16_t* b = gptr(m[k].b + (int64_t)row0 * G);
       for (int h = lane; h < nr * G; h += 64) t[h] = (uint32_t)s[h] | ((uint32_t)b[h] << 16);
     }
   }
@@ -983,7 +990,7 @@ __device__ bool role_router(const DecodeArgs& a, int b, uint8_t* smem, uint32_t 
   }
   if (tid < 8) {
     int e = min(row0 + tid, a.E - 1);
-    if (a.lbias) s += a.lbias[e];
+    if (a.lbias) s += gptr(a.lbias)[e];
     reinterpret_cast<float*>(sys + kSysLg)[tid] = s;
   }
   __syncthreads();
@@ -1062,8 +1069,7 @@ __device__ bool role_gate_up(const DecodeArgs& a, int expert_rank, int rb, int r
     x_stage<true>(X, a.x, a.gamma, inv, H, xs, xh, tid);
     __syncthreads();
     if (!block_routing<NV>(a, epoch, sys, false, tid)) return false;
-    int e = reinterpret_cast<int32_t*>(sys + kSysIdx)[expert_rank];
-    int s = a.slot ? a.slot[e] : e;
+    const int s = reinterpret_cast<int32_t*>(sys + kSysSlot)[expert_rank];
     m[0] = devq_at(mi ? a.up : a.gate, s);
     m[1] = rows_below(m[0], H);
     dst = (size_t)a.Is + (size_t)expert_rank * a.I;
@@ -1252,12 +1258,11 @@ __device__ bool role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
   if (kOnePass && !routed) dtask_load(T, a.shd, row0, CHs, min(t - nrt, CHs - 1));
   // 2. routing, then at once the routed-down weights
   if (!block_routing<NV>(a, epoch, sys, b == 0, t)) return false;
-  const int32_t* idx_s = reinterpret_cast<const int32_t*>(sys + kSysIdx);
+  const int32_t* slot_s = reinterpret_cast<const int32_t*>(sys + kSysSlot);
   const float* w_s = reinterpret_cast<const float*>(sys + kSysW);
   if (kOnePass && routed) {
     const int k = t / CHk, c = t - k * CHk;
-    const int e = idx_s[k];
-    dtask_load(T, devq_at(a.down, a.slot ? a.slot[e] : e), row0, CHk, c);
+    dtask_load(T, devq_at(a.down, slot_s[k]), row0, CHk, c);
   }
   // 3. shared activations once the S blocks are published, shared part
   if (!a.nowait && !a.s_done &&
@@ -1289,9 +1294,8 @@ __device__ bool role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
   } else {
     for (int u = t; u < nrt; u += kBlock) {
       const int k = u / CHk, c = u - k * CHk;
-      const int e = idx_s[k];
       DTask U;
-      dtask_load(U, devq_at(a.down, a.slot ? a.slot[e] : e), row0, CHk, c);
+      dtask_load(U, devq_at(a.down, slot_s[k]), row0, CHk, c);
       dtask_acc(U, ask + (size_t)k * I / 4, ahk + k * CHk, CHk, c, w_s[k], acc);
     }
   }
@@ -1301,7 +1305,7 @@ __device__ bool role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
     uint32_t o = 0;
     if (t < kRowsPerUnit) {
       const int rr = row0 + t;
-      s += bf16_to_f32(a.residual ? (uint32_t)a.residual[rr] : held);
+      s += bf16_to_f32(a.residual ? (uint32_t)gptr(a.residual)[rr] : held);
       o = f32_to_bf16(s);
       held = o;
       if (lout) lout[rr] = (uint16_t)o;
@@ -1313,7 +1317,7 @@ __device__ bool role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
   } else {
     if (threadIdx.x < kRowsPerUnit) {
       const int rr = row0 + threadIdx.x;
-      if (a.residual) s += bf16_to_f32(a.residual[rr]);
+      if (a.residual) s += bf16_to_f32(gptr(a.residual)[rr]);
       a.out[rr] = f32_to_bf16(s);
     }
   }
@@ -1377,8 +1381,11 @@ __device__ __forceinline__ void stack_layer_args(DecodeArgs& a, const DecodeArgs
 }
 
 template <int HC, int IC, int ISC, int EC>
-__global__ __launch_bounds__(kBlock, 4) void k_moe_stack(DecodeArgs a0, const StackLayerDev* tab,
-                                                      int L, uint16_t* xb, uint16_t* lout) {
+// (the table is read-only for the whole launch: __restrict__ lets its
+// fields be read with scalar loads through the constant cache)
+__global__ __launch_bounds__(kBlock, 4) void k_moe_stack(DecodeArgs a0,
+                                                         const StackLayerDev* __restrict__ tab,
+                                                         int L, uint16_t* xb, uint16_t* lout) {
   constexpr int NV = EC ? cdiv(EC, 64) : QMOE_MAX_EXPERTS / 64;
   extern __shared__ __align__(16) uint8_t smem[];
   uint32_t* sys = reinterpret_cast<uint32_t*>(smem);
