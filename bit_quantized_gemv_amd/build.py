@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqmoe.so")
-SOURCES = ["qmoe_api.hip", "qmoe_decode.hip", "qmoe_prefill.hip", "qmoe_pool.hip"]
+SOURCES = ["qmoe_api.hip", "qmoe_decode.hip", "qmoe_router.hip", "qmoe_prefill.hip", "qmoe_pool.hip"]
 ARCH = "gfx950"
 
 

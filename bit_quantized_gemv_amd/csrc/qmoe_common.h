@@ -26,6 +26,8 @@ constexpr int kWavesPerBlock = kBlock / kWave;
 constexpr int kRowsPerUnit = 8;      // rows of one row-block (lane & 7)
 constexpr int kSlots = 8;            // chunk slots per step (lane >> 3)
 
+__host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 

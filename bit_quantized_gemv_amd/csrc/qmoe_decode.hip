@@ -46,6 +46,7 @@
 #include <string.h>
 
 #include "qmoe_common.h"
+#include "qmoe_topk.h"
 
 namespace qmoe {
 
@@ -66,7 +67,6 @@ constexpr int kSysXch = 96;    // top-k exchange slots (2k 64-bit words) of the 
 constexpr int kSysWait = 184;  // stack kernel: 64-bit length of the last wait for a layer input
 constexpr int kSysBytes = 768;
 
-__host__ __device__ constexpr int cdiv(int a, int b) { return (a + b - 1) / b; }
 __host__ __device__ inline size_t al16(size_t n) { return (n + 15) & ~(size_t)15; }
 
 // ----------------------------------------------------------- arguments
@@ -227,24 +227,6 @@ struct NoPre {
 };
 
 // ------------------------------------------------------------ reductions
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                                                0xF, 0xF, false));
-}
-// Maximum over the wave (every lane gets it).
-__device__ __forceinline__ float wave_max(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = fmaxf(v, dpp_f<0x124>(v));  // row_ror:4
-  v = fmaxf(v, dpp_f<0x128>(v));  // row_ror:8
-  float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-  float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
-  float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-  float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
-  return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
-}
-
 // Block-wide sum of one float per thread (fixed order; same bits everywhere).
 __device__ float block_sum(float v, float* red, int tid = threadIdx.x) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
@@ -258,147 +240,6 @@ __device__ float block_sum(float v, float* red, int tid = threadIdx.x) {
 }
 
 // ============================================================== routing
-// One wave: top-k of E logits held as v[m] = logit[lane + 64 m]
-// (descending; ties to the lower index) and the softmax over the kept
-// logits (exp(l - l_max) normalised by their sum).  Results go to idx_s/w_s
-// (LDS) and, optionally, to idx2/w2.
-template <int NV>
-__device__ void wave_topk_vals(const float (&v)[NV], int E, int K, int32_t* idx_s, float* w_s,
-                               int32_t* idx2, float* w2, int tid = threadIdx.x) {
-  const int lane = tid & 63;
-  uint32_t live = 0;
-#pragma unroll
-  for (int m = 0; m < NV; ++m)
-    if (lane + 64 * m < E) live |= 1u << m;
-  float top = 0.f, sel = 0.f;
-  int sel_i = 0;
-  for (int j = 0; j < K; ++j) {
-    float lm = -INFINITY;
-#pragma unroll
-    for (int m = 0; m < NV; ++m)
-      if ((live >> m) & 1u) lm = fmaxf(lm, v[m]);
-    float mx = wave_max(lm);
-    int e = -1;
-#pragma unroll
-    for (int m = NV - 1; m >= 0; --m) {
-      uint64_t bal = __ballot(((live >> m) & 1u) && v[m] == mx);
-      if (bal) e = 64 * m + (int)__builtin_ctzll(bal);
-    }
-    if ((e & 63) == lane) live &= ~(1u << (e >> 6));
-    if (j == 0) top = mx;
-    if (lane == j) {
-      sel = mx;
-      sel_i = e;
-    }
-  }
-  float p = lane < K ? expf(sel - top) : 0.f;
-  float sum = 0.f;
-  for (int j = 0; j < K; ++j)
-    sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), j));
-  if (lane < K) {
-    float wj = p / sum;
-    idx_s[lane] = sel_i;
-    w_s[lane] = wj;
-    if (idx2) idx2[lane] = sel_i;
-    if (w2) w2[lane] = wj;
-  }
-}
-
-// Top-k of logits in memory (device-coherent reads).
-__device__ void wave_topk(const float* lg, int E, int K, int32_t* idx_s, float* w_s, int32_t* idx2,
-                          float* w2) {
-  const int lane = threadIdx.x & 63;
-  float v[QMOE_MAX_EXPERTS / 64];
-#pragma unroll
-  for (int m = 0; m < QMOE_MAX_EXPERTS / 64; ++m) {
-    int e = lane + 64 * m;
-    v[m] = e < E ? ld_dev(lg + e) : -INFINITY;
-  }
-  wave_topk_vals<QMOE_MAX_EXPERTS / 64>(v, E, K, idx_s, w_s, idx2, w2);
-}
-
-// Order value of a logit: an unsigned integer that increases with the
-// fp32 value (-0 counts as +0), and back.
-__device__ __forceinline__ uint32_t topk_ord(float f) {
-  const uint32_t b = __float_as_uint(f + 0.0f);
-  return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
-}
-__device__ __forceinline__ float topk_value(uint32_t u) {
-  return __uint_as_float((u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
-}
-
-// One wave: the same top-k and softmax as wave_topk_vals (descending
-// logits, equal logits by lower index; p_j = exp(l_j - l_max), w_j = p_j /
-// sum(p) summed in rank order), with a short dependency chain:
-//   1. T = the k-th largest order value, bit by bit from the top: keep a
-//      bit when at least k order values are >= the prefix with it (one
-//      ballot count per value slot and bit);
-//   2. the k selected are the values above T and, in index order, the
-//      first k - #(above T) of those equal to T (ballot prefix counts);
-//   3. they are gathered into k slots of `xch` (LDS, 2k words of 8 bytes)
-//      as (order value, complemented index) keys, and lane j < k ranks
-//      slot j against the k keys;
-//   4. lane j takes rank j for the softmax.
-template <int NV>
-__device__ void wave_topk_radix(const float (&v)[NV], int E, int K, int32_t* idx_s, float* w_s,
-                                int32_t* idx2, float* w2, uint64_t* xch, int tid = threadIdx.x) {
-  const int lane = tid & 63;
-  const uint64_t below = (1ull << lane) - 1ull;
-  uint32_t o[NV];
-#pragma unroll
-  for (int m = 0; m < NV; ++m) o[m] = lane + 64 * m < E ? topk_ord(v[m]) : 0u;  // 0: no expert
-  uint32_t T = 0;
-  for (int b = 31; b >= 0; --b) {
-    const uint32_t c = T | (1u << b);
-    uint32_t n = 0;
-#pragma unroll
-    for (int m = 0; m < NV; ++m) n += (uint32_t)__popcll(__ballot(o[m] >= c));
-    if (n >= (uint32_t)K) T = c;
-  }
-  uint32_t above = 0;
-#pragma unroll
-  for (int m = 0; m < NV; ++m) above += (uint32_t)__popcll(__ballot(o[m] > T));
-  const uint32_t need = (uint32_t)K - above;
-  uint32_t ties = 0, base = 0;
-#pragma unroll
-  for (int m = 0; m < NV; ++m) {
-    const uint64_t tie = __ballot(o[m] == T);
-    const bool take =
-        o[m] > T || (o[m] == T && ties + (uint32_t)__popcll(tie & below) < need);
-    ties += (uint32_t)__popcll(tie);
-    const uint64_t sel = __ballot(take);
-    if (take)
-      xch[base + (uint32_t)__popcll(sel & below)] =
-          ((uint64_t)o[m] << 32) | (uint32_t)~(lane + 64 * m);
-    base += (uint32_t)__popcll(sel);
-  }
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  if (lane < K) {
-    const uint64_t kj = xch[lane];
-    uint32_t r = 0;
-    for (int j = 0; j < K; ++j) r += xch[j] > kj ? 1u : 0u;
-    xch[K + r] = kj;
-  }
-  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-  float p = 0.f;
-  int e = 0;
-  if (lane < K) {
-    const uint64_t kr = xch[K + lane];
-    e = (int)~(uint32_t)kr;
-    p = expf(topk_value((uint32_t)(kr >> 32)) - topk_value((uint32_t)(xch[K] >> 32)));
-  }
-  float sum = 0.f;
-  for (int j = 0; j < K; ++j)
-    sum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, p), j));
-  if (lane < K) {
-    const float wj = p / sum;
-    idx_s[lane] = e;
-    w_s[lane] = wj;
-    if (idx2) idx2[lane] = e;
-    if (w2) w2[lane] = wj;
-  }
-}
-
 // One wave: wait until all E tagged logits of one replica carry `epoch`
 // (each is (epoch << 32) | fp32 bits, written with one 64-bit store), then
 // top-k on them.  Every poll reads all of them.  In a launch that follows
@@ -895,67 +736,6 @@ __device__ float router_token(const DevQ& Wr, int row0, int E, int H_rt, const u
     }
   }
   return router_finish(acc, red, tid);
-}
-
-// Standalone router for T tokens: grid (ceil(E/8), ceil(T/kTokTile)); the
-// last row-block of a token tile (per-tile counter) runs top-k.
-constexpr int kTokTile = 8;
-template <int H8C>
-__global__ __launch_bounds__(kBlock) void k_router(DevQ Wr, const float* lbias, const uint16_t* x,
-                                                   int T, int E, int H, int K, int32_t* idx,
-                                                   float* w, float* logits_out, float* logits_ws,
-                                                   uint32_t* ctlw) {
-  extern __shared__ __align__(16) uint8_t smem[];
-  uint32_t* sys = reinterpret_cast<uint32_t*>(smem);
-  float4* xr = reinterpret_cast<float4*>(smem + kSysBytes);
-  float* xh = reinterpret_cast<float*>(smem + kSysBytes + (size_t)H * 4);
-  float* red = reinterpret_cast<float*>(sys + kSysRed);
-  const int row0 = blockIdx.x * kRowsPerUnit;
-  const int t0 = blockIdx.y * kTokTile, t1 = min(T, t0 + kTokTile);
-  auto put = [&](int t, float s) {
-    if (threadIdx.x < 8 && row0 + (int)threadIdx.x < E) {
-      int e = row0 + threadIdx.x;
-      if (lbias) s += lbias[e];
-      st_dev(logits_ws + (size_t)t * E + e, s);
-      if (logits_out) logits_out[(size_t)t * E + e] = s;
-    }
-  };
-  if (H8C) {
-    // the block's 8 router rows stay in registers for all tokens of the
-    // tile; the next token's activations load while this one is computed
-    constexpr int SR = H8C ? cdiv(cdiv(H8C, kSlots), kWavesPerBlock) : 1;
-    RRegs<SR> R;
-    router_load<SR>(R, Wr, row0, E, H, 0);
-    XRegs X;
-    x_load(X, x + (size_t)t0 * H, H);
-    for (int t = t0; t < t1; ++t) {
-      __syncthreads();  // the previous token's staged values are consumed
-      x_stage<false>(X, x + (size_t)t * H, nullptr, 1.f, H, xr, xh);
-      __syncthreads();
-      if (t + 1 < t1) x_load(X, x + (size_t)(t + 1) * H, H);
-      put(t, router_finish(router_compute<SR>(R, H, 0, xr, xh, 0.f), red));
-    }
-  } else {
-    for (int t = t0; t < t1; ++t)
-      put(t, router_token<H8C>(Wr, row0, E, H, x + (size_t)t * H, nullptr, 0.f, xr, xh, red));
-  }
-  wait_vm();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t* cnt = reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(ctlw) + ctl::kCntBase +
-                                                64 * (ctl::kCntRouterTile + blockIdx.y));
-    uint32_t prev = add_dev(cnt, 1u);
-    sys[kSysOk] = prev == gridDim.x - 1;
-    if (prev == gridDim.x - 1) st_dev(cnt, 0u);
-  }
-  __syncthreads();
-  if (!sys[kSysOk]) return;
-  const int wave = threadIdx.x >> 6;
-  int32_t* idx_s = reinterpret_cast<int32_t*>(sys + kSysTkIdx) + wave * 8;
-  float* w_s = reinterpret_cast<float*>(sys + kSysTkW) + wave * 8;
-  for (int t = t0 + wave; t < t1; t += kWavesPerBlock)
-    wave_topk(logits_ws + (size_t)t * E, E, K, idx_s, w_s, idx + (size_t)t * K,
-              w + (size_t)t * K);
 }
 
 // ========================================================= MoE FFN step
@@ -1491,22 +1271,6 @@ qmoe_status launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, 
   return hipGetLastError() == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
 }
 
-qmoe_status launch_router(const qmoe_qtensor& Wr, const float* lbias, const uint16_t* x, int T,
-                          int K, int32_t* idx, float* w, float* logits, uint8_t* ws,
-                          void* stream) {
-  const int E = Wr.rows, H = Wr.cols;
-  WsLayout wl = ws_layout(E, K, 0, 0, T);
-  dim3 grid(cdiv(E, kRowsPerUnit), cdiv(T, kTokTile));
-  float* lw = reinterpret_cast<float*>(ws + wl.logits);
-  uint32_t* c = reinterpret_cast<uint32_t*>(ws + wl.ctl);
-  if (H == 2816)
-    hipLaunchKernelGGL(k_router<176>, grid, dim3(kBlock), router_lds(H), S(stream), devq(Wr), lbias,
-                       x, T, E, H, K, idx, w, logits, lw, c);
-  else
-    hipLaunchKernelGGL(k_router<0>, grid, dim3(kBlock), router_lds(H), S(stream), devq(Wr), lbias,
-                       x, T, E, H, K, idx, w, logits, lw, c);
-  return hipGetLastError() == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
-}
 
 // Dynamic LDS of the step and stack kernels: the largest role.
 static size_t step_lds(int H, int E, int I, int Is, int K) {
