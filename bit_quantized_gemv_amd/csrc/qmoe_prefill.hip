@@ -31,12 +31,24 @@ typedef float f4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kPfRows = 64;   // weight rows (output features) per block
 constexpr int kPfMaxM = 64;   // A rows (an expert's tokens) per pass of a block
-constexpr int kPfMSub = kPfMaxM / 16;
-constexpr int kPfMChunks = 2; // row chunks of one expert handled by separate blocks
+
+// A operands (the fp16 input and the activations) are stored with rows
+// padded to a multiple of 128 columns, the padding zero, so that every
+// K-step of 128 columns reads whole rows and needs no masking.
+__host__ __device__ constexpr int pad128(int n) { return (n + 127) & ~127; }
 
 struct PfLayout {
-  size_t counts, offsets, perm, pos, xh, act, act_sh, y, y_sh, total;
+  size_t counts, offsets, perm, pos, items, xh, act, act_sh, y, y_sh, total;
 };
+
+// Work items of the GEMMs: chunks of at most kPfMaxM A rows of one expert
+// (or of the shared expert).  An upper bound on their number, from the
+// shapes alone: the shared expert's chunks, plus per expert with rows one
+// partial chunk, plus the full chunks of all pairs.
+__host__ __device__ inline int pf_max_items(int E, int K, int T) {
+  const int n = T * K;
+  return (T + kPfMaxM - 1) / kPfMaxM + (E < n ? E : n) + n / kPfMaxM;
+}
 
 __host__ __device__ inline PfLayout pf_layout(int E, int K, int I, int Is, int H, int T) {
   PfLayout L;
@@ -45,9 +57,10 @@ __host__ __device__ inline PfLayout pf_layout(int E, int K, int I, int Is, int H
   L.offsets = o; o += align256((size_t)(E + 1) * 4);
   L.perm = o; o += align256((size_t)T * K * 4);
   L.pos = o; o += align256((size_t)T * K * 4);
-  L.xh = o; o += align256((size_t)T * H * 2);
-  L.act = o; o += align256((size_t)T * K * I * 2);
-  L.act_sh = o; o += align256((size_t)T * Is * 2);
+  L.items = o; o += align256((size_t)(1 + 3 * pf_max_items(E, K, T)) * 4);
+  L.xh = o; o += align256((size_t)T * pad128(H) * 2);
+  L.act = o; o += align256((size_t)T * K * pad128(I) * 2);
+  L.act_sh = o; o += align256((size_t)T * pad128(Is) * 2);
   L.y = o; o += align256((size_t)T * K * H * 4);
   L.y_sh = o; o += align256((size_t)T * H * 4);
   L.total = o;
@@ -63,11 +76,20 @@ size_t prefill_ws_bytes(const qmoe_moe_layer& L, int T) {
 // rank of p among the pairs of its expert = pairs of the same expert in
 // earlier waves (per-wave counts, prefix over waves) + earlier lanes of its
 // wave with the same expert (ballot match on the bits of the expert id).
-__global__ __launch_bounds__(1024) void k_pf_dispatch(const int32_t* idx, int n, int E,
+//
+// It also writes the GEMMs' work list, items = [n_items, (e, row0, M)...]:
+// first the shared expert's chunks of kPfMaxM token rows (e = -1, row0 =
+// first token), then the experts' chunks of kPfMaxM pair rows (row0 = first
+// sorted pair), experts in order of decreasing row count (ties: lower id
+// first), so that the longest blocks start first.
+__global__ __launch_bounds__(1024) void k_pf_dispatch(const int32_t* idx, int n, int T, int E,
                                                       int32_t* counts, int32_t* offsets,
-                                                      int32_t* perm, int32_t* pos_of) {
+                                                      int32_t* perm, int32_t* pos_of,
+                                                      int32_t* items) {
   __shared__ int32_t cnt[16][QMOE_MAX_EXPERTS];  // per-wave counts, then prefixes
   __shared__ int32_t off[QMOE_MAX_EXPERTS + 1];
+  __shared__ int32_t tot[QMOE_MAX_EXPERTS];      // rows per expert
+  __shared__ int32_t ist[QMOE_MAX_EXPERTS + 1];  // chunks per rank, then first item per rank
   const int p = threadIdx.x, wave = p >> 6, lane = p & 63;
   for (int i = p; i < 16 * QMOE_MAX_EXPERTS; i += 1024) (&cnt[0][0])[i] = 0;
   __syncthreads();
@@ -91,16 +113,36 @@ __global__ __launch_bounds__(1024) void k_pf_dispatch(const int32_t* idx, int n,
       s += c;
     }
     off[x + 1] = s;
+    tot[x] = s;
     counts[x] = s;
   }
   if (p == 0) off[0] = 0;
   __syncthreads();
-  // inclusive scan of off[1..E] (Hillis-Steele over up to 512 entries)
+  // experts by decreasing count: rank of expert x, its chunks at that rank
+  int xr = 0;
+  if (p < E) {
+    const int cx = tot[p];
+    for (int y = 0; y < E; ++y) {
+      const int cy = tot[y];
+      xr += (cy > cx) || (cy == cx && y < p);
+    }
+    ist[xr + 1] = (cx + kPfMaxM - 1) / kPfMaxM;
+  }
+  if (p == 0) ist[0] = 0;
+  __syncthreads();
+  // inclusive scans of off[1..E] and ist[1..E] (Hillis-Steele over up to
+  // 512 entries)
   for (int d = 1; d < E; d <<= 1) {
-    int v = 0;
-    if (p >= d && p < E) v = off[p + 1 - d];
+    int v = 0, u = 0;
+    if (p >= d && p < E) {
+      v = off[p + 1 - d];
+      u = ist[p + 1 - d];
+    }
     __syncthreads();
-    if (p >= d && p < E) off[p + 1] += v;
+    if (p >= d && p < E) {
+      off[p + 1] += v;
+      ist[p + 1] += u;
+    }
     __syncthreads();
   }
   for (int x = p; x <= E; x += 1024) offsets[x] = off[x];
@@ -109,25 +151,51 @@ __global__ __launch_bounds__(1024) void k_pf_dispatch(const int32_t* idx, int n,
     perm[pos] = p;
     pos_of[p] = pos;
   }
+  // the work list
+  const int nsh = (T + kPfMaxM - 1) / kPfMaxM;
+  if (p < nsh) {
+    items[1 + 3 * p] = -1;
+    items[2 + 3 * p] = p * kPfMaxM;
+    items[3 + 3 * p] = min(T - p * kPfMaxM, kPfMaxM);
+  }
+  if (p < E) {
+    const int cx = tot[p];
+    for (int c = 0; c * kPfMaxM < cx; ++c) {
+      const int it = nsh + ist[xr] + c;
+      items[1 + 3 * it] = p;
+      items[2 + 3 * it] = off[p] + c * kPfMaxM;
+      items[3 + 3 * it] = min(cx - c * kPfMaxM, kPfMaxM);
+    }
+  }
+  if (p == 0) items[0] = nsh + ist[E];
 }
 
 // ================================================================== prep
-// X bf16 [T][H] -> fp16, columns of each 8 reordered (0,2,4,6,1,3,5,7).
-__global__ __launch_bounds__(kBlock) void k_pf_prep(const uint16_t* X, int n8, _Float16* xh) {
+// X bf16 [T][H] -> fp16 [T][pad128(H)], columns of each 8 reordered
+// (0,2,4,6,1,3,5,7), the padding zero.  Thread v: 8 columns.
+__global__ __launch_bounds__(kBlock) void k_pf_prep(const uint16_t* X, int T, int H,
+                                                    _Float16* xh) {
+  const int H8 = H / 8, P8 = pad128(H) / 8;
   const int v = blockIdx.x * kBlock + threadIdx.x;
-  if (v >= n8) return;
-  uint4 r = reinterpret_cast<const uint4*>(X)[v];
-  uint32_t w[4] = {r.x, r.y, r.z, r.w};
-  float f[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    f[2 * i] = bf16_to_f32(w[i] & 0xffffu);
-    f[2 * i + 1] = bf16_to_f32(w[i] >> 16);
-  }
+  if (v >= T * P8) return;
+  const int t = v / P8, c8 = v - t * P8;
   h8_t o;
-  const int order[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+  if (c8 < H8) {
+    uint4 r = reinterpret_cast<const uint4*>(X)[t * H8 + c8];
+    uint32_t w[4] = {r.x, r.y, r.z, r.w};
+    float f[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = (_Float16)f[order[i]];
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_to_f32(w[i] & 0xffffu);
+      f[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+    const int order[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (_Float16)f[order[i]];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (_Float16)0.f;
+  }
   reinterpret_cast<h8_t*>(xh)[v] = o;
 }
 
@@ -164,9 +232,10 @@ struct PfArgs {
   const int32_t* counts;
   const int32_t* offsets;
   const int32_t* perm;
-  const _Float16* xh;   // [T][H] prepared input
-  _Float16* act;        // [T*K][I] routed activations (sorted order, prepared layout)
-  _Float16* act_sh;     // [T][Is]
+  const int32_t* items;  // [n_items, (e, row0, M) ...] (the dispatch's work list)
+  const _Float16* xh;   // [T][pad128(H)] prepared input
+  _Float16* act;        // [T*K][pad128(I)] routed activations (sorted order, prepared layout)
+  _Float16* act_sh;     // [T][pad128(Is)]
   float* y;             // [T*K][H] routed outputs (sorted order)
   float* y_sh;          // [T][H]
 };
@@ -180,74 +249,97 @@ struct PfShared {
   int32_t rows[kPfMaxM];  // element offset of each A row from the A base
 };
 
+// Weights of one step: codes, and the group's scale and bias as loaded
+// (combined only where they are used, so that no instruction needs a load
+// right after issuing it).
 template <int NM>
 struct PfW {
   u4v_t q[NM];
-  uint32_t sb[NM];
+  uint32_t s[NM], b[NM];  // fp16 bits, zero-extended
 };
 
-// Weights of step kb (clamped to a valid address past the end).
+// Per-lane weight offsets of one pass: the lane's row n_row of every
+// matrix (all NM have the same shape), codes from 32j on in each step.
+struct PfWOff {
+  uint32_t qrow;  // byte offset of the row's codes
+  uint32_t srow;  // element offset of the row's scales and biases
+  uint32_t j16;   // 16 j: the lane's bytes within a step
+  uint32_t qmax;  // last 16-byte chunk of a row: K/2 - 16
+};
+__device__ __forceinline__ PfWOff pf_woff(int n_row, int K) {
+  PfWOff o;
+  o.qrow = (uint32_t)n_row * (uint32_t)(K / 2);
+  o.srow = (uint32_t)n_row * (uint32_t)(K / 64);
+  o.j16 = 16u * (uint32_t)((threadIdx.x & 63) >> 4);
+  o.qmax = (uint32_t)(K / 2 - 16);
+  return o;
+}
+
+// Weights of step kb.  Past the end of a row a lane re-reads the row's last
+// chunk and its group's scale and bias: finite values whose products meet
+// zero A columns.  The bases are uniform and the offsets 32-bit, so the
+// loads take a scalar base and one vector offset each.
 template <int NM>
-__device__ __forceinline__ void pf_load_w(PfW<NM>& B, const DevQ (&W)[NM], int n_row, int K,
+__device__ __forceinline__ void pf_load_w(PfW<NM>& B, const DevQ (&W)[NM], const PfWOff& o,
                                           int kb) {
-  const int j = (threadIdx.x & 63) >> 4;
-  const int c = min(128 * kb + 32 * j, K - 32);
-  const int G = K / 64;
+  const uint32_t cq = min(64u * (uint32_t)kb + o.j16, o.qmax);
+  const uint32_t qo = o.qrow + cq, so = o.srow + (cq >> 5);
 #pragma unroll
   for (int k = 0; k < NM; ++k) {
     // cached loads: a step reads half of each 128-byte line, the next step
     // the other half
-    B.q[k] = *reinterpret_cast<const u4v_t*>(W[k].q + (int64_t)n_row * (K / 2) + c / 2);
-    B.sb[k] = (uint32_t)W[k].s[(int64_t)n_row * G + c / 64] |
-              ((uint32_t)W[k].b[(int64_t)n_row * G + c / 64] << 16);
+    B.q[k] = *reinterpret_cast<const u4v_t*>(W[k].q + qo);
+    B.s[k] = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(W[k].s) + 2u * so);
+    B.b[k] = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(W[k].b) + 2u * so);
   }
 }
 
 // A rows of step kb: thread (r0 = tid/16, seg = tid%16) loads 16 bytes of
-// rows r0 + 16i, i < NMS.  Rows past Mc re-read row Mc-1 (zeroed at store).
+// rows r0 + 16i, i < NMS.  Rows past Mc re-read row Mc - 1: they only feed
+// output rows that are not stored.
 template <int NMS>
 struct PfA {
   u4v_t v[NMS];
 };
+// Byte offsets (from the A base) of this thread's A rows, read from
+// sh.rows once per pass.
 template <int NMS>
-__device__ __forceinline__ void pf_load_a(PfA<NMS>& A, const _Float16* abase, const PfShared& sh,
-                                          int Mc, int K, int kb) {
-  const int seg = threadIdx.x & 15, r0 = threadIdx.x >> 4;
-  const int col = min(128 * kb + 8 * seg, K - 8);
+__device__ __forceinline__ void pf_rows(uint32_t (&roff)[NMS], const PfShared& sh, int Mc) {
+  const int r0 = threadIdx.x >> 4;
 #pragma unroll
-  for (int i = 0; i < NMS; ++i)
-    A.v[i] = *reinterpret_cast<const u4v_t*>(abase + sh.rows[min(r0 + 16 * i, Mc - 1)] + col);
+  for (int i = 0; i < NMS; ++i) roff[i] = 2u * (uint32_t)sh.rows[min(r0 + 16 * i, Mc - 1)];
 }
 template <int NMS>
-__device__ __forceinline__ void pf_store_a(const PfA<NMS>& A, _Float16* buf, int Mc, int K, int kb) {
-  const int seg = threadIdx.x & 15, r0 = threadIdx.x >> 4;
-  const bool colok = 128 * kb + 8 * seg < K;
+__device__ __forceinline__ void pf_load_a(PfA<NMS>& A, const _Float16* abase,
+                                          const uint32_t (&roff)[NMS], int kb) {
+  const int seg = threadIdx.x & 15;
+  const uint32_t col = 2u * (uint32_t)(128 * kb + 8 * seg);
+  const uint8_t* ab = reinterpret_cast<const uint8_t*>(abase);
 #pragma unroll
-  for (int i = 0; i < NMS; ++i) {
-    const int m = r0 + 16 * i;
-    const u4v_t z = {0u, 0u, 0u, 0u};
-    *reinterpret_cast<u4v_t*>(buf + m * kPfAStride + 8 * seg) = (colok && m < Mc) ? A.v[i] : z;
-  }
+  for (int i = 0; i < NMS; ++i) A.v[i] = *reinterpret_cast<const u4v_t*>(ab + (roff[i] + col));
+}
+template <int NMS>
+__device__ __forceinline__ void pf_store_a(const PfA<NMS>& A, _Float16* buf) {
+  const int seg = threadIdx.x & 15, r0 = threadIdx.x >> 4;
+  _Float16* dst = buf + r0 * kPfAStride + 8 * seg;
+#pragma unroll
+  for (int i = 0; i < NMS; ++i) *reinterpret_cast<u4v_t*>(dst + 16 * i * kPfAStride) = A.v[i];
 }
 
 template <int NM, int NMS>
-__device__ __forceinline__ void pf_mma(const PfW<NM>& B, int K, int kb, const _Float16* buf,
+__device__ __forceinline__ void pf_mma(const PfW<NM>& B, const _Float16* buf,
                                        f4_t (&acc)[NMS][NM]) {
   const int lane = threadIdx.x & 63, m = lane & 15, j = lane >> 4;
-  const bool kok = 128 * kb + 32 * j < K;
   h8_t Bf[NM][4];
 #pragma unroll
   for (int k = 0; k < NM; ++k) {
-    _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)(B.sb[k] & 0xffffu));
-    _Float16 bv = __builtin_bit_cast(_Float16, (uint16_t)(B.sb[k] >> 16));
-    if (!kok) sv = bv = (_Float16)0.f;
+    const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)B.s[k]);
+    const _Float16 bv = __builtin_bit_cast(_Float16, (uint16_t)B.b[k]);
     const h2_t s2 = {sv, sv}, b2 = {bv, bv};
-    const u4v_t z = {0u, 0u, 0u, 0u};
-    const u4v_t q = kok ? B.q[k] : z;
-    Bf[k][0] = dequant_word(q.x, s2, b2);
-    Bf[k][1] = dequant_word(q.y, s2, b2);
-    Bf[k][2] = dequant_word(q.z, s2, b2);
-    Bf[k][3] = dequant_word(q.w, s2, b2);
+    Bf[k][0] = dequant_word(B.q[k].x, s2, b2);
+    Bf[k][1] = dequant_word(B.q[k].y, s2, b2);
+    Bf[k][2] = dequant_word(B.q[k].z, s2, b2);
+    Bf[k][3] = dequant_word(B.q[k].w, s2, b2);
   }
 #pragma unroll
   for (int ms = 0; ms < NMS; ++ms) {
@@ -265,11 +357,18 @@ __device__ __forceinline__ void pf_mma(const PfW<NM>& B, int K, int kb, const _F
   }
 }
 
-// C = A W^T over one pass of Mc <= 64 A rows (sh.rows[0..Mc) set), K
-// columns; acc[ms][k]: lane l holds rows 16ms + 4(l/16) + r, column l%16.
-// Weights run two steps ahead in registers; A rows are loaded two steps
-// ahead into registers (two alternating sets) and stored to the LDS buffer
-// of the next step (two alternating buffers, one barrier per step).
+// C = A W^T over one pass of Mc <= 64 A rows (sh.rows[0..Mc) set: element
+// offsets of rows of pad128(K) columns, the padding zero), K columns;
+// acc[ms][k]: lane l holds rows 16ms + 4(l/16) + r, column l%16.
+// Weights run two steps ahead in registers.  A rows are loaded three steps
+// ahead into registers (two alternating sets) and stored, two steps after
+// their loads were issued, to the LDS buffer of the next step (two
+// alternating buffers, one barrier per step).  Step kb: store A(kb + 1),
+// load A(kb + 3) into the set just freed, MMA on A(kb), load W(kb + 2).
+// The loop body has no conditional loads or stores and no exit in the
+// middle (loads past the last step re-read the last step, and the stores
+// past it go to the buffer no one reads next), so every wait for a load in
+// flight waits for that load only.
 template <int NM, int NMS>
 __device__ __forceinline__ void pf_pass(const DevQ (&W)[NM], int n_row, int K, int Mc,
                                         const _Float16* abase, PfShared& sh,
@@ -279,30 +378,36 @@ __device__ __forceinline__ void pf_pass(const DevQ (&W)[NM], int n_row, int K, i
 #pragma unroll
     for (int k = 0; k < NM; ++k) acc[ms][k] = f4_t{0.f, 0.f, 0.f, 0.f};
   const int nkb = (K + 127) / 128;
+  uint32_t roff[NMS];
+  pf_rows<NMS>(roff, sh, Mc);
+  const PfWOff wo = pf_woff(n_row, K);
   PfW<NM> B0, B1;
   PfA<NMS> Aa, Ab;
-  pf_load_w<NM>(B0, W, n_row, K, 0);
-  pf_load_a<NMS>(Aa, abase, sh, Mc, K, 0);
-  pf_load_w<NM>(B1, W, n_row, K, 1);
-  pf_load_a<NMS>(Ab, abase, sh, Mc, K, min(1, nkb - 1));
-  pf_store_a<NMS>(Aa, sh.a[0], Mc, K, 0);
+  // prologue: A(0) -> LDS buffer 0; Aa = A(1), Ab = A(2) in flight
+  pf_load_a<NMS>(Aa, abase, roff, 0);
+  pf_load_w<NM>(B0, W, wo, 0);
+  pf_store_a<NMS>(Aa, sh.a[0]);
+  pf_load_a<NMS>(Aa, abase, roff, min(1, nkb - 1));
+  pf_load_w<NM>(B1, W, wo, 1);
+  pf_load_a<NMS>(Ab, abase, roff, min(2, nkb - 1));
   __syncthreads();
-  for (int kb = 0; kb < nkb; kb += 2) {
-    // step kb: buffer 0 holds A(kb); Ab holds A(kb + 1)
-    pf_load_a<NMS>(Aa, abase, sh, Mc, K, min(kb + 2, nkb - 1));
-    pf_mma<NM, NMS>(B0, K, kb, sh.a[0], acc);
-    pf_load_w<NM>(B0, W, n_row, K, kb + 2);
-    if (kb + 1 >= nkb) break;
-    pf_store_a<NMS>(Ab, sh.a[1], Mc, K, kb + 1);
+  int kb = 0;
+  for (; kb + 2 <= nkb; kb += 2) {
+    // step kb: buffer 0 holds A(kb); Aa holds A(kb + 1), Ab A(kb + 2)
+    pf_store_a<NMS>(Aa, sh.a[1]);
+    pf_load_a<NMS>(Aa, abase, roff, min(kb + 3, nkb - 1));
+    pf_mma<NM, NMS>(B0, sh.a[0], acc);
+    pf_load_w<NM>(B0, W, wo, kb + 2);
     __syncthreads();
-    // step kb + 1: buffer 1 holds A(kb + 1); Aa holds A(kb + 2)
-    pf_load_a<NMS>(Ab, abase, sh, Mc, K, min(kb + 3, nkb - 1));
-    pf_mma<NM, NMS>(B1, K, kb + 1, sh.a[1], acc);
-    pf_load_w<NM>(B1, W, n_row, K, kb + 3);
-    if (kb + 2 >= nkb) break;
-    pf_store_a<NMS>(Aa, sh.a[0], Mc, K, kb + 2);
+    // step kb + 1: buffer 1 holds A(kb + 1); Ab holds A(kb + 2), Aa A(kb + 3)
+    pf_store_a<NMS>(Ab, sh.a[0]);
+    pf_load_a<NMS>(Ab, abase, roff, min(kb + 4, nkb - 1));
+    pf_mma<NM, NMS>(B1, sh.a[1], acc);
+    pf_load_w<NM>(B1, W, wo, kb + 3);
     __syncthreads();
   }
+  // odd number of steps: the last one (buffer 0 holds it, B0 its weights)
+  if (kb < nkb) pf_mma<NM, NMS>(B0, sh.a[0], acc);
   __syncthreads();  // the LDS is free for the next pass
 }
 
@@ -345,95 +450,115 @@ __device__ __forceinline__ void pf_down_store(const f4_t (&acc)[NMS][1], float* 
     }
 }
 
-// gate/up: grid (tiles of 64 rows over max(I, Is), E + 1, kPfMChunks);
-// y = 0: the shared expert (largest, started first), y = e + 1: expert e;
-// z: which 64-row chunks of the expert's rows (z, z + gridDim.z, ...), so
-// that the chunks of the shared and the busiest experts run side by side.
+// Work unit of block b: (item, tile of 64 weight rows).  The shared items
+// (the first nsh) have tsh tiles each and come first; the experts' items
+// have tr tiles each.  Returns false past the last item.
+struct PfUnit {
+  int e, row0, M, n0;
+};
+__device__ __forceinline__ bool pf_unit(const int32_t* items, int T, int tsh, int tr, PfUnit& u) {
+  const int b = blockIdx.x;
+  const int nsh = (T + kPfMaxM - 1) / kPfMaxM;
+  int it, tile;
+  if (b < nsh * tsh) {
+    it = b / tsh;
+    tile = b - it * tsh;
+  } else {
+    const int b2 = b - nsh * tsh;
+    it = nsh + b2 / tr;
+    tile = b2 - (it - nsh) * tr;
+    if (it >= items[0]) return false;
+  }
+  u.e = items[1 + 3 * it];
+  u.row0 = items[2 + 3 * it];
+  u.M = items[3 + 3 * it];
+  u.n0 = tile * kPfRows;
+  return true;
+}
+
+// gate/up: one block per unit (1-D grid); a unit of the shared expert
+// covers token rows [row0, row0 + M) of X, one of expert e the sorted pair
+// rows [row0, row0 + M).
 __global__ __launch_bounds__(kBlock, 2) void k_pf_gu(PfArgs a) {
   __shared__ PfShared sh;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const bool shared = blockIdx.y == 0;
-  const int e = blockIdx.y - 1;
-  const int N = shared ? a.Is : a.I;
-  const int n0 = blockIdx.x * kPfRows;
-  if (n0 >= N) return;
-  const int M = shared ? a.T : a.counts[e];
-  const int base = shared ? 0 : a.offsets[e];
+  PfUnit u;
+  if (!pf_unit(a.items, a.T, a.Is / kPfRows, a.I / kPfRows, u)) return;
+  const bool shared = u.e < 0;
   DevQ W[2];
   if (shared) {
     W[0] = a.shg;
     W[1] = a.shu;
   } else {
-    int s = a.slot ? a.slot[e] : e;
+    int s = a.slot ? a.slot[u.e] : u.e;
     W[0] = devq_at(a.gate, s);
     W[1] = devq_at(a.up, s);
   }
-  const int n = n0 + 16 * wave + (lane & 15);  // N is a multiple of 64
+  const int n = u.n0 + 16 * wave + (lane & 15);  // N is a multiple of 64
   _Float16* out = shared ? a.act_sh : a.act;
-  const int ld = shared ? a.Is : a.I;
-  for (int mc = blockIdx.z * kPfMaxM; mc < M; mc += gridDim.z * kPfMaxM) {
-    const int Mc = min(M - mc, kPfMaxM);
-    __syncthreads();
-    for (int m = threadIdx.x; m < Mc; m += kBlock) {
-      int t = shared ? mc + m : a.perm[base + mc + m] / a.K;
-      sh.rows[m] = t * a.H;
+  const int N = shared ? a.Is : a.I, ld = pad128(N);
+  const int Mc = u.M;
+  for (int m = threadIdx.x; m < Mc; m += kBlock) {
+    int t = shared ? u.row0 + m : a.perm[u.row0 + m] / a.K;
+    sh.rows[m] = t * pad128(a.H);
+  }
+  // the last tile also zeroes the padding columns of its rows
+  if (u.n0 + kPfRows == N) {
+    const int np = ld - N;
+    for (int i = threadIdx.x; i < Mc * np; i += kBlock) {
+      const int m = i / np;
+      out[(size_t)(u.row0 + m) * ld + N + (i - m * np)] = (_Float16)0.f;
     }
-    __syncthreads();
-    if (Mc <= 16) {
-      f4_t acc[1][2];
-      pf_pass<2, 1>(W, n, a.H, Mc, a.xh, sh, acc);
-      pf_gu_store<1>(acc, out, ld, base + mc, Mc, n);
-    } else if (Mc <= 32) {
-      f4_t acc[2][2];
-      pf_pass<2, 2>(W, n, a.H, Mc, a.xh, sh, acc);
-      pf_gu_store<2>(acc, out, ld, base + mc, Mc, n);
-    } else {
-      f4_t acc[4][2];
-      pf_pass<2, 4>(W, n, a.H, Mc, a.xh, sh, acc);
-      pf_gu_store<4>(acc, out, ld, base + mc, Mc, n);
-    }
+  }
+  __syncthreads();
+  if (Mc <= 16) {
+    f4_t acc[1][2];
+    pf_pass<2, 1>(W, n, a.H, Mc, a.xh, sh, acc);
+    pf_gu_store<1>(acc, out, ld, u.row0, Mc, n);
+  } else if (Mc <= 32) {
+    f4_t acc[2][2];
+    pf_pass<2, 2>(W, n, a.H, Mc, a.xh, sh, acc);
+    pf_gu_store<2>(acc, out, ld, u.row0, Mc, n);
+  } else {
+    f4_t acc[4][2];
+    pf_pass<2, 4>(W, n, a.H, Mc, a.xh, sh, acc);
+    pf_gu_store<4>(acc, out, ld, u.row0, Mc, n);
   }
 }
 
-// down: grid (tiles of 64 rows over H, E + 1, kPfMChunks); y and z as for
-// gate/up.
+// down: one block per unit (1-D grid), H / 64 tiles per item.
 __global__ __launch_bounds__(kBlock, 3) void k_pf_down(PfArgs a) {
   __shared__ PfShared sh;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const bool shared = blockIdx.y == 0;
-  const int e = blockIdx.y - 1;
-  const int n0 = blockIdx.x * kPfRows;
-  const int M = shared ? a.T : a.counts[e];
-  const int base = shared ? 0 : a.offsets[e];
+  PfUnit u;
+  if (!pf_unit(a.items, a.T, a.H / kPfRows, a.H / kPfRows, u)) return;
+  const bool shared = u.e < 0;
   const int Kd = shared ? a.Is : a.I;
   const _Float16* src = shared ? a.act_sh : a.act;
   DevQ W[1];
   if (shared) {
     W[0] = a.shd;
   } else {
-    int s = a.slot ? a.slot[e] : e;
+    int s = a.slot ? a.slot[u.e] : u.e;
     W[0] = devq_at(a.down, s);
   }
-  const int n = n0 + 16 * wave + (lane & 15);  // H is a multiple of 64
+  const int n = u.n0 + 16 * wave + (lane & 15);  // H is a multiple of 64
   float* out = shared ? a.y_sh : a.y;
-  for (int mc = blockIdx.z * kPfMaxM; mc < M; mc += gridDim.z * kPfMaxM) {
-    const int Mc = min(M - mc, kPfMaxM);
-    __syncthreads();
-    for (int m = threadIdx.x; m < Mc; m += kBlock) sh.rows[m] = (base + mc + m) * Kd;
-    __syncthreads();
-    if (Mc <= 16) {
-      f4_t acc[1][1];
-      pf_pass<1, 1>(W, n, Kd, Mc, src, sh, acc);
-      pf_down_store<1>(acc, out, a.H, base + mc, Mc, n);
-    } else if (Mc <= 32) {
-      f4_t acc[2][1];
-      pf_pass<1, 2>(W, n, Kd, Mc, src, sh, acc);
-      pf_down_store<2>(acc, out, a.H, base + mc, Mc, n);
-    } else {
-      f4_t acc[4][1];
-      pf_pass<1, 4>(W, n, Kd, Mc, src, sh, acc);
-      pf_down_store<4>(acc, out, a.H, base + mc, Mc, n);
-    }
+  const int Mc = u.M;
+  for (int m = threadIdx.x; m < Mc; m += kBlock) sh.rows[m] = (u.row0 + m) * pad128(Kd);
+  __syncthreads();
+  if (Mc <= 16) {
+    f4_t acc[1][1];
+    pf_pass<1, 1>(W, n, Kd, Mc, src, sh, acc);
+    pf_down_store<1>(acc, out, a.H, u.row0, Mc, n);
+  } else if (Mc <= 32) {
+    f4_t acc[2][1];
+    pf_pass<1, 2>(W, n, Kd, Mc, src, sh, acc);
+    pf_down_store<2>(acc, out, a.H, u.row0, Mc, n);
+  } else {
+    f4_t acc[4][1];
+    pf_pass<1, 4>(W, n, Kd, Mc, src, sh, acc);
+    pf_down_store<4>(acc, out, a.H, u.row0, Mc, n);
   }
 }
 
@@ -502,15 +627,20 @@ qmoe_status launch_prefill(const qmoe_moe_layer& L, const uint16_t* X, int T, co
   a.y = reinterpret_cast<float*>(pf + pl.y);
   a.y_sh = reinterpret_cast<float*>(pf + pl.y_sh);
   int32_t* pos_of = reinterpret_cast<int32_t*>(pf + pl.pos);
-  hipLaunchKernelGGL(k_pf_dispatch, dim3(1), dim3(1024), 0, S(stream), idx, T * K, E,
+  a.items = reinterpret_cast<int32_t*>(pf + pl.items);
+  hipLaunchKernelGGL(k_pf_dispatch, dim3(1), dim3(1024), 0, S(stream), idx, T * K, T, E,
                      const_cast<int32_t*>(a.counts), const_cast<int32_t*>(a.offsets),
-                     const_cast<int32_t*>(a.perm), pos_of);
-  const int n8 = T * H / 8;
-  hipLaunchKernelGGL(k_pf_prep, dim3((n8 + kBlock - 1) / kBlock), dim3(kBlock), 0, S(stream), X, n8,
-                     const_cast<_Float16*>(a.xh));
-  const int ngu = ((I > Is ? I : Is) + kPfRows - 1) / kPfRows;
-  hipLaunchKernelGGL(k_pf_gu, dim3(ngu, E + 1, kPfMChunks), dim3(kBlock), 0, S(stream), a);
-  hipLaunchKernelGGL(k_pf_down, dim3(H / kPfRows, E + 1, kPfMChunks), dim3(kBlock), 0, S(stream), a);
+                     const_cast<int32_t*>(a.perm), pos_of, const_cast<int32_t*>(a.items));
+  const int n8 = T * pad128(H) / 8;
+  hipLaunchKernelGGL(k_pf_prep, dim3((n8 + kBlock - 1) / kBlock), dim3(kBlock), 0, S(stream), X, T,
+                     H, const_cast<_Float16*>(a.xh));
+  // 1-D grids over the work units; blocks past the last item return at once
+  const int nsh = (T + kPfMaxM - 1) / kPfMaxM;
+  const int nr = pf_max_items(E, K, T) - nsh;
+  const int gu_blocks = nsh * (Is / kPfRows) + nr * (I / kPfRows);
+  const int dn_blocks = (nsh + nr) * (H / kPfRows);
+  hipLaunchKernelGGL(k_pf_gu, dim3(gu_blocks), dim3(kBlock), 0, S(stream), a);
+  hipLaunchKernelGGL(k_pf_down, dim3(dn_blocks), dim3(kBlock), 0, S(stream), a);
   hipLaunchKernelGGL(k_pf_combine, dim3((H / 8 + kBlock - 1) / kBlock, T), dim3(kBlock), 0,
                      S(stream), K, H, w, pos_of, a.y, a.y_sh, residual, out);
   return hipGetLastError() == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
