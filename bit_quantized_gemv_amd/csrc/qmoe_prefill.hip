@@ -244,51 +244,92 @@ constexpr int kPfAStride = 136;  // fp16 per staged A row: 128 + 8 (conflict-fre
 
 typedef unsigned int u4v_t __attribute__((ext_vector_type(4)));
 
+constexpr int kPfWaves = kBlock / 64;
+
+// LDS of a block: the A rows of two K-steps (double buffer), the A row
+// offsets, and per wave and matrix the codes of one pair of K-steps (the
+// wave's 16 weight rows × 128 bytes, 16-byte slots swizzled per row).
+template <int NM>
 struct PfShared {
-  _Float16 a[2][kPfMaxM * kPfAStride];  // A rows of two K-steps (double buffer)
+  _Float16 a[2][kPfMaxM * kPfAStride];
   int32_t rows[kPfMaxM];  // element offset of each A row from the A base
+  u4v_t w[kPfWaves][NM][16 * 8];
 };
 
-// Weights of one step: codes, and the group's scale and bias as loaded
-// (combined only where they are used, so that no instruction needs a load
-// right after issuing it).
+// Slot of 16-byte chunk c of row r (r < 16) in a wave's code tile: rows are
+// 128 bytes, so a plain layout puts the same chunk of every row in the same
+// banks; the rotation by r + r/8 spreads the 16 rows of one MFMA fragment
+// read over distinct slots (both for 8 and for 16 lanes per LDS cycle).
+__device__ __forceinline__ int pf_wslot(int r, int c) { return r * 8 + (c ^ ((r + (r >> 3)) & 7)); }
+
+// Codes of one pair of K-steps (256 codes = 128 bytes per row), loaded as
+// whole 128-byte lines: lane l takes chunk l%8 of rows l/8 and 8 + l/8 of
+// the wave's 16 rows.  Past the end of a row the last chunk is re-read:
+// finite values whose products meet zero A columns.
 template <int NM>
-struct PfW {
-  u4v_t q[NM];
+struct PfWG {
+  u4v_t v[NM][2];
+};
+struct PfGOff {
+  uint32_t row0, row1;  // byte offsets of the lane's two rows
+  uint32_t c16;         // 16 (l % 8)
+  uint32_t qmax;        // last 16-byte chunk of a row: K/2 - 16
+};
+__device__ __forceinline__ PfGOff pf_goff(int n_wave0, int K) {
+  const int lane = threadIdx.x & 63;
+  PfGOff o;
+  o.row0 = (uint32_t)(n_wave0 + (lane >> 3)) * (uint32_t)(K / 2);
+  o.row1 = (uint32_t)(n_wave0 + 8 + (lane >> 3)) * (uint32_t)(K / 2);
+  o.c16 = 16u * (uint32_t)(lane & 7);
+  o.qmax = (uint32_t)(K / 2 - 16);
+  return o;
+}
+template <int NM>
+__device__ __forceinline__ void pf_load_wg(PfWG<NM>& G, const DevQ (&W)[NM], const PfGOff& o,
+                                           int bs) {
+  const uint32_t off = min(128u * (uint32_t)bs + o.c16, o.qmax);
+#pragma unroll
+  for (int k = 0; k < NM; ++k) {
+    G.v[k][0] = *reinterpret_cast<const u4v_t*>(W[k].q + (o.row0 + off));
+    G.v[k][1] = *reinterpret_cast<const u4v_t*>(W[k].q + (o.row1 + off));
+  }
+}
+template <int NM>
+__device__ __forceinline__ void pf_store_wg(const PfWG<NM>& G, u4v_t (*wl)[16 * 8]) {
+  const int lane = threadIdx.x & 63, r = lane >> 3, c = lane & 7;
+#pragma unroll
+  for (int k = 0; k < NM; ++k) {
+    wl[k][pf_wslot(r, c)] = G.v[k][0];
+    wl[k][pf_wslot(r + 8, c)] = G.v[k][1];
+  }
+}
+
+// Scale and bias of the group of a lane's codes in step kb, as loaded
+// (combined only where they are used, so that no instruction needs a load
+// right after issuing it).  Lane (n = l%16, j = l/16) takes codes
+// [128 kb + 32 j, +32) of row n in step kb.
+template <int NM>
+struct PfSB {
   uint32_t s[NM], b[NM];  // fp16 bits, zero-extended
 };
-
-// Per-lane weight offsets of one pass: the lane's row n_row of every
-// matrix (all NM have the same shape), codes from 32j on in each step.
-struct PfWOff {
-  uint32_t qrow;  // byte offset of the row's codes
+struct PfSOff {
   uint32_t srow;  // element offset of the row's scales and biases
   uint32_t j16;   // 16 j: the lane's bytes within a step
-  uint32_t qmax;  // last 16-byte chunk of a row: K/2 - 16
+  uint32_t qmax;  // K/2 - 16
 };
-__device__ __forceinline__ PfWOff pf_woff(int n_row, int K) {
-  PfWOff o;
-  o.qrow = (uint32_t)n_row * (uint32_t)(K / 2);
+__device__ __forceinline__ PfSOff pf_soff(int n_row, int K) {
+  PfSOff o;
   o.srow = (uint32_t)n_row * (uint32_t)(K / 64);
   o.j16 = 16u * (uint32_t)((threadIdx.x & 63) >> 4);
   o.qmax = (uint32_t)(K / 2 - 16);
   return o;
 }
-
-// Weights of step kb.  Past the end of a row a lane re-reads the row's last
-// chunk and its group's scale and bias: finite values whose products meet
-// zero A columns.  The bases are uniform and the offsets 32-bit, so the
-// loads take a scalar base and one vector offset each.
 template <int NM>
-__device__ __forceinline__ void pf_load_w(PfW<NM>& B, const DevQ (&W)[NM], const PfWOff& o,
-                                          int kb) {
-  const uint32_t cq = min(64u * (uint32_t)kb + o.j16, o.qmax);
-  const uint32_t qo = o.qrow + cq, so = o.srow + (cq >> 5);
+__device__ __forceinline__ void pf_load_sb(PfSB<NM>& B, const DevQ (&W)[NM], const PfSOff& o,
+                                           int kb) {
+  const uint32_t so = o.srow + (min(64u * (uint32_t)kb + o.j16, o.qmax) >> 5);
 #pragma unroll
   for (int k = 0; k < NM; ++k) {
-    // cached loads: a step reads half of each 128-byte line, the next step
-    // the other half
-    B.q[k] = *reinterpret_cast<const u4v_t*>(W[k].q + qo);
     B.s[k] = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(W[k].s) + 2u * so);
     B.b[k] = *reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(W[k].b) + 2u * so);
   }
@@ -303,8 +344,8 @@ struct PfA {
 };
 // Byte offsets (from the A base) of this thread's A rows, read from
 // sh.rows once per pass.
-template <int NMS>
-__device__ __forceinline__ void pf_rows(uint32_t (&roff)[NMS], const PfShared& sh, int Mc) {
+template <int NMS, int NM>
+__device__ __forceinline__ void pf_rows(uint32_t (&roff)[NMS], const PfShared<NM>& sh, int Mc) {
   const int r0 = threadIdx.x >> 4;
 #pragma unroll
   for (int i = 0; i < NMS; ++i) roff[i] = 2u * (uint32_t)sh.rows[min(r0 + 16 * i, Mc - 1)];
@@ -326,20 +367,24 @@ __device__ __forceinline__ void pf_store_a(const PfA<NMS>& A, _Float16* buf) {
   for (int i = 0; i < NMS; ++i) *reinterpret_cast<u4v_t*>(dst + 16 * i * kPfAStride) = A.v[i];
 }
 
+// MFMAs of one K-step: the lane's codes (16 bytes of row n = l%16 per
+// matrix, half h of the pair in the wave's code tile), dequantized with
+// the group's scale and bias, against the staged A rows.
 template <int NM, int NMS>
-__device__ __forceinline__ void pf_mma(const PfW<NM>& B, const _Float16* buf,
-                                       f4_t (&acc)[NMS][NM]) {
+__device__ __forceinline__ void pf_mma(const u4v_t (*wl)[16 * 8], int h, const PfSB<NM>& B,
+                                       const _Float16* buf, f4_t (&acc)[NMS][NM]) {
   const int lane = threadIdx.x & 63, m = lane & 15, j = lane >> 4;
   h8_t Bf[NM][4];
 #pragma unroll
   for (int k = 0; k < NM; ++k) {
+    const u4v_t q = wl[k][pf_wslot(m, 4 * h + j)];
     const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)B.s[k]);
     const _Float16 bv = __builtin_bit_cast(_Float16, (uint16_t)B.b[k]);
     const h2_t s2 = {sv, sv}, b2 = {bv, bv};
-    Bf[k][0] = dequant_word(B.q[k].x, s2, b2);
-    Bf[k][1] = dequant_word(B.q[k].y, s2, b2);
-    Bf[k][2] = dequant_word(B.q[k].z, s2, b2);
-    Bf[k][3] = dequant_word(B.q[k].w, s2, b2);
+    Bf[k][0] = dequant_word(q.x, s2, b2);
+    Bf[k][1] = dequant_word(q.y, s2, b2);
+    Bf[k][2] = dequant_word(q.z, s2, b2);
+    Bf[k][3] = dequant_word(q.w, s2, b2);
   }
 #pragma unroll
   for (int ms = 0; ms < NMS; ++ms) {
@@ -358,57 +403,91 @@ __device__ __forceinline__ void pf_mma(const PfW<NM>& B, const _Float16* buf,
 }
 
 // C = A W^T over one pass of Mc <= 64 A rows (sh.rows[0..Mc) set: element
-// offsets of rows of pad128(K) columns, the padding zero), K columns;
-// acc[ms][k]: lane l holds rows 16ms + 4(l/16) + r, column l%16.
-// Weights run two steps ahead in registers.  A rows are loaded three steps
-// ahead into registers (two alternating sets) and stored, two steps after
-// their loads were issued, to the LDS buffer of the next step (two
-// alternating buffers, one barrier per step).  Step kb: store A(kb + 1),
-// load A(kb + 3) into the set just freed, MMA on A(kb), load W(kb + 2).
-// The loop body has no conditional loads or stores and no exit in the
-// middle (loads past the last step re-read the last step, and the stores
-// past it go to the buffer no one reads next), so every wait for a load in
-// flight waits for that load only.
-template <int NM, int NMS>
-__device__ __forceinline__ void pf_pass(const DevQ (&W)[NM], int n_row, int K, int Mc,
-                                        const _Float16* abase, PfShared& sh,
-                                        f4_t (&acc)[NMS][NM]) {
+// offsets of rows of pad128(K) columns, the padding zero), K columns, for
+// the wave's 16 weight rows from n_wave0 on; acc[ms][k]: lane l holds rows
+// 16ms + 4(l/16) + r, column n_wave0 + l%16.
+//
+// Pipeline, per iteration four K-steps kb..kb+3 (two pairs):
+//  - codes: each pair of steps is loaded as whole lines into registers
+//    (two alternating sets, four steps ahead) and written to the wave's
+//    code tile in LDS right before its first step;
+//  - scales and biases: per step, four steps ahead (four sets);
+//  - A rows: in AD register sets, loaded AD + 1 steps ahead and stored, AD
+//    steps after their loads were issued, to the LDS buffer of the next
+//    step (two alternating buffers, one barrier per step).  AD is 4 for up
+//    to 32 rows and 2 for more (bounded registers).
+// Loads and stores are unconditional (past the last step they re-read the
+// last one); only the MFMAs of steps past the last are skipped, by a
+// uniform branch.  So every wait for a load in flight waits for that load
+// only.
+// rows(): writes sh.rows[0..Mc) and ends with a block barrier; it runs
+// after the first weight loads are issued, so its reads overlap them.
+template <int NM, int NMS, typename Rows>
+__device__ __forceinline__ void pf_pass(const DevQ (&W)[NM], int n_wave0, int K, int Mc,
+                                        const _Float16* abase, PfShared<NM>& sh,
+                                        f4_t (&acc)[NMS][NM], Rows rows) {
+  constexpr int AD = NMS <= 2 ? 4 : 2;
 #pragma unroll
   for (int ms = 0; ms < NMS; ++ms)
 #pragma unroll
     for (int k = 0; k < NM; ++k) acc[ms][k] = f4_t{0.f, 0.f, 0.f, 0.f};
   const int nkb = (K + 127) / 128;
+  const int wave = threadIdx.x >> 6;
+  u4v_t(*wl)[16 * 8] = sh.w[wave];
+  const PfGOff go = pf_goff(n_wave0, K);
+  const PfSOff so = pf_soff(n_wave0 + ((threadIdx.x & 63) & 15), K);
+  PfWG<NM> G0, G1;
+  PfSB<NM> S0, S1, S2, S3;
+  PfA<NMS> R[AD];  // R[(s + 1) % AD] holds A(s + 1) when step s begins
+  // prologue: the loads of a virtual iteration before the first, in the
+  // loop's own order (G0; per step t the A set it refills, then S_t; G1
+  // before step 2), so that at the loop head the waits counted along both
+  // incoming paths agree: codes of pairs 0 and 1, scales and biases of
+  // steps 0..3, A(1)..A(AD) into R[t % AD]; A(0) goes to LDS buffer 0.
+  pf_load_wg<NM>(G0, W, go, 0);
+  rows();
   uint32_t roff[NMS];
-  pf_rows<NMS>(roff, sh, Mc);
-  const PfWOff wo = pf_woff(n_row, K);
-  PfW<NM> B0, B1;
-  PfA<NMS> Aa, Ab;
-  // prologue: A(0) -> LDS buffer 0; Aa = A(1), Ab = A(2) in flight
-  pf_load_a<NMS>(Aa, abase, roff, 0);
-  pf_load_w<NM>(B0, W, wo, 0);
-  pf_store_a<NMS>(Aa, sh.a[0]);
-  pf_load_a<NMS>(Aa, abase, roff, min(1, nkb - 1));
-  pf_load_w<NM>(B1, W, wo, 1);
-  pf_load_a<NMS>(Ab, abase, roff, min(2, nkb - 1));
+  pf_rows<NMS, NM>(roff, sh, Mc);
+  PfA<NMS> A0;
+  pf_load_a<NMS>(A0, abase, roff, 0);
+  // step t of the virtual iteration loads A(t + 1 - (4 - AD)) when that is
+  // >= 1 (AD = 4: A(1..4); AD = 2: A(1), A(2) in steps 2 and 3)
+  auto pro = [&](int t, PfSB<NM>& S) {
+    const int ia = t + 1 - (4 - AD);
+    if (ia >= 1) pf_load_a<NMS>(R[(t + 1) % AD], abase, roff, min(ia, nkb - 1));
+    pf_load_sb<NM>(S, W, so, t);
+  };
+  pro(0, S0);
+  pro(1, S1);
+  pf_load_wg<NM>(G1, W, go, 1);
+  pro(2, S2);
+  pro(3, S3);
+  pf_store_a<NMS>(A0, sh.a[0]);
   __syncthreads();
-  int kb = 0;
-  for (; kb + 2 <= nkb; kb += 2) {
-    // step kb: buffer 0 holds A(kb); Aa holds A(kb + 1), Ab A(kb + 2)
-    pf_store_a<NMS>(Aa, sh.a[1]);
-    pf_load_a<NMS>(Aa, abase, roff, min(kb + 3, nkb - 1));
-    pf_mma<NM, NMS>(B0, sh.a[0], acc);
-    pf_load_w<NM>(B0, W, wo, kb + 2);
+  // one step s = kb + t: A(s + 1) to the other buffer, A(s + 1 + AD) into
+  // the set just freed, the MFMAs on A(s), scales and biases of s + 4
+  auto step = [&](int kb, int t, PfSB<NM>& S) {
+    PfA<NMS>& X = R[(t + 1) % AD];
+    pf_store_a<NMS>(X, sh.a[(t + 1) & 1]);
+    pf_load_a<NMS>(X, abase, roff, min(kb + t + 1 + AD, nkb - 1));
+    if (t == 0 || kb + t < nkb) pf_mma<NM, NMS>(wl, t & 1, S, sh.a[t & 1], acc);
+    pf_load_sb<NM>(S, W, so, kb + t + 4);
     __syncthreads();
-    // step kb + 1: buffer 1 holds A(kb + 1); Ab holds A(kb + 2), Aa A(kb + 3)
-    pf_store_a<NMS>(Ab, sh.a[0]);
-    pf_load_a<NMS>(Ab, abase, roff, min(kb + 4, nkb - 1));
-    pf_mma<NM, NMS>(B1, sh.a[1], acc);
-    pf_load_w<NM>(B1, W, wo, kb + 3);
-    __syncthreads();
+  };
+  for (int kb = 0; kb < nkb; kb += 4) {
+    const int bs = kb >> 1;
+    // pair bs: its codes to the wave's tile, then the codes of pair bs + 2
+    pf_store_wg<NM>(G0, wl);
+    pf_load_wg<NM>(G0, W, go, bs + 2);
+    step(kb, 0, S0);
+    step(kb, 1, S1);
+    // pair bs + 1 (the tile's reads of pair bs are issued: LDS operations
+    // of one wave run in order)
+    pf_store_wg<NM>(G1, wl);
+    pf_load_wg<NM>(G1, W, go, bs + 3);
+    step(kb, 2, S2);
+    step(kb, 3, S3);
   }
-  // odd number of steps: the last one (buffer 0 holds it, B0 its weights)
-  if (kb < nkb) pf_mma<NM, NMS>(B0, sh.a[0], acc);
-  __syncthreads();  // the LDS is free for the next pass
 }
 
 // Column position of output feature n inside its group of 8 in the prepared
@@ -480,7 +559,7 @@ __device__ __forceinline__ bool pf_unit(const int32_t* items, int T, int tsh, in
 // covers token rows [row0, row0 + M) of X, one of expert e the sorted pair
 // rows [row0, row0 + M).
 __global__ __launch_bounds__(kBlock, 2) void k_pf_gu(PfArgs a) {
-  __shared__ PfShared sh;
+  __shared__ PfShared<2> sh;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   PfUnit u;
   if (!pf_unit(a.items, a.T, a.Is / kPfRows, a.I / kPfRows, u)) return;
@@ -498,10 +577,6 @@ __global__ __launch_bounds__(kBlock, 2) void k_pf_gu(PfArgs a) {
   _Float16* out = shared ? a.act_sh : a.act;
   const int N = shared ? a.Is : a.I, ld = pad128(N);
   const int Mc = u.M;
-  for (int m = threadIdx.x; m < Mc; m += kBlock) {
-    int t = shared ? u.row0 + m : a.perm[u.row0 + m] / a.K;
-    sh.rows[m] = t * pad128(a.H);
-  }
   // the last tile also zeroes the padding columns of its rows
   if (u.n0 + kPfRows == N) {
     const int np = ld - N;
@@ -510,25 +585,31 @@ __global__ __launch_bounds__(kBlock, 2) void k_pf_gu(PfArgs a) {
       out[(size_t)(u.row0 + m) * ld + N + (i - m * np)] = (_Float16)0.f;
     }
   }
-  __syncthreads();
+  auto rows = [&] {
+    for (int m = threadIdx.x; m < Mc; m += kBlock) {
+      int t = shared ? u.row0 + m : a.perm[u.row0 + m] / a.K;
+      sh.rows[m] = t * pad128(a.H);
+    }
+    __syncthreads();
+  };
   if (Mc <= 16) {
     f4_t acc[1][2];
-    pf_pass<2, 1>(W, n, a.H, Mc, a.xh, sh, acc);
+    pf_pass<2, 1>(W, n - (lane & 15), a.H, Mc, a.xh, sh, acc, rows);
     pf_gu_store<1>(acc, out, ld, u.row0, Mc, n);
   } else if (Mc <= 32) {
     f4_t acc[2][2];
-    pf_pass<2, 2>(W, n, a.H, Mc, a.xh, sh, acc);
+    pf_pass<2, 2>(W, n - (lane & 15), a.H, Mc, a.xh, sh, acc, rows);
     pf_gu_store<2>(acc, out, ld, u.row0, Mc, n);
   } else {
     f4_t acc[4][2];
-    pf_pass<2, 4>(W, n, a.H, Mc, a.xh, sh, acc);
+    pf_pass<2, 4>(W, n - (lane & 15), a.H, Mc, a.xh, sh, acc, rows);
     pf_gu_store<4>(acc, out, ld, u.row0, Mc, n);
   }
 }
 
 // down: one block per unit (1-D grid), H / 64 tiles per item.
 __global__ __launch_bounds__(kBlock, 3) void k_pf_down(PfArgs a) {
-  __shared__ PfShared sh;
+  __shared__ PfShared<1> sh;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   PfUnit u;
   if (!pf_unit(a.items, a.T, a.H / kPfRows, a.H / kPfRows, u)) return;
@@ -545,19 +626,21 @@ __global__ __launch_bounds__(kBlock, 3) void k_pf_down(PfArgs a) {
   const int n = u.n0 + 16 * wave + (lane & 15);  // H is a multiple of 64
   float* out = shared ? a.y_sh : a.y;
   const int Mc = u.M;
-  for (int m = threadIdx.x; m < Mc; m += kBlock) sh.rows[m] = (u.row0 + m) * pad128(Kd);
-  __syncthreads();
+  auto rows = [&] {
+    for (int m = threadIdx.x; m < Mc; m += kBlock) sh.rows[m] = (u.row0 + m) * pad128(Kd);
+    __syncthreads();
+  };
   if (Mc <= 16) {
     f4_t acc[1][1];
-    pf_pass<1, 1>(W, n, Kd, Mc, src, sh, acc);
+    pf_pass<1, 1>(W, n - (lane & 15), Kd, Mc, src, sh, acc, rows);
     pf_down_store<1>(acc, out, a.H, u.row0, Mc, n);
   } else if (Mc <= 32) {
     f4_t acc[2][1];
-    pf_pass<1, 2>(W, n, Kd, Mc, src, sh, acc);
+    pf_pass<1, 2>(W, n - (lane & 15), Kd, Mc, src, sh, acc, rows);
     pf_down_store<2>(acc, out, a.H, u.row0, Mc, n);
   } else {
     f4_t acc[4][1];
-    pf_pass<1, 4>(W, n, Kd, Mc, src, sh, acc);
+    pf_pass<1, 4>(W, n - (lane & 15), Kd, Mc, src, sh, acc, rows);
     pf_down_store<4>(acc, out, a.H, u.row0, Mc, n);
   }
 }
