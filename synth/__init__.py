@@ -83,6 +83,9 @@ WORKLOADS: Dict[str, Workload] = {
                                   layers=5, tokens=3, rmsnorm=True),
     "odd_stack_decode": Workload(8, "odd_stack_decode", 1024, 64, 4, 128, 256,
                                  layers=4, tokens=2, rmsnorm=True),
+    # a prefill shape whose widths are not multiples of 128 (padded operand
+    # rows) and whose counts are not powers of two
+    "odd_prefill": Workload(9, "odd_prefill", 576, 24, 4, 192, 320, tokens=33),
 }
 
 

@@ -152,6 +152,22 @@ def test_prefill_forced_routing_tiny(torch_cuda, q, tiny_layer, T):
     _check_rows(got, ref)
 
 
+@pytest.mark.parametrize("T", [5, 33])
+def test_prefill_odd_widths(torch_cuda, q, T):
+    """Hidden and intermediate widths that are not multiples of 128 (576,
+    192, 320: the fp16 operand rows carry zero padding), 24 experts, top-4;
+    forced routing, residual on odd rows counts."""
+    torch = torch_cuda
+    wl = synth.WORKLOADS["odd_prefill"]
+    lw = synth.make_layer(wl, 0)
+    ol, dl = oracle.OracleLayer(lw), synth.device.DeviceLayer(lw)
+    log(f"prefill odd widths T={T}")
+    X = synth.make_tokens(wl, T, stream=70 + T)
+    idx, w = synth.dirichlet_routing(wl, T, stream=30 + T)
+    got, _ = _prefill(torch, q, dl.layer, X, idx, w, residual=True)
+    _check_rows(got, _oracle_rows_forced(ol, X, idx, w, residual=True))
+
+
 def test_prefill_hot_and_repeated_experts(torch_cuda, q, tiny_layer):
     """Every token on the same 8 experts (128 rows each), then one expert
     repeated 8 times per token (1024 rows, more than one pass of 128)."""
