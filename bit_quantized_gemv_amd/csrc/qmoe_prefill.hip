@@ -7,12 +7,16 @@
 //
 // Launches (one stream):
 //   dispatch  counts/offsets of the pairs per expert and their stable order
-//             (expert, then token, then rank), from wave ballots
+//             (expert, then token, then rank), from wave ballots; the work
+//             list of the GEMMs: items of at most 64 rows of one expert
+//             (the shared expert's first, then the experts' by decreasing
+//             row count)
 //   prep      X (bf16) -> fp16, each 8 columns in the order the weights are
-//             unpacked in: (x0,x2,x4,x6,x1,x3,x5,x7)
-//   gemm gu   per (expert, 64 output rows): A = gelu(X_e Wg^T) * (X_e Wu^T)
-//             for the expert's rows; the shared expert over all T rows
-//   gemm down per (expert, 64 output rows): Y_e = A_e Wd^T; shared likewise
+//             unpacked in: (x0,x2,x4,x6,x1,x3,x5,x7), rows padded with zeros
+//             to a multiple of 128 columns
+//   gemm gu   per (item, 64 output rows): A = gelu(X_e Wg^T) * (X_e Wu^T)
+//             for the item's rows
+//   gemm down per (item, 64 output rows): Y_e = A_e Wd^T
 //   combine   out[t] = bf16(Y_s[t] + sum_j w[t][j] Y[pos(t,j)] (+ residual))
 //
 // The GEMMs use v_mfma_f32_16x16x32_f16 with fp32 accumulation.  Weights are
@@ -201,12 +205,13 @@ __global__ __launch_bounds__(kBlock) void k_pf_prep(const uint16_t* X, int T, in
 
 // ================================================================= GEMMs
 // One block: 64 weight rows (wave w: rows n0 + 16w + l%16) of NM matrices
-// against up to 128 rows of A (an expert's tokens), K in steps of 128
-// codes.  Per step the block stages its A rows (fp16, prepared layout) in
-// LDS once for all four waves, while every lane holds the next two steps
-// of its weights in registers: lane (n = l%16, j = l/16) holds codes
-// [128kb + 32j, +32) of its row as 4 words; word t feeds MFMA t (K slots
-// 8j..8j+7), dequantized to fp16 in the order (q0,q2,q4,q6,q1,q3,q5,q7).
+// against up to 64 rows of A (an item: one expert's tokens), K in steps of
+// 128 codes.  Per step the block stages its A rows (fp16, prepared layout)
+// in LDS once for all four waves; each wave stages its 16 weight rows in a
+// code tile of its own (pf_pass), from which lane (n = l%16, j = l/16)
+// takes codes [128kb + 32j, +32) of its row as 4 words; word t feeds MFMA t
+// (K slots 8j..8j+7), dequantized to fp16 in the order
+// (q0,q2,q4,q6,q1,q3,q5,q7).
 __device__ __forceinline__ h8_t dequant_word(uint32_t v, h2_t s2, h2_t b2) {
   const uint32_t lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;
   h2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false);  // q0, q2
@@ -229,9 +234,7 @@ struct PfArgs {
   int T, K, E, H, I, Is;
   DevQ gate, up, down, shg, shu, shd;
   const int32_t* slot;
-  const int32_t* counts;
-  const int32_t* offsets;
-  const int32_t* perm;
+  const int32_t* perm;   // sorted pair -> flat pair index t*K + j
   const int32_t* items;  // [n_items, (e, row0, M) ...] (the dispatch's work list)
   const _Float16* xh;   // [T][pad128(H)] prepared input
   _Float16* act;        // [T*K][pad128(I)] routed activations (sorted order, prepared layout)
@@ -701,8 +704,8 @@ qmoe_status launch_prefill(const qmoe_moe_layer& L, const uint16_t* X, int T, co
   a.gate = devq(L.gate); a.up = devq(L.up); a.down = devq(L.down);
   a.shg = devq(L.sh_gate); a.shu = devq(L.sh_up); a.shd = devq(L.sh_down);
   a.slot = nullptr;
-  a.counts = reinterpret_cast<int32_t*>(pf + pl.counts);
-  a.offsets = reinterpret_cast<int32_t*>(pf + pl.offsets);
+  int32_t* counts = reinterpret_cast<int32_t*>(pf + pl.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(pf + pl.offsets);
   a.perm = reinterpret_cast<int32_t*>(pf + pl.perm);
   a.xh = reinterpret_cast<_Float16*>(pf + pl.xh);
   a.act = reinterpret_cast<_Float16*>(pf + pl.act);
@@ -712,8 +715,8 @@ qmoe_status launch_prefill(const qmoe_moe_layer& L, const uint16_t* X, int T, co
   int32_t* pos_of = reinterpret_cast<int32_t*>(pf + pl.pos);
   a.items = reinterpret_cast<int32_t*>(pf + pl.items);
   hipLaunchKernelGGL(k_pf_dispatch, dim3(1), dim3(1024), 0, S(stream), idx, T * K, T, E,
-                     const_cast<int32_t*>(a.counts), const_cast<int32_t*>(a.offsets),
-                     const_cast<int32_t*>(a.perm), pos_of, const_cast<int32_t*>(a.items));
+                     counts, offsets, const_cast<int32_t*>(a.perm), pos_of,
+                     const_cast<int32_t*>(a.items));
   const int n8 = T * pad128(H) / 8;
   hipLaunchKernelGGL(k_pf_prep, dim3((n8 + kBlock - 1) / kBlock), dim3(kBlock), 0, S(stream), X, T,
                      H, const_cast<_Float16*>(a.xh));
