@@ -15,10 +15,13 @@ the layer's weights are held in 32 separate copies (~14 GB) and consecutive
 steps cycle through them, each with its own input token.
 
 The 128-token prefill chunk (router with the Zipf prior, then the grouped
-MFMA prefill) is timed as a second, reported-only leg on the same weights.
+MFMA prefill) is timed as a second, reported-only leg on the same weights;
+the standalone 4-bit GEMV on a large matrix of the decode width, the
+30-layer stack and (with --streaming) the expert pool are further
+reported-only legs.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--no-prefill] [--copy-calibration]
+                    [--no-prefill] [--no-gemv] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -116,6 +119,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill leg")
+    ap.add_argument("--no-gemv", action="store_true", help="skip the standalone GEMV leg")
     ap.add_argument("--no-stack", action="store_true", help="skip the 30-layer stack leg")
     ap.add_argument("--streaming", action="store_true",
                     help="only the expert-streaming leg (30 layers, pinned host experts, "
@@ -287,6 +291,8 @@ def main():
     }
     if not args.no_prefill:
         res["prefill"] = prefill_leg(torch, q, synth, sd, lw, layers, wl, sptr)
+    if not args.no_gemv:
+        res["gemv"] = gemv_leg(torch, q, sptr)
     if not args.no_stack:
         del layers
         torch.cuda.empty_cache()
@@ -552,6 +558,62 @@ def streaming_leg(torch, q, synth, sd, steps: int = 512):
     log(f"streaming: {res['value']:.1f} tokens/s, hit rate {res['hit_rate']:.3f}, "
         f"H2D {res['h2d_GBps']:.1f} GB/s")
     return res
+
+
+def gemv_leg(torch, q, sptr, rows: int = 65536, cols: int = 2816, copies: int = 8,
+             iters: int = 400):
+    """The standalone 4-bit affine GEMV (qmoe_gemv_affine4) on a large matrix
+    of the decode width (rows x cols, seeded codes, scales ~U(0.005, 0.02),
+    biases -8*scale), cycling through copies that together exceed the 256 MB
+    MALL.  HIP events around `iters` back-to-back launches; algorithmic bytes
+    = codes + fp16 scales and biases + x + y.  Also a plain 512 MiB device
+    copy, for context (bytes read + written per second)."""
+    import ctypes
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(20260)
+    mats = []
+    for _ in range(copies):
+        qw = torch.randint(-2 ** 31, 2 ** 31 - 1, (rows, cols // 8), dtype=torch.int32,
+                           device="cuda", generator=g)
+        sc = (torch.rand(rows, cols // 64, device="cuda", generator=g) * 0.015 + 0.005).half()
+        bi = (-8.0 * sc.float()).half()
+        mats.append(q.QTensor(qw, sc.view(torch.int16), bi.view(torch.int16), rows, cols, 4))
+    x = torch.randn(cols, device="cuda", generator=g).bfloat16().view(torch.int16)
+    y = torch.empty(rows, dtype=torch.float32, device="cuda")
+    nbytes = rows * cols // 2 + rows * (cols // 64) * 4 + cols * 2 + rows * 4
+    fn = q.lib().qmoe_gemv_affine4
+    cts = [ctypes.byref(m.c()) for m in mats]
+    for i in range(2 * copies):
+        fn(cts[i % copies], x.data_ptr(), y.data_ptr(), sptr)
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(iters):
+        rc = fn(cts[i % copies], x.data_ptr(), y.data_ptr(), sptr)
+        if rc:
+            raise q.QmoeError("qmoe_gemv_affine4", rc)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / iters
+    del mats
+    src = torch.ones(COPY_BYTES // 8, dtype=torch.int32, device="cuda")  # 512 MiB: beyond the MALL
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0.record(stream)
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * src.numel() * 4 * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    gbs = nbytes / (us * 1e-6) / 1e9
+    log(f"gemv {rows}x{cols}: {us:.2f} us, {gbs:.0f} GB/s; device copy {copy_gbs:.0f} GB/s")
+    return {"workload": f"4-bit affine g64 GEMV, {rows} x {cols} (decode width), "
+                        f"{copies} copies cycled",
+            "entry": "qmoe_gemv_affine4", "us_per_gemv": us, "algorithmic_bytes": nbytes,
+            "achieved_GBps": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS,
+            "device_copy_GBps_read_plus_write": copy_gbs}
 
 
 def copy_calibration(torch, reps: int = 3):

@@ -84,6 +84,25 @@ def test_gemv_matches_oracle_within_bound(torch_cuda, q, rows, cols):
     assert rel_l2(got, ref) <= 1e-5
 
 
+@pytest.mark.parametrize("rows,cols", [(20003, 2816), (40000, 2112), (70001, 704)])
+def test_gemv_large_matches_oracle_within_bound(torch_cuda, q, rows, cols):
+    """Matrices large enough for the persistent form (more row-blocks than
+    resident waves), with a ragged last row-block: every row within the
+    bound of the oracle's fp64 GEMV."""
+    torch = torch_cuda
+    log(f"gemv parity (persistent) rows={rows} cols={cols}")
+    m = synth.random_qmat(rows, cols, 4, rows + cols)
+    x = synth.random_bf16(cols, 5)
+    xd = bf16_to_f64(x)
+    ref = oracle.qgemv(m, xd)
+    y = torch.full((rows,), float("nan"), dtype=torch.float32, device="cuda")
+    q.qmoe_gemv_affine4(synth.device.qtensor(m), _dev_u16(torch, x), y)
+    got = y.cpu().numpy().astype(np.float64)
+    bound = gemv4_bound(m, xd)
+    assert np.all(np.abs(got - ref) <= bound), np.nanmax(np.abs(got - ref) / bound)
+    assert rel_l2(got, ref) <= 1e-5
+
+
 def test_gemv_rejects_bad_arguments(torch_cuda, q):
     torch = torch_cuda
     m = synth.random_qmat(8, 128, 4, 1)
