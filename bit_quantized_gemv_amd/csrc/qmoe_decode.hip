@@ -1044,34 +1044,55 @@ __device__ bool role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
     const int k = t / CHk, c = t - k * CHk;
     dtask_load(T, devq_at(a.down, slot_s[k]), row0, CHk, c);
   }
-  // 3. shared activations once the S blocks are published, shared part
-  if (!a.nowait && !a.s_done &&
-      !block_wait_flags(flags, a.nS, epoch, ctlw, 2, sys, kPollWave, t))
-    return false;
-  stage_run(act_of(a, blockIdx.x % ctl::kRep), 0, Is, Is, as_sh, ah_sh, t);
-  __syncthreads();
-  if (kOnePass) {
-    if (!routed && t < ntask) dtask_acc(T, as_sh, ah_sh, CHs, t - nrt, 1.0f, acc);
+  if constexpr (kOnePass) {
+    // 3-4. two passes through one copy of the wait / staging / accumulate
+    //    code: pass 0 takes the shared activations once the S blocks are
+    //    published, pass 1 the routed ones once the G blocks of all K
+    //    experts are (one wait, one staging pass).  Each lane's one task
+    //    falls in one of the passes.  The routed pass, on the critical
+    //    path, runs instructions the shared pass has already fetched.
+#pragma clang loop unroll(disable)
+    for (int p = 0; p < 2; ++p) {
+      if (!a.nowait && !(p == 0 && a.s_done) &&
+          !block_wait_flags(flags + (p ? a.nS : 0), p ? K * a.perG : a.nS, epoch, ctlw, 2 + p, sys,
+                            kPollWave, t))
+        return false;
+      const int off = p ? Is : 0;
+      stage_run(act_of(a, blockIdx.x % ctl::kRep), off, p ? K * I : Is, p ? I : Is,
+                as_sh + off / 4, ah_sh + off / 32, t);
+      __syncthreads();
+      // the weights as if reloaded per pass: their decoded forms are not
+      // hoisted out of the loop and held in registers across both passes
+#pragma unroll
+      for (int r = 0; r < kRowsPerUnit; ++r)
+        asm volatile("" : "+v"(T.w[r].x), "+v"(T.w[r].y), "+v"(T.w[r].z), "+v"(T.w[r].w),
+                     "+v"(T.sb[r]));
+      if (p ? routed : (!routed && t < ntask)) {
+        const int k = routed ? t / CHk : 0;
+        const int base = routed ? Is + k * I : 0;  // first activation of the task's segment
+        dtask_acc(T, as_sh + base / 4, ah_sh + base / 32, routed ? CHk : CHs,
+                  routed ? t - k * CHk : t - nrt, routed ? w_s[k] : 1.0f, acc);
+      }
+    }
   } else {
+    // 3. shared activations once the S blocks are published, shared part
+    if (!a.nowait && !a.s_done &&
+        !block_wait_flags(flags, a.nS, epoch, ctlw, 2, sys, kPollWave, t))
+      return false;
+    stage_run(act_of(a, blockIdx.x % ctl::kRep), 0, Is, Is, as_sh, ah_sh, t);
+    __syncthreads();
     for (int c = t; c < CHs; c += kBlock) {
       DTask U;
       dtask_load(U, a.shd, row0, CHs, c);
       dtask_acc(U, as_sh, ah_sh, CHs, c, 1.0f, acc);
     }
-  }
-  // 4. one wait for the G blocks of all K experts, their activations in one
-  //    pass, routed part
-  if (!a.nowait &&
-      !block_wait_flags(flags + a.nS, K * a.perG, epoch, ctlw, 3, sys, kPollWave, t))
-    return false;
-  stage_run(act_of(a, blockIdx.x % ctl::kRep), Is, K * I, I, as_sh + Is / 4, ah_sh + Is / 32, t);
-  __syncthreads();
-  if (kOnePass) {
-    if (routed) {
-      const int k = t / CHk, c = t - k * CHk;
-      dtask_acc(T, ask + (size_t)k * I / 4, ahk + k * CHk, CHk, c, w_s[k], acc);
-    }
-  } else {
+    // 4. one wait for the G blocks of all K experts, their activations in
+    //    one pass, routed part
+    if (!a.nowait &&
+        !block_wait_flags(flags + a.nS, K * a.perG, epoch, ctlw, 3, sys, kPollWave, t))
+      return false;
+    stage_run(act_of(a, blockIdx.x % ctl::kRep), Is, K * I, I, as_sh + Is / 4, ah_sh + Is / 32, t);
+    __syncthreads();
     for (int u = t; u < nrt; u += kBlock) {
       const int k = u / CHk, c = u - k * CHk;
       DTask U;
