@@ -565,7 +565,7 @@ def gemv_leg(torch, q, sptr, rows: int = 65536, cols: int = 2816, copies: int = 
     """The standalone 4-bit affine GEMV (qmoe_gemv_affine4) on a large matrix
     of the decode width (rows x cols, seeded codes, scales ~U(0.005, 0.02),
     biases -8*scale), cycling through copies that together exceed the 256 MB
-    MALL.  One untimed round of `iters` back-to-back launches, then HIP
+    MALL.  Three untimed rounds of `iters` back-to-back launches, then HIP
     events around each of three such rounds (the median is reported); algorithmic bytes
     = codes + fp16 scales and biases + x + y.  Also a plain 512 MiB device
     copy, for context (bytes read + written per second)."""
@@ -594,9 +594,11 @@ def gemv_leg(torch, q, sptr, rows: int = 65536, cols: int = 2816, copies: int = 
             if rc:
                 raise q.QmoeError("qmoe_gemv_affine4", rc)
 
-    # the first few hundred launches over freshly allocated copies run ~12%
-    # slower: one untimed round, then three timed rounds (median reported)
-    launches()
+    # the first few hundred launches over freshly allocated copies run up to
+    # ~12% slower: three untimed rounds, then three timed rounds (median
+    # reported)
+    for _ in range(3):
+        launches()
     reps = []
     for _ in range(3):
         torch.cuda.synchronize()

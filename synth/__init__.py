@@ -86,6 +86,10 @@ WORKLOADS: Dict[str, Workload] = {
     # a prefill shape whose widths are not multiples of 128 (padded operand
     # rows) and whose counts are not powers of two
     "odd_prefill": Workload(9, "odd_prefill", 576, 24, 4, 192, 320, tokens=33),
+    # a decode layer whose expert count is not a multiple of the router's 8
+    # rows per block (its last router block has 5 rows), with odd widths
+    "odd_experts_decode": Workload(10, "odd_experts_decode", 576, 21, 4, 192, 320, tokens=3,
+                                   rmsnorm=True),
 }
 
 

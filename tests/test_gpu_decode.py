@@ -275,6 +275,21 @@ def test_moe_decode_end_to_end(torch_cuda, q, tiny_layer, big_layer, which, n):
         _check_decode_token(ol, X[t], got, gidx, gw, residual=bool(t % 2))
 
 
+def test_moe_decode_odd_expert_count(torch_cuda, q):
+    """E = 21 (the last router block holds 5 rows), H = 576, RMSNorm: the
+    one-launch step against the oracle, with and without the residual."""
+    torch = torch_cuda
+    wl = synth.WORKLOADS["odd_experts_decode"]
+    lw = synth.make_layer(wl, 0)
+    ol, dl = oracle.OracleLayer(lw), synth.device.DeviceLayer(lw)
+    X = synth.make_tokens(wl, wl.tokens, stream=23)
+    ws = dl.layer.new_workspace(1)
+    for t in range(wl.tokens):
+        log(f"decode odd experts token {t}")
+        got, gidx, gw = _decode(torch, q, dl, X[t], residual=bool(t % 2), ws=ws)
+        _check_decode_token(ol, X[t], got, gidx, gw, residual=bool(t % 2))
+
+
 def test_moe_decode_single_launch_equals_phased(torch_cuda, q, big_layer):
     """One launch with in-kernel waits and three ordered launches run the
     same arithmetic: outputs are bitwise equal, repeatedly."""
