@@ -90,6 +90,9 @@ WORKLOADS: Dict[str, Workload] = {
     # rows per block (its last router block has 5 rows), with odd widths
     "odd_experts_decode": Workload(10, "odd_experts_decode", 576, 21, 4, 192, 320, tokens=3,
                                    rmsnorm=True),
+    # the largest expert count the kernels take (512), narrow experts
+    "max_experts_decode": Workload(11, "max_experts_decode", 512, 512, 8, 64, 128, tokens=2,
+                                   rmsnorm=True),
 }
 
 

@@ -130,7 +130,8 @@ def _router(torch, q, Wr, X, K, bias=None):
     return idx.cpu().numpy(), w.cpu().numpy(), lg.cpu().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("wl,T", [(TINY, 3), (LAYER, 1), (LAYER, 37), (LAYER, 128)])
+@pytest.mark.parametrize("wl,T", [(TINY, 3), (LAYER, 1), (LAYER, 37), (LAYER, 128),
+                                  (synth.WORKLOADS["max_experts_decode"], 5)])
 def test_router_topk_parity(torch_cuda, q, wl, T):
     """GPU logits within the fp32 bound of the fp64 logits; GPU idx equal to
     the oracle's top-k of the GPU's own logits; weights its softmax."""
@@ -286,6 +287,22 @@ def test_moe_decode_odd_expert_count(torch_cuda, q):
     ws = dl.layer.new_workspace(1)
     for t in range(wl.tokens):
         log(f"decode odd experts token {t}")
+        got, gidx, gw = _decode(torch, q, dl, X[t], residual=bool(t % 2), ws=ws)
+        _check_decode_token(ol, X[t], got, gidx, gw, residual=bool(t % 2))
+
+
+def test_moe_decode_max_expert_count(torch_cuda, q):
+    """E = 512 (the most the kernels take; 64 router blocks, top-k over 8
+    values per lane), I = 64, Is = 128: widths with no compile-time
+    specialisation, whose down blocks take their tasks pass by pass."""
+    torch = torch_cuda
+    wl = synth.WORKLOADS["max_experts_decode"]
+    lw = synth.make_layer(wl, 0)
+    ol, dl = oracle.OracleLayer(lw), synth.device.DeviceLayer(lw)
+    X = synth.make_tokens(wl, wl.tokens, stream=25)
+    ws = dl.layer.new_workspace(1)
+    for t in range(wl.tokens):
+        log(f"decode max experts token {t}")
         got, gidx, gw = _decode(torch, q, dl, X[t], residual=bool(t % 2), ws=ws)
         _check_decode_token(ol, X[t], got, gidx, gw, residual=bool(t % 2))
 
