@@ -75,8 +75,34 @@ size_t prefill_ws_bytes(const qmoe_moe_layer& L, int T) {
   return pf_layout(L.n_experts, L.top_k, L.inter, L.shared_inter, L.hidden, T).total;
 }
 
+// ================================================================== prep
+// X bf16 [T][H] -> fp16 [T][pad128(H)], columns of each 8 reordered
+// (0,2,4,6,1,3,5,7), the padding zero.  Word v: 8 columns.
+__device__ __forceinline__ void pf_prep_word(const uint16_t* X, int T, int H, _Float16* xh, int v) {
+  const int H8 = H / 8, P8 = pad128(H) / 8;
+  const int t = v / P8, c8 = v - t * P8;
+  h8_t o;
+  if (c8 < H8) {
+    uint4 r = reinterpret_cast<const uint4*>(X)[t * H8 + c8];
+    uint32_t w[4] = {r.x, r.y, r.z, r.w};
+    float f[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_to_f32(w[i] & 0xffffu);
+      f[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+    const int order[8] = {0, 2, 4, 6, 1, 3, 5, 7};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (_Float16)f[order[i]];
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] = (_Float16)0.f;
+  }
+  reinterpret_cast<h8_t*>(xh)[v] = o;
+}
+
 // ============================================================== dispatch
-// One block of 1024 threads, thread p = flat pair index t*K + j (n <= 1024).
+// Block 0 (1024 threads): thread p = flat pair index t*K + j (n <= 1024).
 // rank of p among the pairs of its expert = pairs of the same expert in
 // earlier waves (per-wave counts, prefix over waves) + earlier lanes of its
 // wave with the same expert (ballot match on the bits of the expert id).
@@ -86,10 +112,18 @@ size_t prefill_ws_bytes(const qmoe_moe_layer& L, int T) {
 // first token), then the experts' chunks of kPfMaxM pair rows (row0 = first
 // sorted pair), experts in order of decreasing row count (ties: lower id
 // first), so that the longest blocks start first.
+// Blocks 1.. of the same launch prepare the A rows (independent work: the
+// chunk saves a launch).
 __global__ __launch_bounds__(1024) void k_pf_dispatch(const int32_t* idx, int n, int T, int E,
                                                       int32_t* counts, int32_t* offsets,
                                                       int32_t* perm, int32_t* pos_of,
-                                                      int32_t* items) {
+                                                      int32_t* items, const uint16_t* X, int H,
+                                                      _Float16* xh) {
+  if (blockIdx.x > 0) {
+    const int v = (blockIdx.x - 1) * 1024 + threadIdx.x;
+    if (v < T * (pad128(H) / 8)) pf_prep_word(X, T, H, xh, v);
+    return;
+  }
   __shared__ int32_t cnt[16][QMOE_MAX_EXPERTS];  // per-wave counts, then prefixes
   __shared__ int32_t off[QMOE_MAX_EXPERTS + 1];
   __shared__ int32_t tot[QMOE_MAX_EXPERTS];      // rows per expert
@@ -172,35 +206,6 @@ __global__ __launch_bounds__(1024) void k_pf_dispatch(const int32_t* idx, int n,
     }
   }
   if (p == 0) items[0] = nsh + ist[E];
-}
-
-// ================================================================== prep
-// X bf16 [T][H] -> fp16 [T][pad128(H)], columns of each 8 reordered
-// (0,2,4,6,1,3,5,7), the padding zero.  Thread v: 8 columns.
-__global__ __launch_bounds__(kBlock) void k_pf_prep(const uint16_t* X, int T, int H,
-                                                    _Float16* xh) {
-  const int H8 = H / 8, P8 = pad128(H) / 8;
-  const int v = blockIdx.x * kBlock + threadIdx.x;
-  if (v >= T * P8) return;
-  const int t = v / P8, c8 = v - t * P8;
-  h8_t o;
-  if (c8 < H8) {
-    uint4 r = reinterpret_cast<const uint4*>(X)[t * H8 + c8];
-    uint32_t w[4] = {r.x, r.y, r.z, r.w};
-    float f[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = bf16_to_f32(w[i] & 0xffffu);
-      f[2 * i + 1] = bf16_to_f32(w[i] >> 16);
-    }
-    const int order[8] = {0, 2, 4, 6, 1, 3, 5, 7};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = (_Float16)f[order[i]];
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] = (_Float16)0.f;
-  }
-  reinterpret_cast<h8_t*>(xh)[v] = o;
 }
 
 // ================================================================= GEMMs
@@ -714,12 +719,10 @@ qmoe_status launch_prefill(const qmoe_moe_layer& L, const uint16_t* X, int T, co
   a.y_sh = reinterpret_cast<float*>(pf + pl.y_sh);
   int32_t* pos_of = reinterpret_cast<int32_t*>(pf + pl.pos);
   a.items = reinterpret_cast<int32_t*>(pf + pl.items);
-  hipLaunchKernelGGL(k_pf_dispatch, dim3(1), dim3(1024), 0, S(stream), idx, T * K, T, E,
-                     counts, offsets, const_cast<int32_t*>(a.perm), pos_of,
-                     const_cast<int32_t*>(a.items));
-  const int n8 = T * pad128(H) / 8;
-  hipLaunchKernelGGL(k_pf_prep, dim3((n8 + kBlock - 1) / kBlock), dim3(kBlock), 0, S(stream), X, T,
-                     H, const_cast<_Float16*>(a.xh));
+  const int n8 = T * (pad128(H) / 8);
+  hipLaunchKernelGGL(k_pf_dispatch, dim3(1 + (n8 + 1023) / 1024), dim3(1024), 0, S(stream), idx,
+                     T * K, T, E, counts, offsets, const_cast<int32_t*>(a.perm), pos_of,
+                     const_cast<int32_t*>(a.items), X, H, const_cast<_Float16*>(a.xh));
   // 1-D grids over the work units; blocks past the last item return at once
   const int nsh = (T + kPfMaxM - 1) / kPfMaxM;
   const int nr = pf_max_items(E, K, T) - nsh;
