@@ -225,7 +225,8 @@ __device__ __forceinline__ DevQ devq_at(DevQ d, int64_t slot) {
 // hitting one line; consumer block b reads replica b % kRep.
 namespace ctl {
 constexpr int kError = 0;             // word: nonzero when an in-kernel wait gave up
-constexpr int kRep = 16;
+constexpr int kRep = 4;              // fewer stores per producer; more readers per replica
+                                      // (decode step: 4 beat 1, 2, 8 and 16)
 constexpr int kRepStride = 4352;      // bytes between replicas (4 KiB + 256)
 constexpr int kTagBase = 4096;        // byte offset of the tagged-logit replicas
 constexpr int kFlagBase = kTagBase + kRep * kRepStride;   // per-block flag replicas:

@@ -34,8 +34,8 @@
 // epoch (derived from the launch's dispatch-packet address, so it differs
 // from the previous call's without any reset); exchanged values travel as
 // device-coherent stores/loads; small values that many blocks poll (router
-// logits, flags, gate/up activations) are written in 16 replicas so that
-// pollers spread over memory channels.  No atomics, no cache fences.
+// logits, flags, gate/up activations) are written in a few replicas so
+// that pollers spread over memory channels.  No atomics, no cache fences.
 //
 // Every weight and scale load is unconditional (out-of-range chunks re-read
 // a valid address and only the arithmetic is predicated) and, for the model
