@@ -130,8 +130,8 @@ def main():
                     help="time the three-launch variant instead of the single launch")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only; multi-GPU runs are not "
-                          "part of it (--gpus must be 1)"}))
+        print(json.dumps({"error": "the MoE step runs on one GPU: --gpus must be 1 (the "
+                          "library has no multi-GPU path)"}))
         sys.exit(2)
 
     import torch

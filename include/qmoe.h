@@ -97,7 +97,7 @@ typedef struct {
   const float* logit_bias;
 } qmoe_moe_layer;
 
-/* Limits of this build (checked; larger sizes give QMOE_ERR_UNSUPPORTED). */
+/* Limits of the kernels (checked; larger sizes give QMOE_ERR_UNSUPPORTED). */
 #define QMOE_MAX_TOP_K 8
 #define QMOE_MAX_EXPERTS 512
 #define QMOE_MAX_HIDDEN 16384
