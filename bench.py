@@ -84,32 +84,47 @@ def measured_traffic():
 
 
 def host_threads() -> int:
+    """Threads the oracle may use: every core this process may run on."""
     try:
-        n = len(os.sched_getaffinity(0))
+        return max(1, len(os.sched_getaffinity(0)))
     except AttributeError:
-        n = os.cpu_count() or 1
-    return max(1, min(n, 16))
+        return max(1, os.cpu_count() or 1)
 
 
-def cpu_baseline(lw, X, seconds_hint: float = 15.0):
-    """The fp64 oracle (as it stands) over a bounded sample of tokens of the
-    same layer, threaded over tokens on the host cores."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(lw, X):
+    """The fp64 oracle (as it stands) on a bounded sample of tokens of the
+    same layer: one thread over a few tokens, then every host core (one
+    token per thread) over a larger sample."""
     import oracle
 
     L = oracle.OracleLayer(lw)
     cores = host_threads()
+    n1 = 6
     t0 = time.perf_counter()
-    L.forward(X[0])
-    one = time.perf_counter() - t0
-    n = int(max(cores, min(4 * cores, seconds_hint * cores / max(one, 1e-3))))
-    n = min(n, X.shape[0])
+    for t in range(n1):
+        L.forward(X[t])
+    one = n1 / (time.perf_counter() - t0)
+    n = min(X.shape[0], max(2 * cores, 32))
+    n = max(cores, n - n % cores) if n >= cores else n
     threads = min(cores, n)
     t0 = time.perf_counter()
     oracle.forward_many(L, X[:n], threads=threads)
     dt = time.perf_counter() - t0
     return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"{n} decode tokens of one layer (same shapes and weights), fp64 scalar C, "
-                      f"{threads} threads over tokens"}
+            "value_1thread": one, "cpu_model": cpu_model(), "host_cores": cores,
+            "sample": f"{n} decode tokens of one layer (same shapes and weights) on {threads} "
+                      f"threads, one token per thread; 1-thread figure over {n1} tokens; "
+                      f"fp64 scalar C oracle"}
 
 
 def main():
@@ -121,9 +136,9 @@ def main():
     ap.add_argument("--no-prefill", action="store_true", help="skip the prefill leg")
     ap.add_argument("--no-gemv", action="store_true", help="skip the standalone GEMV leg")
     ap.add_argument("--no-stack", action="store_true", help="skip the 30-layer stack leg")
-    ap.add_argument("--streaming", action="store_true",
-                    help="only the expert-streaming leg (30 layers, pinned host experts, "
-                         "16 device slots per layer); prints its own JSON line")
+    ap.add_argument("--no-streaming", action="store_true",
+                    help="skip the expert-streaming leg (30 layers, pinned host experts, "
+                         "16 device slots per layer)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
     ap.add_argument("--phased", action="store_true",
@@ -140,9 +155,6 @@ def main():
     import synth
     import synth.device as sd
 
-    if args.streaming:
-        print(json.dumps(streaming_leg(torch, q, synth, sd)), flush=True)
-        return
 
     wl = synth.WORKLOADS["layer_decode"]
     log("generating layer weights")
@@ -206,26 +218,30 @@ def main():
         if rc:
             raise q.QmoeError("qmoe_moe_decode", rc)
 
-    log("warmup")
-    for i in range(args.warmup):
+    # One untimed pass over every weight copy and every token, whatever
+    # --warmup says (the first launches on freshly allocated copies run
+    # slower), then the requested warmup steps.
+    log("warm pass over every weight copy and token, then warmup")
+    n_warm = max(COPIES, N_TOKENS) + args.warmup
+    for i in range(n_warm):
         step(i)
     torch.cuda.synchronize()
     if q.qmoe_workspace_status(ws) != 0:
         raise SystemExit("device wait failure during warmup")
 
-    # timed region: K steps in groups of SAMPLE consecutive launches.  The
-    # first launch of a group records a HIP event at its kernel's start and
-    # the last one at its kernel's end (the dispatches' own timestamps, on
-    # the launch stream); the launches in between are plain.  A group's span
-    # over SAMPLE is the average launch duration with the kernels running
-    # back to back, as a caller's would.  (A launch that records events
-    # costs the host about 29 us, more than the kernel takes: with events on
-    # every launch the loop would be host-bound.)  The three-launch variant
-    # is bracketed by event records every step.
+    # timed region: exactly K steps, in groups of up to SAMPLE consecutive
+    # launches.  The first launch of a group records a HIP event at its
+    # kernel's start and the last one at its kernel's end (the dispatches'
+    # own timestamps, on the launch stream); the launches in between are
+    # plain.  Sum of group spans over K is the average launch duration with
+    # the kernels running back to back, as a caller's would.  (A launch that
+    # records events costs the host about 29 us, more than the kernel takes:
+    # with events on every launch the loop would be host-bound.)  The
+    # three-launch variant is bracketed by event records every step.
     sample = 1 if args.phased else SAMPLE
-    K = max(sample, args.steps - args.steps % sample)
-    groups = K // sample
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * groups)]
+    K = max(1, args.steps)
+    groups = [(g0, min(sample, K - g0)) for g0 in range(0, K, sample)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * len(groups))]
     for e in ev:  # create the underlying hipEvents before the timed region
         e.record(stream)
     evh = [e.cuda_event for e in ev]
@@ -234,25 +250,26 @@ def main():
     if args.phased:
         for i in range(K):
             ev[2 * i].record(stream)
-            step(args.warmup + i)
+            step(n_warm + i)
             ev[2 * i + 1].record(stream)
     else:
-        for i in range(K):
-            n, r = divmod(i, sample)
-            e0 = evh[2 * n] if r == 0 else None
-            e1 = evh[2 * n + 1] if r == sample - 1 else None
-            if e0 or e1:
-                timed_step(args.warmup + i, e0, e1)
-            else:
-                plain_step(args.warmup + i)
+        for n, (g0, gs) in enumerate(groups):
+            for r in range(gs):
+                e0 = evh[2 * n] if r == 0 else None
+                e1 = evh[2 * n + 1] if r == gs - 1 else None
+                if e0 or e1:
+                    timed_step(n_warm + g0 + r, e0, e1)
+                else:
+                    plain_step(n_warm + g0 + r)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     code = q.qmoe_workspace_status(ws)
     if code != 0:
         raise SystemExit(f"device wait failure (code {code})")
-    kern_ms = np.array([ev[2 * n].elapsed_time(ev[2 * n + 1]) / sample for n in range(groups)])
-    kern_us = float(np.mean(kern_ms) * 1e3)
-    kern_med_us = float(np.median(kern_ms) * 1e3)
+    spans = np.array([ev[2 * n].elapsed_time(ev[2 * n + 1]) for n in range(len(groups))])
+    sizes = np.array([gs for _, gs in groups], dtype=np.float64)
+    kern_us = float(spans.sum() / sizes.sum() * 1e3)
+    kern_med_us = float(np.median(spans / sizes) * 1e3)
     elapsed = t1 - t0
     ms_per_step = elapsed * 1e3 / K
     tok_s = K / elapsed
@@ -286,22 +303,27 @@ def main():
                      "kernel": "k_moe_step (whole decode step)" if not args.phased else
                                "k_moe_step (three role launches)",
                      "kernel_us_mean": kern_us, "kernel_us_median": kern_med_us,
-                     "launch_us_basis": f"HIP events spanning {sample} consecutive launches, "
-                                        f"{groups} groups",},
+                     "launch_us_basis": f"HIP events spanning up to {sample} consecutive "
+                                        f"launches, {len(groups)} groups over the {K} timed "
+                                        f"steps, after {n_warm} untimed steps",},
     }
     if not args.no_prefill:
         res["prefill"] = prefill_leg(torch, q, synth, sd, lw, layers, wl, sptr)
     if not args.no_gemv:
         res["gemv"] = gemv_leg(torch, q, sptr)
+    del layers, cstructs
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     if not args.no_stack:
-        del layers
-        torch.cuda.empty_cache()
         res["stack"] = stack_leg(torch, q, synth, sd, sptr)
+    if not args.no_streaming:
+        res["streaming"] = streaming_leg(torch, q, synth, sd)
     if args.copy_calibration:
         copy_calibration(torch)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(lw, X)
+    torch.cuda.synchronize()
     print(json.dumps(res), flush=True)
 
 
@@ -454,6 +476,11 @@ def stack_leg(torch, q, synth, sd, sptr, tokens: int = 256, warmup: int = 8):
         raise SystemExit("device wait failure in the stack leg")
     kern_tok = np.array([ev[2 * t].elapsed_time(ev[2 * t + 1])
                          for t in range(0, tokens, SAMPLE)]) * 1e3
+    # release the stack's device objects (table, workspaces, events) before
+    # the next leg and before the interpreter exits
+    del stk, ev, ev1, evh, cl, dls, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     kern_token_us = float(kern_tok.mean())
     kern = kern_tok / n
     log(f"stack, one launch per layer: {tokens / wall:.0f} tokens/s, "
@@ -479,10 +506,17 @@ def streaming_leg(torch, q, synth, sd, steps: int = 512):
     """Expert-streaming decode: the 30-layer stack with every routed expert
     in pinned host memory and 16 device slots per layer.  Per layer:
     RMSNorm, router, routing to the host, shared gate/up while the pool
-    copies the missing experts on a side stream, then the routed part."""
+    copies the missing experts on a side stream, then the routed part.
+
+    Run three ways over the same tokens: all experts resident (no copies),
+    streamed with the copies overlapping the shared expert, and streamed
+    with every layer's copies finished before its shared expert starts (a
+    fresh pool: the same LFU decisions).  The overlap achieved is the part
+    of the copy time the overlapped run hides:
+    (t_serial - t_overlap) / (t_serial - t_resident)."""
     st = synth.WORKLOADS["streaming_decode"]
     L, E, K, H, S = st.layers, st.n_experts, st.top_k, st.hidden, st.slots
-    log(f"generating {L} layers into pinned host memory")
+    log(f"streaming: generating {L} layers into pinned host memory")
     lws = []
     host = None
     for l in range(L):
@@ -493,15 +527,9 @@ def streaming_leg(torch, q, synth, sd, steps: int = 512):
         host[l * E:(l + 1) * E].copy_(torch.from_numpy(lw.blobs))
         lw.blobs = lw.blobs[:1]  # the host copy now lives in pinned memory
         lws.append(lw)
-    arenas = [torch.zeros((S, blob), dtype=torch.uint8, device="cuda") for _ in range(L)]
-    dls = [sd.DeviceLayer(lw, blobs=arenas[l]) for l, lw in enumerate(lws)]
-    pool = q.Pool(L, E, S, blob, [host[i].data_ptr() for i in range(L * E)],
-                  [a.data_ptr() for a in arenas])
-    maps = [torch.zeros(E, dtype=torch.int32, device="cuda") for _ in range(L)]
     X = torch.from_numpy(synth.make_tokens(st, steps, stream=5).view(np.int16)).cuda()
     compute = torch.cuda.current_stream()
     copy = torch.cuda.Stream()
-    ws = dls[0].layer.new_workspace(1)
     rws = torch.zeros(q.qmoe_router_workspace_bytes(E, 1), dtype=torch.uint8, device="cuda")
     idx = torch.empty(K, dtype=torch.int32, device="cuda")
     w = torch.empty(K, dtype=torch.float32, device="cuda")
@@ -512,51 +540,99 @@ def streaming_leg(torch, q, synth, sd, steps: int = 512):
     ready = torch.cuda.Event()
     ready.record(copy)
 
-    def token(t):
-        x = X[t]
-        for l, dl in enumerate(dls):
-            Ly = dl.layer
-            q.qmoe_rmsnorm(x, dl.gamma, 1e-6, 1, H, h)
-            q.qmoe_router_topk(Ly.router, dl.logit_bias, h, 1, K, idx, w, None, rws)
-            idx_h.copy_(idx, non_blocking=True)
-            ev_idx.record(compute)
-            q.qmoe_expert_ffn_shared(Ly, h, ws)
-            ev_idx.synchronize()
-            s = pool.acquire(l, idx_h.data_ptr(), K, maps[l], copy, ready.cuda_event)
-            compute.wait_event(ready)
-            out = buf[l & 1]
-            q.qmoe_expert_ffn_routed(Ly, h, idx, w, maps[l], x, out, ws)
-            x = out
-        return s
+    def run(dls, pool, serial):
+        ws = dls[0].layer.new_workspace(1)
+        maps = [torch.zeros(E, dtype=torch.int32, device="cuda") for _ in range(L)]
+        half = None
 
-    t0 = time.perf_counter()
-    last = None
-    for t in range(steps):
-        s = token(t)
-        if t == steps // 2:
-            torch.cuda.synchronize()
-            last = (time.perf_counter(), s.hits, s.misses, s.h2d_bytes)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    s = pool.stats()
-    hits, misses = s.hits, s.misses
-    wh = (s.hits - last[1]) / max(1, (s.hits - last[1]) + (s.misses - last[2]))
-    warm_s = t1 - last[0]
-    warm_tokens = steps - steps // 2 - 1
-    res = {"metric": "expert-streaming stack decode tokens/s (pinned host experts, 16-slot LFU)",
-           "value": steps / (t1 - t0), "unit": "tokens/s", "n_gpus": 1, "steps": steps,
-           "higher_is_better": True, "dtype": "f32", "data": "synthetic (seeded)",
-           "config": {"workload": "30-layer MoE decode stack, batch 1, hidden 2816, 128 experts "
-                                  "per layer in pinned host memory, 16 device slots per layer, "
-                                  "Zipf(1.1) log-prior on the router logits"},
-           "hit_rate": hits / (hits + misses), "hit_rate_second_half": wh,
+        def token(t):
+            x = X[t]
+            for l, dl in enumerate(dls):
+                Ly = dl.layer
+                q.qmoe_rmsnorm(x, dl.gamma, 1e-6, 1, H, h)
+                q.qmoe_router_topk(Ly.router, dl.logit_bias, h, 1, K, idx, w, None, rws)
+                smap = None
+                if pool is not None:
+                    idx_h.copy_(idx, non_blocking=True)
+                    ev_idx.record(compute)
+                    if serial:
+                        ev_idx.synchronize()
+                        pool.acquire(l, idx_h.data_ptr(), K, maps[l], copy, ready.cuda_event)
+                        compute.wait_event(ready)
+                q.qmoe_expert_ffn_shared(Ly, h, ws)
+                if pool is not None:
+                    if not serial:
+                        ev_idx.synchronize()
+                        pool.acquire(l, idx_h.data_ptr(), K, maps[l], copy, ready.cuda_event)
+                        compute.wait_event(ready)
+                    smap = maps[l]
+                out = buf[l & 1]
+                q.qmoe_expert_ffn_routed(Ly, h, idx, w, smap, x, out, ws)
+                x = out
+
+        t0 = time.perf_counter()
+        for t in range(steps):
+            token(t)
+            if t == steps // 2 - 1:
+                torch.cuda.synchronize()
+                s = pool.stats() if pool is not None else None
+                half = (time.perf_counter(), s)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        if q.qmoe_workspace_status(ws) != 0:
+            raise SystemExit("device wait failure in the streaming leg")
+        return t0, half, t1
+
+    # resident: every expert of every layer on the device
+    res_dls = []
+    for l, lw in enumerate(lws):
+        blobs = host[l * E:(l + 1) * E].to("cuda")
+        res_dls.append(sd.DeviceLayer(lw, blobs=blobs))
+    t0, _, t1 = run(res_dls, None, False)
+    t_res = t1 - t0
+    del res_dls
+    torch.cuda.empty_cache()
+
+    arenas = [torch.zeros((S, blob), dtype=torch.uint8, device="cuda") for _ in range(L)]
+    dls = [sd.DeviceLayer(lw, blobs=arenas[l]) for l, lw in enumerate(lws)]
+    hp = [host[i].data_ptr() for i in range(L * E)]
+    ap = [a.data_ptr() for a in arenas]
+    out = {}
+    for serial in (False, True):
+        pool = q.Pool(L, E, S, blob, hp, ap)
+        t0, (th, sh), t1 = run(dls, pool, serial)
+        s = pool.stats()
+        pool.close()
+        out[serial] = (t0, th, sh, t1, s)
+    t0, th, sh, t1, s = out[False]
+    t_ovl = t1 - t0
+    t_ser = out[True][3] - out[True][0]
+    warm_tokens = steps - steps // 2
+    warm_s = t1 - th
+    whits, wmiss = s.hits - sh.hits, s.misses - sh.misses
+    res = {"workload": "30-layer MoE decode stack, batch 1, hidden 2816, 128 experts per layer "
+                       "in pinned host memory, 16 device slots per layer (LFU), Zipf(1.1) "
+                       "log-prior on the router logits",
+           "steps": steps, "tokens_per_s": steps / t_ovl,
+           "tokens_per_s_warm": warm_tokens / warm_s,
+           "hit_rate": s.hits / (s.hits + s.misses),
+           "hit_rate_warm": whits / max(1, whits + wmiss),
            "h2d_bytes": s.h2d_bytes,
-           "h2d_GBps": s.h2d_bytes / (t1 - t0) / 1e9,
-           "tokens_per_s_second_half": warm_tokens / warm_s,
-           "h2d_GBps_second_half": (s.h2d_bytes - last[3]) / warm_s / 1e9}
-    pool.close()
-    log(f"streaming: {res['value']:.1f} tokens/s, hit rate {res['hit_rate']:.3f}, "
-        f"H2D {res['h2d_GBps']:.1f} GB/s")
+           "h2d_GBps": s.h2d_bytes / t_ovl / 1e9,
+           "h2d_GBps_warm": (s.h2d_bytes - sh.h2d_bytes) / warm_s / 1e9,
+           "tokens_per_s_resident": steps / t_res,
+           "tokens_per_s_serialized_copies": steps / t_ser,
+           "overlap_achieved": (t_ser - t_ovl) / max(1e-9, t_ser - t_res),
+           "warm": f"second half of the run ({warm_tokens} tokens)",
+           "overlap_basis": "(t_serialized - t_overlapped) / (t_serialized - t_resident), "
+                            "same tokens and LFU decisions"}
+    log(f"streaming: {res['tokens_per_s']:.1f} tokens/s, hit rate {res['hit_rate']:.3f} "
+        f"(warm {res['hit_rate_warm']:.3f}), H2D {res['h2d_GBps']:.1f} GB/s, overlap "
+        f"{res['overlap_achieved']:.2f} (resident {res['tokens_per_s_resident']:.0f}, "
+        f"serialized {res['tokens_per_s_serialized_copies']:.0f} tokens/s)")
+    del dls, arenas, host
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     return res
 
 

@@ -19,7 +19,8 @@ import os
 from typing import Dict, Optional
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqmoe.so")
+# QMOE_LIB may name another build of the same library (the trace build)
+LIB_PATH = os.environ.get("QMOE_LIB") or os.path.join(_HERE, "libqmoe.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(
@@ -96,6 +97,8 @@ _lib.qmoe_workspace_bytes.argtypes = [C.POINTER(_Layer), C.c_int32]
 _lib.qmoe_router_workspace_bytes.restype = C.c_size_t
 _lib.qmoe_router_workspace_bytes.argtypes = [C.c_int32, C.c_int32]
 _lib.qmoe_workspace_status.argtypes = [_vp, C.c_size_t, C.POINTER(C.c_int32), _vp]
+_lib.qmoe_workspace_tag_counter.argtypes = [_vp, C.c_size_t, C.POINTER(C.c_uint32), _vp]
+_lib.qmoe_workspace_raise_tag_counter.argtypes = [_vp, C.c_size_t, C.c_uint32, _vp]
 _lib.qmoe_stack_table_bytes.restype = C.c_size_t
 _lib.qmoe_stack_table_bytes.argtypes = [C.c_int32]
 _lib.qmoe_stack_table_init.argtypes = [C.POINTER(_Layer), C.c_int32, _vp, C.c_size_t, _vp]
@@ -108,7 +111,8 @@ for _f in ("qmoe_gemv_affine4", "qmoe_router_topk", "qmoe_expert_ffn", "qmoe_moe
            "qmoe_workspace_status", "qmoe_prefill_dispatch_offsets", "qmoe_moe_decode_timed",
            "qmoe_expert_ffn_shared", "qmoe_expert_ffn_routed", "qmoe_pool_create",
            "qmoe_pool_plan", "qmoe_pool_acquire", "qmoe_pool_stats_get",
-           "qmoe_stack_table_init", "qmoe_stack_decode"):
+           "qmoe_stack_table_init", "qmoe_stack_decode", "qmoe_workspace_tag_counter",
+           "qmoe_workspace_raise_tag_counter"):
     getattr(_lib, _f).restype = C.c_int
 
 
@@ -400,6 +404,22 @@ def qmoe_workspace_status(ws, stream=None) -> int:
     return int(code.value)
 
 
+def qmoe_workspace_tag_counter(ws, stream=None) -> int:
+    """The workspace's tag counter (synchronises the stream)."""
+    v = C.c_uint32(0)
+    _check("qmoe_workspace_tag_counter",
+           _lib.qmoe_workspace_tag_counter(_ptr(ws), ws.numel() * ws.element_size(), C.byref(v),
+                                           _stream(stream)))
+    return int(v.value)
+
+
+def qmoe_workspace_raise_tag_counter(ws, value: int, stream=None) -> None:
+    """Test hook: raise the workspace's tag counter to `value`."""
+    _check("qmoe_workspace_raise_tag_counter",
+           _lib.qmoe_workspace_raise_tag_counter(_ptr(ws), ws.numel() * ws.element_size(),
+                                                 int(value), _stream(stream)))
+
+
 __all__ = [
     "QTensor", "MoeLayer", "QmoeError", "lib", "LIB_PATH",
     "qmoe_gemv_affine4", "qmoe_router_topk", "qmoe_expert_ffn", "qmoe_moe_decode",
@@ -407,7 +427,8 @@ __all__ = [
     "PoolStats", "qmoe_prefill_grouped", "qmoe_prefill_dispatch_offsets",
     "qmoe_rmsnorm",
     "qmoe_workspace_bytes",
-    "qmoe_router_workspace_bytes", "qmoe_workspace_status",
+    "qmoe_router_workspace_bytes", "qmoe_workspace_status", "qmoe_workspace_tag_counter",
+    "qmoe_workspace_raise_tag_counter",
     "qmoe_stack_table_bytes", "qmoe_stack_table_init", "qmoe_stack_workspace_bytes",
     "qmoe_stack_decode", "Stack",
 ]

@@ -1,6 +1,9 @@
 """Build libqmoe.so (the gfx950 HIP library behind include/qmoe.h) in-tree.
 
-    python -m bit_quantized_gemv_amd.build        # or build() from Python
+    python -m bit_quantized_gemv_amd.build          # or build() from Python
+    python -m bit_quantized_gemv_amd.build --trace  # libqmoe_trace.so: the same
+        library with per-block phase timestamps in the decode step kernel
+        (qmoe_trace_set); the binding loads it when QMOE_LIB names it
 """
 from __future__ import annotations
 
@@ -13,6 +16,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqmoe.so")
+TRACE_LIB = os.path.join(PKG, "libqmoe_trace.so")
 SOURCES = ["qmoe_api.hip", "qmoe_decode.hip", "qmoe_router.hip", "qmoe_prefill.hip", "qmoe_pool.hip"]
 ARCH = "gfx950"
 
@@ -33,13 +37,16 @@ def flags() -> list:
             "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, trace: bool = False) -> str:
     srcs = [os.path.join(CSRC, s) for s in SOURCES if os.path.exists(os.path.join(CSRC, s))]
+    out = TRACE_LIB if trace else LIB
+    extra = ["-DQMOE_TRACE"] if trace else []
+    tag = ".trace" if trace else ""
     objs = []
     procs = []
     for s in srcs:
-        o = os.path.join(CSRC, os.path.basename(s) + ".o")
-        cmd = [hipcc()] + flags() + ["-c", s, "-o", o]
+        o = os.path.join(CSRC, os.path.basename(s) + tag + ".o")
+        cmd = [hipcc()] + flags() + extra + ["-c", s, "-o", o]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((subprocess.Popen(cmd, stderr=subprocess.PIPE, text=True), s))
@@ -53,13 +60,13 @@ def build(verbose: bool = False) -> str:
             print(err, file=sys.stderr)
     if errs:
         raise RuntimeError("hipcc failed:\n" + "\n".join(errs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = out + ".tmp%d" % os.getpid()
     subprocess.check_call([hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     for o in objs:
         os.remove(o)
-    return LIB
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, trace="--trace" in sys.argv[1:]))

@@ -240,6 +240,38 @@ qmoe_status qmoe_workspace_status(void* ws, size_t ws_bytes, int32_t* device_cod
   return QMOE_OK;
 }
 
+qmoe_status qmoe_workspace_tag_counter(void* ws, size_t ws_bytes, uint32_t* value, void* stream) {
+  if (!ws || !value) return QMOE_ERR_NULL_ARG;
+  if (ws_bytes < kCtlBytes) return QMOE_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  uint32_t v[ctl::kGenRep];
+  for (int r = 0; r < ctl::kGenRep; ++r)
+    if (hipMemcpyAsync(&v[r], static_cast<uint8_t*>(ws) + ctl::kGenBase + ctl::kGenStride * r, 4,
+                       hipMemcpyDeviceToHost, st) != hipSuccess)
+      return QMOE_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return QMOE_ERR_HIP;
+  for (int r = 1; r < ctl::kGenRep; ++r)
+    if (v[r] != v[0]) return QMOE_ERR_DEVICE;
+  *value = v[0];
+  return QMOE_OK;
+}
+
+qmoe_status qmoe_workspace_raise_tag_counter(void* ws, size_t ws_bytes, uint32_t value,
+                                             void* stream) {
+  if (!ws) return QMOE_ERR_NULL_ARG;
+  if (ws_bytes < kCtlBytes) return QMOE_ERR_WORKSPACE;
+  uint32_t cur = 0;
+  qmoe_status s = qmoe_workspace_tag_counter(ws, ws_bytes, &cur, stream);
+  if (s != QMOE_OK) return s;
+  if (value < cur || value >= ctl::kGenLimit) return QMOE_ERR_BAD_SHAPE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  for (int r = 0; r < ctl::kGenRep; ++r)
+    if (hipMemcpyAsync(static_cast<uint8_t*>(ws) + ctl::kGenBase + ctl::kGenStride * r, &value, 4,
+                       hipMemcpyHostToDevice, st) != hipSuccess)
+      return QMOE_ERR_HIP;
+  return hipStreamSynchronize(st) == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
+}
+
 qmoe_status qmoe_moe_decode_timed(const qmoe_moe_layer* L, const uint16_t* x,
                                   const int32_t* expert_slot, int32_t residual, uint16_t* out,
                                   int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,

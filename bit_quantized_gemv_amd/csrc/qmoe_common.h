@@ -225,6 +225,17 @@ __device__ __forceinline__ DevQ devq_at(DevQ d, int64_t slot) {
 // hitting one line; consumer block b reads replica b % kRep.
 namespace ctl {
 constexpr int kError = 0;             // word: nonzero when an in-kernel wait gave up
+// Tag counter G of the workspace, in kGenRep replicas kGenStride bytes
+// apart (block b reads replica b % kGenRep).  A call whose flags and tags
+// are matched against the values v = G+1 .. G+n (one per layer) raises G by
+// n once every block of the call has read it, so every value a call waits
+// for is larger than any flag or tag already in the workspace.  A zero-
+// filled workspace starts at G = 0 (flags and tags 0).  Near the top of the
+// 32-bit range the control area is cleared instead and G restarts at 0.
+constexpr int kGenBase = 64;
+constexpr int kGenRep = 8;
+constexpr int kGenStride = 64;
+constexpr uint32_t kGenLimit = 0xFFFFFF00u;
 constexpr int kRep = 4;              // fewer stores per producer; more readers per replica
                                       // (decode step: 4 beat 1, 2, 8 and 16)
 constexpr int kRepStride = 4352;      // bytes between replicas (4 KiB + 256)
@@ -236,7 +247,10 @@ constexpr int kMaxFlags = kRepStride / 4;
 constexpr int kCntBase = kFlagBase + kRep * kRepStride;   // counters, 64 B apart
 constexpr int kCntRouterTile = 0;     // [16] standalone router: per token tile
 constexpr int kCntStack = 16;         // layer stack: output blocks done with the last layer
-constexpr int kNCnt = kCntStack + 1;
+constexpr int kCntDone = 17;          // [kGenRep] one-layer call: its last role's blocks done,
+                                      // per group (block index % kGenRep)
+constexpr int kCntDoneTop = kCntDone + kGenRep;  // groups done
+constexpr int kNCnt = kCntDoneTop + 1;
 constexpr int kBytes = kCntBase + kNCnt * 64;
 }  // namespace ctl
 constexpr size_t kCtlBytes = (size_t)ctl::kBytes;

@@ -31,11 +31,13 @@
 // reports a device error instead of hanging.
 //
 // Hand-offs: every producer block raises its own flag word to the call's
-// epoch (derived from the launch's dispatch-packet address, so it differs
-// from the previous call's without any reset); exchanged values travel as
-// device-coherent stores/loads; small values that many blocks poll (router
-// logits, flags, gate/up activations) are written in a few replicas so
-// that pollers spread over memory channels.  No atomics, no cache fences.
+// tag, a value of the workspace's tag counter that no earlier call has
+// used (the counter advances once every block of a call has read it);
+// exchanged values travel as device-coherent stores/loads; small values
+// that many blocks poll (router logits, flags, gate/up activations) are
+// written in a few replicas so that pollers spread over memory channels.
+// No cache fences; the only atomics are the completion counts that advance
+// the tag counter at the end of a call.
 //
 // Every weight and scale load is unconditional (out-of-range chunks re-read
 // a valid address and only the arithmetic is predicated) and, for the model
@@ -60,12 +62,41 @@ constexpr uint64_t kWaitTicks = 20000000ull;  // 0.2 s of the 100 MHz clock
 constexpr uint64_t kHoldTicks = 0;
 
 // LDS "sys" words at the start of every block's LDS
-constexpr int kSysEpoch = 0, kSysOk = 1, kSysIdx = 8, kSysW = 16, kSysRed = 32;
+constexpr int kSysOk = 1, kSysDone = 2, kSysIdx = 8, kSysW = 16, kSysRed = 32;
 constexpr int kSysSlot = 24;  // stacked position of each routed expert
 constexpr int kSysTkIdx = 96, kSysTkW = 160;  // per-wave top-k of the standalone router
 constexpr int kSysXch = 96;    // top-k exchange slots (2k 64-bit words) of the step roles
 constexpr int kSysWait = 184;  // stack kernel: 64-bit length of the last wait for a layer input
+constexpr int kSysTrace = 128; // trace builds: kNStamp 64-bit phase timestamps
+constexpr int kNStamp = 16;
 constexpr int kSysBytes = 768;
+
+// Trace builds (-DQMOE_TRACE) record per-block phase timestamps of the step
+// kernel: s_memrealtime values (the 100 MHz constant clock, the same on every
+// CU) kept in the block's LDS while it works, so that a stamp adds no memory
+// operation, and written out when the block ends to
+// qmoe_trace_buf[((G % slots) * blocks + block) * kNStamp + i] (G: the
+// call's tag counter).  Stamp i is taken by lane 0 of the wave that reaches
+// the phase named in the role that uses it (thread 0 takes every stamp);
+// unused stamps stay 0.
+#ifdef QMOE_TRACE
+__device__ uint64_t* qmoe_trace_buf;
+__device__ int qmoe_trace_slots;
+#define QMOE_STAMP(sys, i)                                                              \
+  do {                                                                                  \
+    if (threadIdx.x == 0)                                                               \
+      reinterpret_cast<uint64_t*>((sys) + kSysTrace)[i] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#else
+#define QMOE_STAMP(sys, i) \
+  do {                     \
+  } while (0)
+#endif
+// Stamps: 0 block start; 1 first weight loads issued; 2 input staged (R, S,
+// G) / routing known (D); 3 routing known (G) / logits published (R) /
+// shared flags seen (D); 4 computed (S, G) / shared staged (D); 5 published
+// (S, G) / routed flags seen (D); 6 routed staged (D); 7 combined (D);
+// 8 output stored (D); 9 done counted (D, S of a shared-only call).
 
 __host__ __device__ inline size_t al16(size_t n) { return (n + 15) & ~(size_t)15; }
 
@@ -93,7 +124,10 @@ struct DecodeArgs {
   int s_done;               // 1: the S blocks ran in an earlier launch
   int dwait;                // stack: output blocks of the previous layer to wait for
   uint32_t dtag;            // stack: their flag value
+  int cnt;                  // role whose blocks count the call done: kCntNone/S/D
+  uint32_t ntags;           // tag values the call uses (advance of the tag counter)
 };
+constexpr int kCntNone = 0, kCntS = 1, kCntD = 2;
 
 __device__ __forceinline__ uint32_t* ctl_of(const DecodeArgs& a) {
   return reinterpret_cast<uint32_t*>(a.ws + a.wl.ctl);
@@ -111,19 +145,73 @@ __device__ __forceinline__ float* act_of(const DecodeArgs& a, int r) {
 }
 
 // --------------------------------------------------------------- waits
-// The epoch of a one-layer call: every launch is a new packet of its queue,
-// so the packet's address differs from the previous launch's and is the
-// same for all of the launch's blocks.  Every flag and tag is rewritten by
-// every call, so only the previous call's values can be present when one
-// starts.  Epochs are odd; the layers of a stack call use even tags.
-__device__ __forceinline__ uint32_t launch_epoch() {
-  return ((uint32_t)(reinterpret_cast<uintptr_t>(__builtin_amdgcn_dispatch_ptr()) >> 6) << 1) | 1u;
+// The workspace's tag counter G (see ctl::kGenBase): a one-layer call
+// matches its flags and tags against G + 1, a stack call layer l's against
+// G + 1 + l.  Every value ever written to a flag or tag of the workspace
+// is <= G, so stale words never match.  Read device-coherently from this
+// block's replica.
+__device__ __forceinline__ uint32_t load_gen(const uint8_t* ws, size_t ctl_off) {
+  return ld_dev(reinterpret_cast<const uint32_t*>(ws + ctl_off + ctl::kGenBase +
+                                                  ctl::kGenStride * (blockIdx.x % ctl::kGenRep)));
 }
 
-// Tag of layer l of a stack call: even and nonzero.  A stack call leaves
-// every flag and tag at zero when it completes, so the tags of its layers
-// only have to differ from each other and from the odd one-layer epochs.
-__device__ __forceinline__ uint32_t stack_tag(int l) { return 2u * (uint32_t)(l + 1); }
+// Zero every flag and tag replica and restart the tag counter (the counter
+// is about to leave its range).  Only the last block of a call runs this,
+// when no block of the call reads the control area any more.
+__device__ void ctl_restart(uint8_t* ws, size_t ctl_off, int E, int tid = threadIdx.x) {
+  uint8_t* c = ws + ctl_off;
+  for (int r = 0; r < ctl::kRep; ++r) {
+    uint64_t* tg = reinterpret_cast<uint64_t*>(c + ctl::kTagBase + (size_t)r * ctl::kRepStride);
+    uint32_t* fl = reinterpret_cast<uint32_t*>(c + ctl::kFlagBase + (size_t)r * ctl::kRepStride);
+    for (int i = tid; i < E; i += kBlock) st_dev(tg + i, (uint64_t)0);
+    for (int i = tid; i < ctl::kMaxFlags; i += kBlock) st_dev(fl + i, 0u);
+  }
+  wait_vm();
+  __syncthreads();
+  if (tid < ctl::kGenRep)
+    st_dev(reinterpret_cast<uint32_t*>(c + ctl::kGenBase + ctl::kGenStride * tid), 0u);
+}
+
+// The call's tags are used up: G += n in every replica, or a restart when G
+// would leave its range.  Whole block, by its last block only.
+__device__ void gen_advance(uint8_t* ws, size_t ctl_off, int E, uint32_t gen, uint32_t n,
+                            int tid = threadIdx.x) {
+  if (gen + n >= ctl::kGenLimit) {
+    ctl_restart(ws, ctl_off, E, tid);
+    return;
+  }
+  if (tid < ctl::kGenRep)
+    st_dev(reinterpret_cast<uint32_t*>(ws + ctl_off + ctl::kGenBase + ctl::kGenStride * tid),
+           gen + n);
+}
+
+// Block i of the n blocks of the role whose completion ends a one-layer
+// call (every block of the call has read the tag counter when all of them
+// are done): count it; the last one advances the counter by the call's
+// tags.  Counters per group of blocks (i % kGenRep), then one for the
+// groups, so that few atomics meet on one address.  Whole block.
+__device__ void call_done(const DecodeArgs& a, int i, int n, uint32_t gen, uint32_t* sys,
+                          int tid = threadIdx.x) {
+  if (tid == 0) {
+    uint8_t* c = a.ws + a.wl.ctl + ctl::kCntBase;
+    const int g = i % ctl::kGenRep;
+    const uint32_t ng = (uint32_t)((n - g + ctl::kGenRep - 1) / ctl::kGenRep);
+    const uint32_t ngroups = (uint32_t)min(n, ctl::kGenRep);
+    uint32_t* cg = reinterpret_cast<uint32_t*>(c + 64 * (ctl::kCntDone + g));
+    uint32_t last = 0;
+    if (add_dev(cg, 1u) == ng - 1) {
+      st_dev(cg, 0u);
+      uint32_t* top = reinterpret_cast<uint32_t*>(c + 64 * ctl::kCntDoneTop);
+      if (add_dev(top, 1u) == ngroups - 1) {
+        st_dev(top, 0u);
+        last = 1;
+      }
+    }
+    sys[kSysDone] = last;
+  }
+  __syncthreads();
+  if (sys[kSysDone]) gen_advance(a.ws, a.wl.ctl, a.E, gen, a.ntags, tid);
+}
 
 // One full wave: wait until flags[0..n) all equal `epoch`.  Every poll reads
 // all n flags at once (a few loads per lane), so the wait ends one round
@@ -770,6 +858,7 @@ __device__ bool role_router(const DecodeArgs& a, int b, uint8_t* smem, uint32_t 
   } else {
     s = router_token<HC / 16>(a.router, row0, a.E, H, a.x, a.gamma, a.eps, xr, xh, red);
   }
+  QMOE_STAMP(sys, 2);
   if (tid < 8) {
     int e = min(row0 + tid, a.E - 1);
     if (a.lbias) s += gptr(a.lbias)[e];
@@ -782,6 +871,7 @@ __device__ bool role_router(const DecodeArgs& a, int b, uint8_t* smem, uint32_t 
     uint64_t v = ((uint64_t)epoch << 32) | __float_as_uint(reinterpret_cast<float*>(sys + kSysLg)[j]);
     st_dev(reinterpret_cast<uint64_t*>(rep_of(a, ctl::kTagBase, rep)) + row0 + j, v);
   }
+  QMOE_STAMP(sys, 3);
   return true;
 }
 
@@ -831,6 +921,7 @@ __device__ bool role_gate_up(const DecodeArgs& a, int expert_rank, int rb, int r
     bool ok = true;
     rows4_run<2, HC / 64>(m, row0, rows, H, half * CWh, CWh, xs, xh, sbl,
                           [&] {
+                            QMOE_STAMP(sys, 1);
                             if constexpr (STK) {
                               ok = wait_prev_layer(a, sys, 0, tid);
                               x_load_dev(X, a.x, H, tid);
@@ -838,6 +929,7 @@ __device__ bool role_gate_up(const DecodeArgs& a, int expert_rank, int rb, int r
                             float inv = a.gamma ? x_inv_rms(X, a.x, H, a.eps, red, tid) : 1.f;
                             x_stage<true>(X, a.x, a.gamma, inv, H, xs, xh, tid);
                             __syncthreads();
+                            QMOE_STAMP(sys, 2);
                           },
                           acc, tid);
     if (!ok) return false;
@@ -850,13 +942,17 @@ __device__ bool role_gate_up(const DecodeArgs& a, int expert_rank, int rb, int r
     float inv = a.gamma ? x_inv_rms(X, a.x, H, a.eps, red, tid) : 1.f;
     x_stage<true>(X, a.x, a.gamma, inv, H, xs, xh, tid);
     __syncthreads();
+    QMOE_STAMP(sys, 2);
     if (!block_routing<NV>(a, epoch, sys, false, tid)) return false;
+    QMOE_STAMP(sys, 3);
     const int s = reinterpret_cast<int32_t*>(sys + kSysSlot)[expert_rank];
     m[0] = devq_at(mi ? a.up : a.gate, s);
     m[1] = rows_below(m[0], H);
     dst = (size_t)a.Is + (size_t)expert_rank * a.I;
-    rows4_run<2, HC / 64>(m, row0, rows, H, half * CWh, CWh, xs, xh, sbl, [] {}, acc, tid);
+    rows4_run<2, HC / 64>(m, row0, rows, H, half * CWh, CWh, xs, xh, sbl,
+                          [&] { QMOE_STAMP(sys, 1); }, acc, tid);
   }
+  QMOE_STAMP(sys, 4);
   if ((lane >> 3) == 0) {
     red[(wave * 2 + 0) * 8 + (lane & 7)] = acc[0];
     red[(wave * 2 + 1) * 8 + (lane & 7)] = acc[1];
@@ -1038,8 +1134,10 @@ __device__ bool role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
   // 1. shared-down weights
   hold_until(t_start, kHoldTicks);
   if (kOnePass && !routed) dtask_load(T, a.shd, row0, CHs, min(t - nrt, CHs - 1));
+  QMOE_STAMP(sys, 1);
   // 2. routing, then at once the routed-down weights
   if (!block_routing<NV>(a, epoch, sys, b == 0, t)) return false;
+  QMOE_STAMP(sys, 2);
   const int32_t* slot_s = reinterpret_cast<const int32_t*>(sys + kSysSlot);
   const float* w_s = reinterpret_cast<const float*>(sys + kSysW);
   if (kOnePass && routed) {
@@ -1059,10 +1157,12 @@ __device__ bool role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
           !block_wait_flags(flags + (p ? a.nS : 0), p ? K * a.perG : a.nS, epoch, ctlw, 2 + p, sys,
                             kPollWave, t))
         return false;
+      QMOE_STAMP(sys, 3 + 2 * p);
       const int off = p ? Is : 0;
       stage_run(act_of(a, blockIdx.x % ctl::kRep), off, p ? K * I : Is, p ? I : Is,
                 as_sh + off / 4, ah_sh + off / 32, t);
       __syncthreads();
+      QMOE_STAMP(sys, 4 + 2 * p);
       // the weights as if reloaded per pass: their decoded forms are not
       // hoisted out of the loop and held in registers across both passes
 #pragma unroll
@@ -1104,6 +1204,7 @@ __device__ bool role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
   }
   // 5. combine: rows over the block, residual, bf16
   float s = rows8_block_sum(acc, red, t);
+  QMOE_STAMP(sys, 7);
   if constexpr (STK) {
     uint32_t o = 0;
     if (t < kRowsPerUnit) {
@@ -1124,31 +1225,60 @@ __device__ bool role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
       a.out[rr] = f32_to_bf16(s);
     }
   }
+  QMOE_STAMP(sys, 8);
   return true;
 }
 
 // EC: number of experts when known at compile time (0: up to 512).
+#ifdef QMOE_TRACE
+__device__ void trace_flush(uint32_t* sys, uint32_t gen) {
+  __syncthreads();
+  if (qmoe_trace_buf && threadIdx.x < kNStamp) {
+    const size_t slot = gen % (uint32_t)qmoe_trace_slots;
+    qmoe_trace_buf[(slot * gridDim.x + blockIdx.x) * kNStamp + threadIdx.x] =
+        reinterpret_cast<uint64_t*>(sys + kSysTrace)[threadIdx.x];
+  }
+}
+#endif
+
 template <int HC, int IC, int ISC, int EC>
 __global__ __launch_bounds__(kBlock) void k_moe_step(DecodeArgs a) {
   constexpr int NV = EC ? cdiv(EC, 64) : QMOE_MAX_EXPERTS / 64;
   extern __shared__ __align__(16) uint8_t smem[];
+  uint32_t* sys = reinterpret_cast<uint32_t*>(smem);
   const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
-  const uint32_t epoch = launch_epoch();
+#ifdef QMOE_TRACE
+  if (threadIdx.x < kNStamp) reinterpret_cast<uint64_t*>(sys + kSysTrace)[threadIdx.x] = 0;
+  QMOE_STAMP(sys, 0);
+#endif
+  const uint32_t gen = load_gen(a.ws, a.wl.ctl);
+  const uint32_t epoch = gen + 1;
   const int rb = a.role0 + blockIdx.x;
   if (rb < a.nR) {
     role_router<HC, false>(a, rb, smem, epoch);
   } else if (rb < a.nR + a.nS) {
     const int s = rb - a.nR;
-    role_gate_up<HC, NV, false>(a, -1, s, ISC ? ISC : a.Is, smem, epoch, t_start);
+    // (a block whose wait gave up publishes all the same, so that its
+    // consumers end at once; the error word marks the call as failed)
+    const bool ok = role_gate_up<HC, NV, false>(a, -1, s, ISC ? ISC : a.Is, smem, epoch, t_start);
     block_publish(a, s, epoch);
+    QMOE_STAMP(sys, 5);
+    if (ok && a.cnt == kCntS) call_done(a, s, a.nS, gen, sys);
   } else if (rb < a.nR + a.nS + a.nG) {
     const int gb = rb - a.nR - a.nS;
     role_gate_up<HC, NV, false>(a, gb / a.perG, gb % a.perG, IC ? IC : a.I, smem, epoch, t_start);
     block_publish(a, a.nS + gb, epoch);
+    QMOE_STAMP(sys, 5);
   } else {
     uint32_t held = 0;
-    role_down<IC, ISC, NV, false>(a, rb - a.nR - a.nS - a.nG, smem, epoch, t_start, held, nullptr);
+    const int d = rb - a.nR - a.nS - a.nG;
+    if (!role_down<IC, ISC, NV, false>(a, d, smem, epoch, t_start, held, nullptr)) return;
+    if (a.cnt == kCntD) call_done(a, d, a.nD, gen, sys);
   }
+#ifdef QMOE_TRACE
+  QMOE_STAMP(sys, 9);
+  trace_flush(sys, gen);
+#endif
 }
 
 // ============================================================ layer stack
@@ -1168,7 +1298,7 @@ __global__ __launch_bounds__(kBlock) void k_moe_step(DecodeArgs a) {
 // buffers, the tags.
 __device__ __forceinline__ void stack_layer_args(DecodeArgs& a, const DecodeArgs& a0,
                                                  const StackLayerDev* tab, int l, int L,
-                                                 uint16_t* xb, int H) {
+                                                 uint16_t* xb, int H, uint32_t tag0) {
   a = a0;
   const StackLayerDev& T = tab[l];
   a.router = T.router; a.gate = T.gate; a.up = T.up; a.down = T.down;
@@ -1180,7 +1310,7 @@ __device__ __forceinline__ void stack_layer_args(DecodeArgs& a, const DecodeArgs
   a.idx_out = a0.idx_out ? a0.idx_out + (size_t)l * a0.K : nullptr;
   a.w_out = a0.w_out ? a0.w_out + (size_t)l * a0.K : nullptr;
   a.dwait = l ? a0.nD : 0;
-  a.dtag = stack_tag(l - 1);
+  a.dtag = tag0 + (uint32_t)l - 1u;
 }
 
 template <int HC, int IC, int ISC, int EC>
@@ -1196,60 +1326,65 @@ __global__ __launch_bounds__(kBlock, 4) void k_moe_stack(DecodeArgs a0,
   const int rb = blockIdx.x;
   const int H = HC ? HC : a0.H;
   const int nRSG = a0.nR + a0.nS + a0.nG;
+  // layer l's flags and tags carry G + 1 + l
+  const uint32_t gen = load_gen(a0.ws, a0.wl.ctl);
+  const uint32_t tag0 = gen + 1;
   if (threadIdx.x == 0) *reinterpret_cast<uint64_t*>(sys + kSysWait) = 0;
   DecodeArgs a;
   // every role runs its own loop over the layers
   if (rb < a0.nR) {
     for (int l = 0; l < L; ++l) {
-      stack_layer_args(a, a0, tab, l, L, xb, H);
+      stack_layer_args(a, a0, tab, l, L, xb, H, tag0);
       __syncthreads();  // the previous layer's LDS contents are consumed
       int b = rb;
       opaque_s(b);
-      if (!role_router<HC, true>(a, b, smem, stack_tag(l))) return;
+      if (!role_router<HC, true>(a, b, smem, tag0 + (uint32_t)l)) return;
     }
     return;
   }
   if (rb < a0.nR + a0.nS) {
     const int sb = rb - a0.nR;
     for (int l = 0; l < L; ++l) {
-      stack_layer_args(a, a0, tab, l, L, xb, H);
+      stack_layer_args(a, a0, tab, l, L, xb, H, tag0);
       __syncthreads();
       int b = sb;
       opaque_s(b);
-      if (!role_gate_up<HC, NV, true>(a, -1, b, ISC ? ISC : a.Is, smem, stack_tag(l), t_start))
+      if (!role_gate_up<HC, NV, true>(a, -1, b, ISC ? ISC : a.Is, smem, tag0 + (uint32_t)l,
+                                      t_start))
         return;
-      block_publish(a, sb, stack_tag(l), opaque_tid());
+      block_publish(a, sb, tag0 + (uint32_t)l, opaque_tid());
     }
     return;
   }
   if (rb < nRSG) {
     const int gb = rb - a0.nR - a0.nS;
     for (int l = 0; l < L; ++l) {
-      stack_layer_args(a, a0, tab, l, L, xb, H);
+      stack_layer_args(a, a0, tab, l, L, xb, H, tag0);
       __syncthreads();
       int b = gb;
       opaque_s(b);
       if (!role_gate_up<HC, NV, true>(a, b / a.perG, b % a.perG, IC ? IC : a.I, smem,
-                                      stack_tag(l), t_start))
+                                      tag0 + (uint32_t)l, t_start))
         return;
-      block_publish(a, a.nS + gb, stack_tag(l), opaque_tid());
+      block_publish(a, a.nS + gb, tag0 + (uint32_t)l, opaque_tid());
     }
     return;
   }
   const int d = rb - nRSG;
   uint32_t held = 0;
   for (int l = 0; l < L; ++l) {
-    stack_layer_args(a, a0, tab, l, L, xb, H);
+    stack_layer_args(a, a0, tab, l, L, xb, H, tag0);
     __syncthreads();
     int b = d;
     opaque_s(b);
-    if (!role_down<IC, ISC, NV, true>(a, b, smem, stack_tag(l), t_start, held,
+    if (!role_down<IC, ISC, NV, true>(a, b, smem, tag0 + (uint32_t)l, t_start, held,
                                       lout ? lout + (size_t)l * H : nullptr))
       return;
     // the last layer's outputs have no reader inside the launch
-    if (l < L - 1) block_publish(a, a.nS + a.nG + d, stack_tag(l), opaque_tid());
+    if (l < L - 1) block_publish(a, a.nS + a.nG + d, tag0 + (uint32_t)l, opaque_tid());
   }
-  // output blocks: count the finished ones; the last clears the control area
+  // output blocks: count the finished ones; the last advances the tag
+  // counter past this call's layers
   wait_vm();
   __syncthreads();
   uint32_t* cnt = reinterpret_cast<uint32_t*>(a0.ws + a0.wl.ctl + ctl::kCntBase +
@@ -1260,18 +1395,26 @@ __global__ __launch_bounds__(kBlock, 4) void k_moe_stack(DecodeArgs a0,
   }
   __syncthreads();
   if (!sys[kSysOk]) return;
-  const int nflag = a0.nS + a0.nG + a0.nD;
-  for (int r = 0; r < ctl::kRep; ++r) {
-    uint64_t* tg = reinterpret_cast<uint64_t*>(rep_of(a0, ctl::kTagBase, r));
-    uint32_t* fl = reinterpret_cast<uint32_t*>(rep_of(a0, ctl::kFlagBase, r));
-    for (int i = threadIdx.x; i < a0.E; i += kBlock) st_dev(tg + i, (uint64_t)0);
-    for (int i = threadIdx.x; i < nflag; i += kBlock) st_dev(fl + i, 0u);
-  }
   if (threadIdx.x == 0) st_dev(cnt, 0u);
+  gen_advance(a0.ws, a0.wl.ctl, a0.E, gen, (uint32_t)L);
 }
 
 // ======================================================== host launchers
 static hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+#ifdef QMOE_TRACE
+}  // namespace qmoe
+// Trace builds only: where the step kernel writes its phase stamps (device
+// buffer of slots * blocks * 16 uint64; NULL turns tracing off).
+extern "C" qmoe_status qmoe_trace_set(void* buf, int32_t slots) {
+  if (slots < 1) return QMOE_ERR_BAD_SHAPE;
+  if (hipMemcpyToSymbol(HIP_SYMBOL(qmoe::qmoe_trace_buf), &buf, sizeof(buf)) != hipSuccess ||
+      hipMemcpyToSymbol(HIP_SYMBOL(qmoe::qmoe_trace_slots), &slots, sizeof(slots)) != hipSuccess)
+    return QMOE_ERR_HIP;
+  return QMOE_OK;
+}
+namespace qmoe {
+#endif
 
 qmoe_status launch_gemv4(const qmoe_qtensor& W, const uint16_t* x, float* y, void* stream) {
   const int units = cdiv(W.rows, kRowsPerUnit);
@@ -1372,9 +1515,16 @@ qmoe_status launch_moe_step(const qmoe_moe_layer& L, const uint16_t* x, const in
   const size_t lds = step_lds(a.H, a.E, a.I, a.Is, a.K);
   a.nowait = phased;
   a.s_done = 0;
+  a.dwait = 0;
+  a.dtag = 0;
+  // one tag per call; the blocks of the call's last role advance the
+  // workspace's tag counter when all of them are done
+  a.ntags = 1;
+  a.cnt = kCntD;
   if (mode == kStepShared || mode == kStepRouted) {
     if (mode == kStepRouted && !idx_in) return QMOE_ERR_NULL_ARG;
     if (mode == kStepShared) {
+      a.cnt = kCntS;
       a.role0 = a.nR;
       launch_step(a, a.nS, lds, stream, e0, e1);
     } else {
@@ -1389,7 +1539,9 @@ qmoe_status launch_moe_step(const qmoe_moe_layer& L, const uint16_t* x, const in
     launch_step(a, a.nR + a.nS + a.nG + a.nD, lds, stream, e0, e1);
     return hipGetLastError() == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
   }
-  // router; shared + routed gate/up; down (waits are then satisfied on entry)
+  // router; shared + routed gate/up; down (waits are then satisfied on
+  // entry).  The three launches share the call's tag; the last advances it.
+  a.cnt = kCntNone;
   if (a.nR) {
     a.role0 = 0;
     launch_step(a, a.nR, lds, stream, e0, nullptr);
@@ -1397,6 +1549,7 @@ qmoe_status launch_moe_step(const qmoe_moe_layer& L, const uint16_t* x, const in
   }
   a.role0 = a.nR;
   launch_step(a, a.nS + a.nG, lds, stream, e0, nullptr);
+  a.cnt = kCntD;
   a.role0 = a.nR + a.nS + a.nG;
   launch_step(a, a.nD, lds, stream, nullptr, e1);
   return hipGetLastError() == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;

@@ -210,6 +210,24 @@ size_t qmoe_router_workspace_bytes(int32_t n_experts, int32_t T);
 qmoe_status qmoe_workspace_status(void* ws, size_t ws_bytes, int32_t* device_code,
                                   void* stream);
 
+/* The workspace's tag counter.  Cross-block hand-offs inside a decode call
+ * match flag and tag words against values above every value already in
+ * the workspace: a one-layer call (qmoe_moe_decode, _timed, _phased,
+ * qmoe_expert_ffn, the split FFN calls) uses counter + 1, a stack call of n
+ * layers counter + 1 .. counter + n, and the call's last block raises the
+ * counter by that many once every block of the call has read it.  So no
+ * word left by an earlier call, of any shape or mode, matches a later
+ * call's, whatever else ran in between.  A zero-filled workspace starts at
+ * 0; near the top of the 32-bit range the last block zeroes every flag and
+ * tag and restarts the counter at 0.
+ * qmoe_workspace_tag_counter reads it (synchronising `stream`; all replicas
+ * must agree, else QMOE_ERR_DEVICE).  qmoe_workspace_raise_tag_counter sets
+ * it to `value` (test hook; only raising is allowed, and only below the
+ * restart threshold 0xFFFFFF00, else QMOE_ERR_BAD_SHAPE). */
+qmoe_status qmoe_workspace_tag_counter(void* ws, size_t ws_bytes, uint32_t* value, void* stream);
+qmoe_status qmoe_workspace_raise_tag_counter(void* ws, size_t ws_bytes, uint32_t value,
+                                             void* stream);
+
 const char* qmoe_status_string(qmoe_status s);
 
 /* ---------------------------------------------------------------------

@@ -74,6 +74,10 @@ WORKLOADS: Dict[str, Workload] = {
     "streaming_decode": Workload(5, "streaming_decode", 2816, 128, 8, 704, 2112,
                                  layers=30, tokens=512, rmsnorm=True, zipf=True,
                                  slots=16),
+    # the first 3 layers of the streaming stack (same seeds, full shapes),
+    # 16 steps: pool parity at the real sizes
+    "streaming_decode_3l": Workload(5, "streaming_decode_3l", 2816, 128, 8, 704, 2112,
+                                    layers=3, tokens=16, rmsnorm=True, zipf=True, slots=16),
     # small-shape version of the streaming stack, for parity tests
     "tiny_streaming_decode": Workload(6, "tiny_streaming_decode", 512, 32, 8, 256, 512,
                                       layers=3, tokens=12, rmsnorm=True, zipf=True, slots=16),

@@ -72,6 +72,84 @@ def gemv8_bound(m, x: np.ndarray) -> np.ndarray:
     return gamma_n(64 + m.cols // 16) * M
 
 
+def _abs_dequant(m) -> np.ndarray:
+    """|W| of a QMat as fp64 [rows][cols] (from the byte-view codes)."""
+    q = codes_of(m)
+    s = np.repeat(m.s.view(np.float16).astype(np.float64), 64, axis=1)
+    b = np.repeat(m.b.view(np.float16).astype(np.float64), 64, axis=1)
+    return np.abs(s * q + b)
+
+
+def _bf16_step(v: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 numbers at |v| (the subnormal quantum below 2^-126)."""
+    a = np.maximum(np.abs(v), 2.0**-126)
+    return np.exp2(np.floor(np.log2(a)) - 7)
+
+
+def routing_bound(router, x_bits, logits64, gamma=None, eps: float = 1e-6) -> np.ndarray:
+    """Per-expert bound on |device logit - fp64 logit| for one token.
+
+    The device computes the router GEMV in fp32 (bounded by gemv8_bound) and
+    adds the logit bias with one more fp32 rounding (|l| * 2^-24; doubled for
+    the fp32 representation of the fp64 reference).  With an RMSNorm in front
+    (gamma given, x the layer input), the device's bf16 expert input may sit
+    one bf16 step away from the oracle's wherever the exact value
+    x * gamma / rms lies within 64 fp32 roundings of a bf16 rounding midpoint
+    (the fp32 sum of squares, square root, division and two products); each
+    such element can move logit e by |W_ec| times that step."""
+    x = bf16_to_f64(x_bits)
+    if gamma is None:
+        h = x
+    else:
+        g = bf16_to_f64(gamma)
+        hv = x * g / np.sqrt(np.mean(x * x) + eps)
+        step = _bf16_step(hv)
+        frac = np.abs(hv) / step
+        dist = np.abs(frac - np.floor(frac) - 0.5) * step
+        cand = dist <= 64 * U32 * np.abs(hv)
+        # the expert input the oracle rounds to (round to nearest even of hv)
+        import oracle
+
+        h = bf16_to_f64(oracle.rmsnorm(x_bits, gamma, eps))
+    B = gemv8_bound(router, h) + 2 * np.abs(np.asarray(logits64, np.float64)) * U32
+    if gamma is not None and np.any(cand):
+        # |W (h_dev - h)| plus the GEMV bound's growth from |h_dev| <= |h| + step
+        moved = _abs_dequant(router)[:, cand] @ step[cand]
+        B = B + (1 + gamma_n(64 + router.cols // 16)) * moved
+    return B
+
+
+def routing_certified(bound, logits64, gidx) -> bool:
+    """True when the device's ranking gidx (top-k in rank order, every other
+    expert below the last) is consistent with the fp64 logits moved by at
+    most `bound` each: for every expert a the device ranks above b,
+    l_b - l_a <= bound_a + bound_b (SURVEY's P6 certificate)."""
+    lg = np.asarray(logits64, np.float64)
+    B = np.asarray(bound, np.float64)
+    sel = [int(e) for e in gidx]
+    if len(set(sel)) != len(sel):
+        return False
+    rest = np.setdiff1d(np.arange(lg.size), sel)
+    for j, a in enumerate(sel):
+        below = np.concatenate([np.asarray(sel[j + 1:], dtype=np.int64), rest])
+        if below.size and np.max(lg[below] - B[below]) > lg[a] + B[a]:
+            return False
+    return True
+
+
+def weights_consistent(bound, logits64, gidx, gw) -> bool:
+    """The device's combine weights gw for its routing gidx against the fp64
+    softmax over the same experts: each logit may be off by its bound B, so
+    log w_j may move by at most B_j + max_i B_i (i over the kept experts);
+    plus 1e-5 relative for the fp32 softmax itself."""
+    lg = np.asarray(logits64, np.float64)[np.asarray(gidx)]
+    B = np.asarray(bound, np.float64)[np.asarray(gidx)]
+    ref = np.exp(lg - lg.max())
+    ref = ref / ref.sum()
+    tol = np.expm1(B + B.max()) + 1e-5
+    return bool(np.all(np.abs(np.asarray(gw, np.float64) - ref) <= tol * ref + 1e-30))
+
+
 def have_gpu() -> bool:
     try:
         import torch

@@ -1,19 +1,28 @@
 """GPU parity of the 30-layer decode stack (RMSNorm -> router top-8 ->
 shared + routed FFN -> residual per layer, independent seeded layers)
-against the fp64 oracle: teacher-forced per layer, then free-running.  The
-one-launch stack decode must reproduce the one-layer launches bit for bit."""
+against the fp64 oracle over 32 tokens: teacher-forced per layer, then
+free-running.  The one-launch stack decode must reproduce the one-layer
+launches bit for bit.
+
+Routing differences are accepted only as certified near-ties: the device's
+ranking must be consistent with the fp64 logits moved by at most the fp32
+error bound of each router row (tests.helpers.routing_bound)."""
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 
 import oracle
 import synth
 import synth.device
-from tests.helpers import bf16_to_f64, log, rel_l2, to_u16
+from tests.helpers import (bf16_to_f64, log, rel_l2, routing_bound, routing_certified,
+                           to_u16, weights_consistent)
 
 pytestmark = pytest.mark.gpu
 
 STACK = synth.WORKLOADS["stack30_decode"]
-N_TOKENS = 3
+N_TOKENS = 32
+THREADS = 16
 
 
 @pytest.fixture(scope="module")
@@ -36,15 +45,8 @@ def stack_kernel(stack):
     return q.Stack([dl.layer for _, _, dl in stack])
 
 
-def _near_tie(lg, a, b):
-    gap = max(abs(lg[i] - lg[j]) for i, j in zip(a, b))
-    return gap <= 1e-3 * max(1.0, abs(lg).max())
-
-
-def _run_gpu(torch, q, layers, x):
+def _run_gpu(torch, q, layers, x, ws):
     """Layer by layer on the device; returns every layer's input and routing."""
-    L0 = layers[0][2].layer
-    ws = L0.new_workspace(1)
     cur = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
     xs, idxs = [x], []
     for lw, ol, dl in layers:
@@ -55,7 +57,6 @@ def _run_gpu(torch, q, layers, x):
         cur = out
         xs.append(to_u16(out))
         idxs.append((idx.cpu().numpy(), w.cpu().numpy()))
-    assert q.qmoe_workspace_status(ws) == 0
     return xs, idxs
 
 
@@ -71,18 +72,19 @@ def _run_stack_kernel(torch, stk, x):
     return to_u16(lo), idx.cpu().numpy(), w.cpu().numpy(), to_u16(out)
 
 
-def test_stack_teacher_forced_and_free_running(stack, stack_kernel):
+@pytest.fixture(scope="module")
+def device_runs(stack, stack_kernel):
+    """Every token through the 30 one-layer launches and through the
+    one-launch stack: the two must agree bit for bit."""
     import torch
-    from concurrent.futures import ThreadPoolExecutor
 
     import bit_quantized_gemv_amd as q
 
     X = synth.make_tokens(STACK, N_TOKENS, stream=81)
+    ws = stack[0][2].layer.new_workspace(1)
     runs = []
     for t in range(N_TOKENS):
-        log(f"stack token {t}: 30 layers on the device")
-        runs.append(_run_gpu(torch, q, stack, X[t]))
-        log(f"stack token {t}: one-launch stack decode")
+        runs.append(_run_gpu(torch, q, stack, X[t], ws))
         lo, idx, w, out = _run_stack_kernel(torch, stack_kernel, X[t])
         xs, routing = runs[-1]
         for l in range(STACK.layers):
@@ -90,38 +92,73 @@ def test_stack_teacher_forced_and_free_running(stack, stack_kernel):
             assert np.array_equal(idx[l], routing[l][0]), (t, l)
             assert np.array_equal(w[l].view(np.uint32), routing[l][1].view(np.uint32)), (t, l)
         assert np.array_equal(out, xs[-1])
+    assert q.qmoe_workspace_status(ws) == 0
     assert q.qmoe_workspace_status(stack_kernel.ws) == 0
+    log(f"{N_TOKENS} tokens x {STACK.layers} layers: one-launch stack == one-layer launches")
+    return X, runs
 
-    # teacher-forced: the oracle's layer l on the device's input to layer l
-    flips = 0
-    worst = 0.0
-    with ThreadPoolExecutor(max_workers=8) as ex:
-        for l, (lw, ol, dl) in enumerate(stack):
-            res = list(ex.map(lambda t: ol.forward(runs[t][0][l], residual=True), range(N_TOKENS)))
-            for t in range(N_TOKENS):
-                gidx, gw = runs[t][1][l]
-                r = res[t]
-                if list(gidx) != list(r["idx"]):
-                    assert _near_tie(r["logits"], gidx, r["idx"]), (l, t, "routing flip not a near-tie")
-                    flips += 1
-                    r = ol.forward(runs[t][0][l], residual=True, force_idx=gidx,
-                                   force_w=gw.astype(np.float64))
-                e = rel_l2(bf16_to_f64(runs[t][0][l + 1]), bf16_to_f64(r["out"]))
-                worst = max(worst, e)
-                assert e <= 2e-3, (l, t, e)
-    log(f"  teacher-forced: worst layer relL2 {worst:.2e}, certified near-tie flips {flips}")
 
-    # free-running: the device's 30-layer trajectory against the oracle's own.
-    # Rounding differences compound through the residual layers (the FFN
-    # output dominates the stream), so the bar is the oracle's own
-    # divergence under per-layer perturbations at least as large as the
-    # device's largest per-layer difference: the lowest bf16 bit of 3% of
-    # the elements flipped after every layer (seeded).
+@pytest.fixture(scope="module")
+def teacher_forced(stack, device_runs):
+    """The oracle's layer l on the device's input to layer l, for every token
+    and layer.  Returns the per-(token, layer) relL2 and the certified
+    routing flips {(t, l): (idx, w)}."""
+    X, runs = device_runs
+
+    def one(job):
+        t, l = job
+        lw, ol, _ = stack[l]
+        xin = runs[t][0][l]
+        r = ol.forward(xin, residual=True)
+        gidx, gw = runs[t][1][l]
+        flip = None
+        B = routing_bound(lw.router, xin, r["logits"], gamma=lw.gamma)
+        assert weights_consistent(B, r["logits"], gidx, gw), (t, l, "combine weights")
+        if list(gidx) != list(r["idx"]):
+            assert routing_certified(B, r["logits"], gidx), (t, l, "routing flip not certified")
+            flip = (gidx, gw)
+            r = ol.forward(xin, residual=True, force_idx=gidx, force_w=gw.astype(np.float64))
+        return t, l, rel_l2(bf16_to_f64(runs[t][0][l + 1]), bf16_to_f64(r["out"])), flip
+
+    jobs = [(t, l) for t in range(N_TOKENS) for l in range(STACK.layers)]
+    with ThreadPoolExecutor(max_workers=THREADS) as ex:
+        res = list(ex.map(one, jobs))
+    err = {(t, l): e for t, l, e, _ in res}
+    flips = {(t, l): f for t, l, _, f in res if f is not None}
+    return err, flips
+
+
+def test_stack_teacher_forced(teacher_forced):
+    err, flips = teacher_forced
+    worst = max(err.values())
+    log(f"  teacher-forced over {N_TOKENS} tokens x {STACK.layers} layers: worst layer relL2 "
+        f"{worst:.2e}, certified near-tie flips {len(flips)}")
+    assert worst <= 2e-3
+
+
+def test_stack_free_running(stack, device_runs, teacher_forced):
+    """The device's 30-layer trajectory against the oracle's own.  Rounding
+    differences compound through the residual layers (the FFN output
+    dominates the stream), so the bar is the oracle's own divergence under
+    per-layer perturbations at least as large as the device's largest
+    per-layer difference: the lowest bf16 bit of 6% of the elements flipped
+    after every layer (seeded).  Where the teacher-forced comparison found a
+    certified routing flip, the oracle takes the device's routing there, in
+    both of its runs."""
+    X, runs = device_runs
+    err, flips = teacher_forced
+    worst = max(err.values())
+
     def free(t, flip_frac, seed):
         rng = np.random.default_rng(seed)
         x, xs, step = X[t], [], []
-        for lw, ol, dl in stack:
-            y = ol.forward(x, residual=True)["out"].copy()
+        for l, (lw, ol, dl) in enumerate(stack):
+            f = flips.get((t, l))
+            if f is None:
+                y = ol.forward(x, residual=True)["out"].copy()
+            else:
+                y = ol.forward(x, residual=True, force_idx=f[0],
+                               force_w=f[1].astype(np.float64))["out"].copy()
             if flip_frac:
                 m = rng.random(y.shape) < flip_frac
                 z = y.copy()
@@ -132,9 +169,10 @@ def test_stack_teacher_forced_and_free_running(stack, stack_kernel):
             x = y
         return xs, step
 
-    jobs = [(t, 0.0, 0) for t in range(N_TOKENS)] + [(t, 0.03, 100 + t) for t in range(N_TOKENS)]
-    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+    jobs = [(t, 0.0, 0) for t in range(N_TOKENS)] + [(t, 0.06, 100 + t) for t in range(N_TOKENS)]
+    with ThreadPoolExecutor(max_workers=THREADS) as ex:
         res = list(ex.map(lambda j: free(*j), jobs))
+    ratios = []
     for t in range(N_TOKENS):
         clean, _ = res[t]
         pert, steps = res[N_TOKENS + t]
@@ -142,10 +180,10 @@ def test_stack_teacher_forced_and_free_running(stack, stack_kernel):
         for l in (9, 19, 29):
             e = rel_l2(bf16_to_f64(runs[t][0][l + 1]), bf16_to_f64(clean[l]))
             d = rel_l2(bf16_to_f64(pert[l]), bf16_to_f64(clean[l]))
-            log(f"  token {t} after layer {l + 1}: device vs oracle {e:.2e}, "
-                f"oracle vs perturbed oracle {d:.2e}")
-            if flips == 0:
-                assert e <= max(2e-3, 2 * d), (t, l, e, d)
+            ratios.append(e / max(d, 1e-12))
+            assert e <= max(2e-3, 2 * d), (t, l, e, d)
+    log(f"  free-running over {N_TOKENS} tokens: device divergence / perturbed-oracle divergence "
+        f"median {np.median(ratios):.2f}, max {max(ratios):.2f}")
 
 
 def test_stack_residual_stream_grows_and_stays_finite(stack):
@@ -156,7 +194,9 @@ def test_stack_residual_stream_grows_and_stays_finite(stack):
     import bit_quantized_gemv_amd as q
 
     x = synth.make_tokens(STACK, 1, stream=82)[0]
-    xs, _ = _run_gpu(torch, q, stack, x)
+    ws = stack[0][2].layer.new_workspace(1)
+    xs, _ = _run_gpu(torch, q, stack, x, ws)
+    assert q.qmoe_workspace_status(ws) == 0
     for l in range(STACK.layers):
         a, b = bf16_to_f64(xs[l]), bf16_to_f64(xs[l + 1])
         assert np.all(np.isfinite(b))

@@ -11,14 +11,10 @@ import pytest
 import oracle
 import synth
 import synth.device
-from tests.helpers import bf16_to_f64, log, rel_l2, to_u16
+from tests.helpers import (bf16_to_f64, log, rel_l2, routing_bound, routing_certified,
+                           to_u16, weights_consistent)
 
 pytestmark = pytest.mark.gpu
-
-
-def _near_tie(lg, a, b):
-    gap = max(abs(lg[i] - lg[j]) for i, j in zip(a, b))
-    return gap <= 1e-3 * max(1.0, abs(lg).max())
 
 
 def _build(name):
@@ -97,12 +93,13 @@ def _teacher_forced(wl, layers, x, lo, idx, w):
         ol = layers[l][1]
         r = ol.forward(ins[l], residual=True)
         flip = list(idx[l]) != list(r["idx"])
+        lw = layers[l][0]
+        B = routing_bound(lw.router, ins[l], r["logits"], gamma=lw.gamma)
+        assert weights_consistent(B, r["logits"], idx[l], w[l]), (l, "combine weights")
         if flip:
-            assert _near_tie(r["logits"], idx[l], r["idx"]), (l, "routing flip not a near-tie")
+            assert routing_certified(B, r["logits"], idx[l]), (l, "routing flip not certified")
             r = ol.forward(ins[l], residual=True, force_idx=idx[l],
                            force_w=w[l].astype(np.float64))
-        else:
-            assert np.allclose(w[l], r["w"], rtol=1e-4, atol=1e-6), l
         return rel_l2(bf16_to_f64(lo[l]), bf16_to_f64(r["out"])), flip
 
     with ThreadPoolExecutor(max_workers=8) as ex:

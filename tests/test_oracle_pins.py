@@ -260,6 +260,34 @@ def test_layer_forward_matches_numpy_brute_force(residual):
     assert list(r["out"]) == [oracle.double_to_bf16(v) for v in r["y"]]
 
 
+def test_router_logit_bias_enters_once_with_its_sign():
+    """logits_e = sum_c Wr[e][c] h_c + beta_e: against a numpy dequant matmul
+    plus beta, with beta large enough to change the routing, so that a
+    dropped, negated or rescaled bias term fails; the layer's routing and
+    weights follow the biased logits."""
+    from scipy.special import softmax
+
+    lw = synth.make_layer(TINY)
+    beta = np.random.default_rng(11).normal(0, 40, TINY.n_experts).astype(np.float32)
+    h = synth.random_bf16(128, 12)
+    hd = synth.bf16_bits_to_f32(h).astype(np.float64)
+    plain = _numpy_dequant(lw.router) @ hd
+    ref = plain + beta.astype(np.float64)
+    L = oracle.OracleLayer(lw, logit_bias=beta)
+    got = L.router_logits(h)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+    assert not np.allclose(got, plain - beta, rtol=1e-6)
+    assert not np.allclose(got, plain + 2 * beta.astype(np.float64), rtol=1e-6)
+    unbiased = oracle.OracleLayer(lw, use_prior=False).router_logits(h)
+    assert np.allclose(got - unbiased, beta.astype(np.float64), rtol=0, atol=1e-12 * np.abs(ref).max())
+    r = L.forward(h)
+    idx = np.argsort(-ref, kind="stable")[:TINY.top_k]
+    assert list(r["idx"]) == list(idx)
+    assert list(idx) != list(np.argsort(-plain, kind="stable")[:TINY.top_k])
+    assert np.allclose(r["w"], softmax(ref[idx]), rtol=1e-12)
+    assert np.allclose(r["logits"], ref, rtol=1e-12, atol=1e-12 * np.abs(ref).max())
+
+
 def test_layer_zero_input_gives_zero():
     lw = synth.make_layer(TINY)
     r = oracle.OracleLayer(lw).forward(np.zeros(128, dtype=np.uint16), residual=True)
