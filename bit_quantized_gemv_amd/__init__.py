@@ -68,6 +68,8 @@ _lib.qmoe_expert_ffn.argtypes = [C.POINTER(_Layer), _vp, _vp, _vp, _vp, _vp, _vp
 _lib.qmoe_moe_decode.argtypes = [C.POINTER(_Layer), _vp, _vp, C.c_int32, _vp, _vp, _vp, _vp,
                                  C.c_size_t, _vp]
 _lib.qmoe_moe_decode_phased.argtypes = _lib.qmoe_moe_decode.argtypes
+_lib.qmoe_moe_decode_noalloc.argtypes = [C.POINTER(_Layer), _vp, _vp, C.c_int32, _vp, _vp, _vp,
+                                         _vp]
 _lib.qmoe_moe_decode_timed.argtypes = _lib.qmoe_moe_decode.argtypes + [_vp, _vp]
 _lib.qmoe_prefill_grouped.argtypes = [C.POINTER(_Layer), _vp, C.c_int32, _vp, _vp, _vp, _vp, _vp,
                                       C.c_size_t, _vp]
@@ -112,6 +114,7 @@ for _f in ("qmoe_gemv_affine4", "qmoe_router_topk", "qmoe_expert_ffn", "qmoe_moe
            "qmoe_expert_ffn_shared", "qmoe_expert_ffn_routed", "qmoe_pool_create",
            "qmoe_pool_plan", "qmoe_pool_acquire", "qmoe_pool_stats_get",
            "qmoe_stack_table_init", "qmoe_stack_decode", "qmoe_workspace_tag_counter",
+           "qmoe_moe_decode_noalloc",
            "qmoe_workspace_raise_tag_counter"):
     getattr(_lib, _f).restype = C.c_int
 
@@ -313,6 +316,15 @@ def qmoe_moe_decode(layer: MoeLayer, x, expert_slot, residual: bool, out, idx_ou
         _ptr(idx_out), _ptr(w_out), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)))
 
 
+def qmoe_moe_decode_noalloc(layer: MoeLayer, x, expert_slot, residual: bool, out, idx_out,
+                            w_out, stream=None) -> None:
+    """qmoe_moe_decode with the library's own per-GPU workspace (no
+    allocation; calls on one GPU must not overlap)."""
+    _check("qmoe_moe_decode_noalloc", _lib.qmoe_moe_decode_noalloc(
+        C.byref(layer.c()), _ptr(x), _ptr(expert_slot), int(bool(residual)), _ptr(out),
+        _ptr(idx_out), _ptr(w_out), _stream(stream)))
+
+
 def qmoe_moe_decode_timed(layer: MoeLayer, x, expert_slot, residual: bool, out, idx_out, w_out,
                           ws, ev_start, ev_stop, stream=None) -> None:
     """qmoe_moe_decode whose launch records two HIP events (raw handles, e.g.
@@ -423,7 +435,7 @@ def qmoe_workspace_raise_tag_counter(ws, value: int, stream=None) -> None:
 __all__ = [
     "QTensor", "MoeLayer", "QmoeError", "lib", "LIB_PATH",
     "qmoe_gemv_affine4", "qmoe_router_topk", "qmoe_expert_ffn", "qmoe_moe_decode",
-    "qmoe_moe_decode_timed", "qmoe_expert_ffn_shared", "qmoe_expert_ffn_routed", "Pool",
+    "qmoe_moe_decode_timed", "qmoe_moe_decode_noalloc", "qmoe_expert_ffn_shared", "qmoe_expert_ffn_routed", "Pool",
     "PoolStats", "qmoe_prefill_grouped", "qmoe_prefill_dispatch_offsets",
     "qmoe_rmsnorm",
     "qmoe_workspace_bytes",

@@ -6,8 +6,17 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "qmoe.h"
 #include "qmoe_common.h"
+
+// Workspace of qmoe_moe_decode_noalloc: a fixed device array, one copy per
+// GPU (each device holds it until the process ends).  Host code never uses
+// this name as an address: the device address comes from
+// hipGetSymbolAddress, per device (see scratch_for_device).
+constexpr size_t kScratchBytes = (size_t)512 << 10;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace qmoe {
 qmoe_status launch_gemv4(const qmoe_qtensor& W, const uint16_t* x, float* y, void* stream);
@@ -18,7 +27,8 @@ qmoe_status launch_router(const qmoe_qtensor& Wr, const float* lbias, const uint
 qmoe_status launch_moe_step(const qmoe_moe_layer& L, const uint16_t* x, const int32_t* idx_in,
                             const float* w_in, const int32_t* slot, const uint16_t* residual,
                             uint16_t* out, int32_t* idx_out, float* w_out, uint8_t* ws, int mode,
-                            void* stream, void* ev_start = nullptr, void* ev_stop = nullptr);
+                            void* stream, void* ev_start = nullptr, void* ev_stop = nullptr,
+                            int heal = 0);
 qmoe_status launch_prefill(const qmoe_moe_layer& L, const uint16_t* X, int T, const int32_t* idx,
                            const float* w, const uint16_t* residual, uint16_t* out, uint8_t* ws,
                            void* stream);
@@ -84,6 +94,39 @@ static size_t stack_ws_bytes(const qmoe_moe_layer* L) {
 static bool same_shape(const qmoe_moe_layer& a, const qmoe_moe_layer& b) {
   return a.hidden == b.hidden && a.n_experts == b.n_experts && a.top_k == b.top_k &&
          a.inter == b.inter && a.shared_inter == b.shared_inter && a.rms_eps == b.rms_eps;
+}
+
+// Zero n16 16-byte words (a kernel, not hipMemsetAsync, so that the fill
+// can sit in a captured graph).
+__global__ void k_zero16(uint4* p, size_t n16) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0, 0, 0, 0);
+}
+
+// The current device's address of `scratch`, looked up once per device
+// (with that device current) and kept; the first call on a device also
+// enqueues the zero fill a workspace needs before its first use, on the
+// caller's stream, ahead of that call's kernels.
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static uint8_t* g_scratch[kMaxDevices];
+
+static qmoe_status scratch_for_device(hipStream_t st, uint8_t** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return QMOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return QMOE_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return QMOE_ERR_HIP;
+    hipLaunchKernelGGL(k_zero16, dim3(256), dim3(256), 0, st, static_cast<uint4*>(p),
+                       kScratchBytes / 16);
+    if (hipGetLastError() != hipSuccess) return QMOE_ERR_HIP;
+    g_scratch[dev] = static_cast<uint8_t*>(p);
+  }
+  *out = g_scratch[dev];
+  return QMOE_OK;
 }
 }  // namespace qmoe
 
@@ -196,6 +239,21 @@ qmoe_status qmoe_moe_decode(const qmoe_moe_layer* L, const uint16_t* x, const in
   if (ws_bytes < ws_bytes_layer(L, 1)) return QMOE_ERR_WORKSPACE;
   return launch_moe_step(*L, x, nullptr, nullptr, expert_slot, residual ? x : nullptr, out,
                          idx_out, w_out, static_cast<uint8_t*>(ws), 0, stream);
+}
+
+qmoe_status qmoe_moe_decode_noalloc(const qmoe_moe_layer* L, const uint16_t* x,
+                                    const int32_t* expert_slot, int32_t residual, uint16_t* out,
+                                    int32_t* idx_out, float* w_out, void* stream) {
+  qmoe_status s = check_layer(L);
+  if (s != QMOE_OK) return s;
+  if (!x || !out) return QMOE_ERR_NULL_ARG;
+  if (!al16(x)) return QMOE_ERR_ALIGN;
+  if (ws_bytes_layer(L, 1) > kScratchBytes) return QMOE_ERR_WORKSPACE;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  uint8_t* ws = nullptr;
+  if ((s = scratch_for_device(st, &ws)) != QMOE_OK) return s;
+  return launch_moe_step(*L, x, nullptr, nullptr, expert_slot, residual ? x : nullptr, out,
+                         idx_out, w_out, ws, 0, stream, nullptr, nullptr, /*heal=*/1);
 }
 
 qmoe_status qmoe_prefill_grouped(const qmoe_moe_layer* L, const uint16_t* X, int32_t T,

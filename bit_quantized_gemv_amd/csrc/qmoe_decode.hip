@@ -126,6 +126,8 @@ struct DecodeArgs {
   uint32_t dtag;            // stack: their flag value
   int cnt;                  // role whose blocks count the call done: kCntNone/S/D
   uint32_t ntags;           // tag values the call uses (advance of the tag counter)
+  int heal;                 // 1: a failed wait is cleared by the call's last block (no
+                            // caller can read the error word of this workspace)
 };
 constexpr int kCntNone = 0, kCntS = 1, kCntD = 2;
 
@@ -187,9 +189,12 @@ __device__ void gen_advance(uint8_t* ws, size_t ctl_off, int E, uint32_t gen, ui
 
 // Block i of the n blocks of the role whose completion ends a one-layer
 // call (every block of the call has read the tag counter when all of them
-// are done): count it; the last one advances the counter by the call's
-// tags.  Counters per group of blocks (i % kGenRep), then one for the
-// groups, so that few atomics meet on one address.  Whole block.
+// are done, whether their waits completed or not): count it; the last one
+// advances the counter by the call's tags.  Counters per group of blocks
+// (i % kGenRep), then one for the groups, so that few atomics meet on one
+// address.  After a failed wait the counter stays (qmoe_workspace_status
+// restarts the control area), or with `heal` the last block restarts it and
+// clears the error word itself.  Whole block.
 __device__ void call_done(const DecodeArgs& a, int i, int n, uint32_t gen, uint32_t* sys,
                           int tid = threadIdx.x) {
   if (tid == 0) {
@@ -210,7 +215,14 @@ __device__ void call_done(const DecodeArgs& a, int i, int n, uint32_t gen, uint3
     sys[kSysDone] = last;
   }
   __syncthreads();
-  if (sys[kSysDone]) gen_advance(a.ws, a.wl.ctl, a.E, gen, a.ntags, tid);
+  if (!sys[kSysDone]) return;
+  uint32_t* err = reinterpret_cast<uint32_t*>(a.ws + a.wl.ctl) + ctl::kError;
+  if (ld_dev(err) == 0) {
+    gen_advance(a.ws, a.wl.ctl, a.E, gen, a.ntags, tid);
+  } else if (a.heal) {
+    ctl_restart(a.ws, a.wl.ctl, a.E, tid);
+    if (tid == 0) st_dev(err, 0u);
+  }
 }
 
 // One full wave: wait until flags[0..n) all equal `epoch`.  Every poll reads
@@ -1263,7 +1275,8 @@ __global__ __launch_bounds__(kBlock) void k_moe_step(DecodeArgs a) {
     const bool ok = role_gate_up<HC, NV, false>(a, -1, s, ISC ? ISC : a.Is, smem, epoch, t_start);
     block_publish(a, s, epoch);
     QMOE_STAMP(sys, 5);
-    if (ok && a.cnt == kCntS) call_done(a, s, a.nS, gen, sys);
+    (void)ok;
+    if (a.cnt == kCntS) call_done(a, s, a.nS, gen, sys);
   } else if (rb < a.nR + a.nS + a.nG) {
     const int gb = rb - a.nR - a.nS;
     role_gate_up<HC, NV, false>(a, gb / a.perG, gb % a.perG, IC ? IC : a.I, smem, epoch, t_start);
@@ -1272,7 +1285,7 @@ __global__ __launch_bounds__(kBlock) void k_moe_step(DecodeArgs a) {
   } else {
     uint32_t held = 0;
     const int d = rb - a.nR - a.nS - a.nG;
-    if (!role_down<IC, ISC, NV, false>(a, d, smem, epoch, t_start, held, nullptr)) return;
+    role_down<IC, ISC, NV, false>(a, d, smem, epoch, t_start, held, nullptr);
     if (a.cnt == kCntD) call_done(a, d, a.nD, gen, sys);
   }
 #ifdef QMOE_TRACE
@@ -1487,7 +1500,7 @@ static void launch_step(const DecodeArgs& a, int blocks, size_t lds, void* strea
 qmoe_status launch_moe_step(const qmoe_moe_layer& L, const uint16_t* x, const int32_t* idx_in,
                             const float* w_in, const int32_t* slot, const uint16_t* residual,
                             uint16_t* out, int32_t* idx_out, float* w_out, uint8_t* ws, int mode,
-                            void* stream, void* ev_start, void* ev_stop) {
+                            void* stream, void* ev_start, void* ev_stop, int heal) {
   const int phased = mode == kStepPhased;
   if (!moe_step_supported(L)) return QMOE_ERR_UNSUPPORTED;
   hipEvent_t e0 = reinterpret_cast<hipEvent_t>(ev_start);
@@ -1521,6 +1534,7 @@ qmoe_status launch_moe_step(const qmoe_moe_layer& L, const uint16_t* x, const in
   // workspace's tag counter when all of them are done
   a.ntags = 1;
   a.cnt = kCntD;
+  a.heal = heal;
   if (mode == kStepShared || mode == kStepRouted) {
     if (mode == kStepRouted && !idx_in) return QMOE_ERR_NULL_ARG;
     if (mode == kStepShared) {

@@ -155,6 +155,24 @@ qmoe_status qmoe_moe_decode_phased(const qmoe_moe_layer* L, const uint16_t* x,
                                    uint16_t* out, int32_t* idx_out, float* w_out,
                                    void* ws, size_t ws_bytes, void* stream);
 
+/* qmoe_moe_decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same step and kernels, bitwise the same results, with the
+ * workspace in a fixed 512 KiB device array of the library, one per GPU (held
+ * until the process ends; the first call on a GPU looks it up and zero-fills
+ * it on `stream`).  Nothing is allocated or freed.  Layers whose workspace
+ * (qmoe_workspace_bytes(L, 1)) exceeds 512 KiB get QMOE_ERR_WORKSPACE.  Every
+ * call on a GPU uses that GPU's one array, which keeps the last call's
+ * state: calls that overlap on one GPU race, so order them (one stream, or
+ * events between streams).  No caller can read this array's error word: a
+ * failed in-kernel wait (which valid inputs do not cause) leaves that call's
+ * outputs undefined, and the call's last block restores the array for the
+ * next call. */
+qmoe_status qmoe_moe_decode_noalloc(const qmoe_moe_layer* L, const uint16_t* x,
+                                    const int32_t* expert_slot, int32_t residual,
+                                    uint16_t* out, int32_t* idx_out, float* w_out,
+                                    void* stream);
+
 /* qmoe_moe_decode with kernel timing: ev_start and ev_stop (hipEvent_t, or
  * NULL) are recorded by the launch itself at the start and at the end of
  * the step's kernel, so hipEventElapsedTime gives the kernel's duration

@@ -118,3 +118,21 @@ def test_stack_sizes_and_validation_before_launch():
     assert lib.qmoe_stack_table_init(arr, 2, tab, 2 * one - 1, None) == 4
     assert lib.qmoe_stack_table_init(arr, 0, tab, 2 * one, None) == 2
     assert lib.qmoe_stack_table_init(arr, 2, None, 2 * one, None) == 1
+
+
+def test_noalloc_decode_rejects_a_layer_beyond_its_array():
+    """Hidden 16384, 512 experts (a 985,344-byte workspace): rejected on the
+    host before anything is launched (the tensor pointers are never read)."""
+    import bit_quantized_gemv_amd as q
+
+    lib = q.lib()
+
+    def qt(rows, cols, bits, p=0x100000):
+        return q._QT(p, p + 0x1000000, p + 0x2000000, rows, cols, bits, 64, 0)
+
+    H, E, K, I, Is = 16384, 512, 8, 2048, 1024
+    L = q._Layer(H, E, K, I, Is, qt(E, H, 8), qt(I, H, 4), qt(I, H, 4), qt(H, I, 4),
+                 qt(Is, H, 4), qt(Is, H, 4), qt(H, Is, 4), None, 1e-6, None)
+    assert lib.qmoe_workspace_bytes(C.byref(L), 1) > (512 << 10)
+    assert lib.qmoe_moe_decode_noalloc(C.byref(L), 0x3000, None, 0, 0x6000, None, None,
+                                       None) == 4  # QMOE_ERR_WORKSPACE
