@@ -27,6 +27,13 @@ if not os.path.exists(LIB_PATH):
         f"{LIB_PATH} is missing: build it with `python -m bit_quantized_gemv_amd.build` "
         "(the quantized MoE path has no CPU fallback)")
 
+# One HIP runtime per process: torch's libtorch_hip asks for its bundled
+# libamdhip64 by file name, so if this library (which names the runtime by
+# its soname) were loaded first, torch would map a second runtime next to
+# it, and device symbols set through one would be unknown to the other.
+# Loading torch first makes this library bind to torch's runtime.
+import torch  # noqa: E402,F401
+
 _lib = C.CDLL(LIB_PATH)
 
 # status codes

@@ -92,11 +92,13 @@ __device__ int qmoe_trace_slots;
   do {                     \
   } while (0)
 #endif
-// Stamps: 0 block start; 1 first weight loads issued; 2 input staged (R, S,
-// G) / routing known (D); 3 routing known (G) / logits published (R) /
-// shared flags seen (D); 4 computed (S, G) / shared staged (D); 5 published
-// (S, G) / routed flags seen (D); 6 routed staged (D); 7 combined (D);
-// 8 output stored (D); 9 done counted (D, S of a shared-only call).
+// Stamps: 0 block start; 1 first weight loads issued; 2 input staged (S,
+// G) / logits computed (R) / routing known (D); 3 routing known (G) /
+// logits published (R) / shared flags seen (D); 4 computed (S, G) / input
+// staged (R) / shared staged (D); 5 published (S, G) / routed flags seen
+// (D); 6 routed staged (D); 7 combined (D); 8 output stored (D); 9 block
+// end; 10 routing seen (G, D: the poll that saw every tag returned); 11
+// top-k done (G, D); 12-14 top-k select, gather, rank done (G, D).
 
 __host__ __device__ inline size_t al16(size_t n) { return (n + 15) & ~(size_t)15; }
 
@@ -239,9 +241,9 @@ __device__ bool wave_wait_flags(const uint32_t* flags, int n, uint32_t epoch, ui
   __builtin_amdgcn_s_setprio(2);
   for (int it = 0;; ++it) {
     {
-      bool ok = true;
-      for (int i = lane; i < n; i += 64) ok = ok && ld_dev(flags + i) == epoch;
-      if (__all(ok)) {
+      uint32_t bad = 0;  // every load issued before the first compare
+      for (int i = lane; i < n; i += 64) bad |= ld_dev(flags + i) ^ epoch;
+      if (__all(bad == 0)) {
         __builtin_amdgcn_s_setprio(0);
         return true;
       }
@@ -348,7 +350,8 @@ __device__ float block_sum(float v, float* red, int tid = threadIdx.x) {
 // its producers, no waiting.
 template <int NV>
 __device__ bool wave_routing(const DecodeArgs& a, uint32_t epoch, int32_t* idx_s, float* w_s,
-                             bool write_out, uint64_t* xch, int tid = threadIdx.x) {
+                             bool write_out, uint64_t* xch, uint32_t* sys, int tid = threadIdx.x) {
+  (void)sys;
   const int lane = tid & 63;
   const uint64_t* tag = reinterpret_cast<const uint64_t*>(
       rep_of(a, ctl::kTagBase, blockIdx.x % ctl::kRep));
@@ -375,10 +378,16 @@ __device__ bool wave_routing(const DecodeArgs& a, uint32_t epoch, int32_t* idx_s
     }
     __builtin_amdgcn_s_sleep(kPollSleep);
   }
+  QMOE_STAMP(sys, 10);
   // the selection runs at the polling priority: it is on every consumer's
   // critical path
+#ifdef QMOE_TRACE
+  uint64_t* tstamps = tid == 0 ? reinterpret_cast<uint64_t*>(sys + kSysTrace) + 12 : nullptr;
+#else
+  uint64_t* tstamps = nullptr;
+#endif
   wave_topk_radix<NV>(v, a.E, a.K, idx_s, w_s, write_out ? a.idx_out : nullptr,
-                      write_out ? a.w_out : nullptr, xch, tid);
+                      write_out ? a.w_out : nullptr, xch, tid, tstamps);
   __builtin_amdgcn_s_setprio(0);
   return true;
 }
@@ -405,7 +414,8 @@ __device__ bool block_routing(const DecodeArgs& a, uint32_t epoch, uint32_t* sys
   }
   if (tid < 64) {
     bool ok = wave_routing<NV>(a, epoch, idx_s, w_s, write_out,
-                               reinterpret_cast<uint64_t*>(sys + kSysXch), tid);
+                               reinterpret_cast<uint64_t*>(sys + kSysXch), sys, tid);
+    QMOE_STAMP(sys, 11);
     if (ok && tid < a.K) {
       const int e = idx_s[tid];
       slot_s[tid] = a.slot ? gptr(a.slot)[e] : e;
@@ -821,6 +831,9 @@ __device__ float router_token(const DevQ& Wr, int row0, int E, int H_rt, const u
   {
     RRegs<SR> R;
     router_load<SR>(R, Wr, row0, E, H, 0, tid);
+    uint32_t* sys = reinterpret_cast<uint32_t*>(red) - kSysRed;
+    (void)sys;
+    QMOE_STAMP(sys, 1);
     if constexpr (XDEV) {
       pre();
       x_load_dev(X, x, H, tid);
@@ -828,6 +841,7 @@ __device__ float router_token(const DevQ& Wr, int row0, int E, int H_rt, const u
     float inv = gamma ? x_inv_rms(X, x, H, eps, red, tid) : 1.f;
     x_stage<false>(X, x, gamma, inv, H, xr, xh, tid);
     __syncthreads();
+    QMOE_STAMP(sys, 4);
     acc = router_compute<SR>(R, H, 0, xr, xh, acc, tid);
   }
   if (!H8C) {

@@ -32,9 +32,12 @@ __device__ __forceinline__ float topk_value(uint32_t u) {
 //      as (order value, complemented index) keys, and lane j < k ranks
 //      slot j against the k keys;
 //   4. lane j takes rank j for the softmax.
+// stamps (trace builds; else null): s_memrealtime after the select, the
+// gather and the ranking, in stamps[0..3).
 template <int NV>
 __device__ void wave_topk_radix(const float (&v)[NV], int E, int K, int32_t* idx_s, float* w_s,
-                                int32_t* idx2, float* w2, uint64_t* xch, int tid = threadIdx.x) {
+                                int32_t* idx2, float* w2, uint64_t* xch, int tid = threadIdx.x,
+                                uint64_t* stamps = nullptr) {
   const int lane = tid & 63;
   const uint64_t below = (1ull << lane) - 1ull;
   uint32_t o[NV];
@@ -48,6 +51,7 @@ __device__ void wave_topk_radix(const float (&v)[NV], int E, int K, int32_t* idx
     for (int m = 0; m < NV; ++m) n += (uint32_t)__popcll(__ballot(o[m] >= c));
     if (n >= (uint32_t)K) T = c;
   }
+  if (stamps && lane == 0) stamps[0] = __builtin_amdgcn_s_memrealtime();
   uint32_t above = 0;
 #pragma unroll
   for (int m = 0; m < NV; ++m) above += (uint32_t)__popcll(__ballot(o[m] > T));
@@ -66,6 +70,7 @@ __device__ void wave_topk_radix(const float (&v)[NV], int E, int K, int32_t* idx
     base += (uint32_t)__popcll(sel);
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  if (stamps && lane == 0) stamps[1] = __builtin_amdgcn_s_memrealtime();
   if (lane < K) {
     const uint64_t kj = xch[lane];
     uint32_t r = 0;
@@ -73,6 +78,7 @@ __device__ void wave_topk_radix(const float (&v)[NV], int E, int K, int32_t* idx
     xch[K + r] = kj;
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  if (stamps && lane == 0) stamps[2] = __builtin_amdgcn_s_memrealtime();
   float p = 0.f;
   int e = 0;
   if (lane < K) {

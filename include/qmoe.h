@@ -105,12 +105,20 @@ typedef struct {
 #define QMOE_MAX_LAYERS 128
 
 /* y[r] = sum_c W[r][c] x[c] for a 4-bit affine matrix (the quantized GEMV).
+ * Defined by: elsolitario.org, TurboFieldfare article, section "Detalles
+ * técnicos y rendimiento" (MLX affine 4-bit weights, group size 64);
+ * iitog.ru, "TurboFieldfare: движок с открытым кодом…", technical paragraph
+ * (a quantized-GEMV kernel).
  * W: bits=4, group=64, expert_stride_bytes ignored.  x: bf16 [cols].
  * y: fp32 [rows].  Returns QMOE_ERR_UNSUPPORTED for bits != 4. */
 qmoe_status qmoe_gemv_affine4(const qmoe_qtensor* W, const uint16_t* x, float* y,
                               void* stream);
 
-/* Router of T tokens: logits[t][e] = sum_c Wr[e][c] x[t][c] (+ bias[e]);
+/* Router of T tokens (devtrends.cc "Come eseguire un modello da 26 miliardi…",
+ * section "Qual è il trucco principale dell'architettura": a router per
+ * layer selects 8 experts; remio.ai "TurboFieldfare esegue Mac Gemma 4 26B
+ * in 2 GB…", section "L'affermazione dei 2 GB…": the router is 8-bit affine):
+ * logits[t][e] = sum_c Wr[e][c] x[t][c] (+ bias[e]);
  * keep the top_k largest (ties: lower expert index first), ordered by
  * descending logit; w[t][j] = softmax over the kept logits (equal to a full
  * softmax renormalised over the kept experts).
@@ -122,7 +130,11 @@ qmoe_status qmoe_router_topk(const qmoe_qtensor* Wr, const float* logit_bias,
                              int32_t* idx, float* w, float* logits, void* ws,
                              size_t ws_bytes, void* stream);
 
-/* FFN of one token given its routing: for M in {shared, idx[0..k)}
+/* FFN of one token given its routing (remio.ai "TurboFieldfare esegue Mac
+ * Gemma 4 26B in 2 GB…", sections "Mac Gemma 4 26B entra nello spazio
+ * disponibile…" (eight routed experts and one shared expert) and
+ * "L'affermazione dei 2 GB…" (the shared and routed branches are combined)):
+ * for M in {shared, idx[0..k)}
  *   a_M = gelu_tanh(W_gate,M h) * (W_up,M h);   y_M = W_down,M a_M
  *   out = bf16( y_shared + sum_j w[j] y_idx[j]  (+ residual) )
  * h: bf16 [H] (the expert input, already normalised if the model norms).
@@ -135,7 +147,10 @@ qmoe_status qmoe_expert_ffn(const qmoe_moe_layer* L, const uint16_t* h,
                             const int32_t* expert_slot, const uint16_t* residual,
                             uint16_t* out, void* ws, size_t ws_bytes, void* stream);
 
-/* One whole decode step of one layer for one token, in a single launch:
+/* One whole decode step of one layer for one token, in a single launch
+ * (remio.ai "TurboFieldfare esegue Mac Gemma 4 26B in 2 GB…", section
+ * "L'affermazione dei 2 GB…": router, experts and combine, per layer and
+ * token):
  *   h = L->rms_gamma ? bf16(rmsnorm(x) * gamma) : x
  *   routing = top-k softmax of the router on h (+ logit_bias)
  *   out = bf16( FFN combine as in qmoe_expert_ffn  (+ x if residual) )
@@ -184,7 +199,10 @@ qmoe_status qmoe_moe_decode_timed(const qmoe_moe_layer* L, const uint16_t* x,
                                   void* ev_start, void* ev_stop);
 
 /* Chunked prefill of T <= 128 tokens that share one loaded copy of each
- * expert: the (token, rank) pairs are grouped by expert (stable: expert,
+ * expert (devtrends.cc "Come eseguire un modello da 26 miliardi…", section
+ * "Prestazioni nel mondo reale": 128-token chunks, one loaded expert serves
+ * a group of rows; remio.ai, section "L'affermazione dei 2 GB…": chunks of
+ * up to 128 tokens): the (token, rank) pairs are grouped by expert (stable: expert,
  * then token, then rank) and every expert runs one grouped dequantizing
  * GEMM over its rows on the matrix cores; the shared expert runs as a dense
  * GEMM over all T rows; then

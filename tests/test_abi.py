@@ -136,3 +136,21 @@ def test_noalloc_decode_rejects_a_layer_beyond_its_array():
     assert lib.qmoe_workspace_bytes(C.byref(L), 1) > (512 << 10)
     assert lib.qmoe_moe_decode_noalloc(C.byref(L), 0x3000, None, 0, 0x6000, None, None,
                                        None) == 4  # QMOE_ERR_WORKSPACE
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """Importing the package before torch maps a single libamdhip64: the
+    library binds to torch's HIP runtime instead of loading a second one
+    (with two, device symbols set through one are unknown to the other)."""
+    import subprocess
+    import sys
+
+    code = ("import sys; sys.path.insert(0, %r)\n"
+            "import bit_quantized_gemv_amd\n"
+            "import torch\n"
+            "maps = open('/proc/self/maps').read().split('\\n')\n"
+            "libs = {l.split()[-1] for l in maps if 'libamdhip64' in l}\n"
+            "print(len(libs), sorted(libs))\n" % ROOT)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    assert r.stdout.split()[0] == "1", r.stdout
