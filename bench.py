@@ -50,7 +50,7 @@ COPY_BYTES = 1 << 30
 # valid only for the kernel sources it was measured on.
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "k_moe_step_layer_decode_pmc.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "bit_quantized_gemv_amd", "csrc", f)
-                  for f in ("qmoe_decode.hip", "qmoe_common.h")]
+                  for f in ("qmoe_decode.hip", "qmoe_common.h", "qmoe_topk.h")]
 
 
 def log(msg):
