@@ -68,6 +68,10 @@ _vp = C.c_void_p
 _lib.qmoe_status_string.restype = C.c_char_p
 _lib.qmoe_status_string.argtypes = [C.c_int]
 _lib.qmoe_gemv_affine4.argtypes = [C.POINTER(_QT), _vp, _vp, _vp]
+_lib.qmoe_tiled4_bytes.restype = C.c_size_t
+_lib.qmoe_tiled4_bytes.argtypes = [C.c_int32, C.c_int32]
+_lib.qmoe_repack_tiled4.argtypes = [_vp, _vp, _vp, C.c_int32, C.c_int32, _vp, C.c_size_t]
+_lib.qmoe_gemv_tiled4.argtypes = [_vp, C.c_int32, C.c_int32, _vp, _vp, C.c_int32, _vp]
 _lib.qmoe_router_topk.argtypes = [C.POINTER(_QT), _vp, _vp, C.c_int32, C.c_int32, _vp, _vp, _vp,
                                   _vp, C.c_size_t, _vp]
 _lib.qmoe_expert_ffn.argtypes = [C.POINTER(_Layer), _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -121,7 +125,7 @@ for _f in ("qmoe_gemv_affine4", "qmoe_router_topk", "qmoe_expert_ffn", "qmoe_moe
            "qmoe_expert_ffn_shared", "qmoe_expert_ffn_routed", "qmoe_pool_create",
            "qmoe_pool_plan", "qmoe_pool_acquire", "qmoe_pool_stats_get",
            "qmoe_stack_table_init", "qmoe_stack_decode", "qmoe_workspace_tag_counter",
-           "qmoe_moe_decode_noalloc",
+           "qmoe_moe_decode_noalloc", "qmoe_repack_tiled4", "qmoe_gemv_tiled4",
            "qmoe_workspace_raise_tag_counter"):
     getattr(_lib, _f).restype = C.c_int
 
@@ -232,6 +236,33 @@ def qmoe_gemv_affine4(W: QTensor, x, y, stream=None) -> None:
     qt = W.c()
     _check("qmoe_gemv_affine4", _lib.qmoe_gemv_affine4(C.byref(qt), _ptr(x), _ptr(y),
                                                         _stream(stream)))
+
+
+def qmoe_tiled4_bytes(rows: int, cols: int) -> int:
+    return int(_lib.qmoe_tiled4_bytes(rows, cols))
+
+
+def qmoe_repack_tiled4(q, scales, biases, rows: int, cols: int):
+    """Host-side repack (numpy arrays in, a uint8 numpy array out): codes
+    uint8 [rows][cols/2], scales and biases fp16 bits (uint16) [rows][cols/64]."""
+    import numpy as np
+
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = np.ascontiguousarray(scales, dtype=np.uint16)
+    b = np.ascontiguousarray(biases, dtype=np.uint16)
+    n = qmoe_tiled4_bytes(rows, cols)
+    if n == 0:
+        raise QmoeError("qmoe_tiled4_bytes", 2)
+    out = np.empty(n, dtype=np.uint8)
+    _check("qmoe_repack_tiled4", _lib.qmoe_repack_tiled4(
+        q.ctypes.data, s.ctypes.data, b.ctypes.data, rows, cols, out.ctypes.data, n))
+    return out
+
+
+def qmoe_gemv_tiled4(tiled, rows: int, cols: int, x, y, row_blocks_per_wave: int = 0,
+                     stream=None) -> None:
+    _check("qmoe_gemv_tiled4", _lib.qmoe_gemv_tiled4(_ptr(tiled), rows, cols, _ptr(x), _ptr(y),
+                                                      row_blocks_per_wave, _stream(stream)))
 
 
 def qmoe_router_topk(Wr: QTensor, logit_bias, x, T: int, top_k: int, idx, w, logits, ws,

@@ -2,6 +2,7 @@
 // argument validation, workspace sizing, and dispatch to the launchers.
 // Nothing here allocates, frees or synchronises (qmoe_workspace_status
 // excepted, which reads one word back).
+#include <cstring>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -20,6 +21,10 @@ static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 
 namespace qmoe {
 qmoe_status launch_gemv4(const qmoe_qtensor& W, const uint16_t* x, float* y, void* stream);
+size_t tiled4_size(int rows, int cols);
+bool gemv_tiled4_supported(int cols);
+qmoe_status launch_gemv_tiled4(const uint8_t* T, int rows, int cols, const uint16_t* x, float* y,
+                               int rbw, void* stream);
 qmoe_status launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int T, int H,
                            uint16_t* out, void* stream);
 qmoe_status launch_router(const qmoe_qtensor& Wr, const float* lbias, const uint16_t* x, int T,
@@ -165,6 +170,51 @@ qmoe_status qmoe_gemv_affine4(const qmoe_qtensor* W, const uint16_t* x, float* y
   if (W->cols > QMOE_MAX_HIDDEN) return QMOE_ERR_UNSUPPORTED;
   if (!al16(x)) return QMOE_ERR_ALIGN;
   return launch_gemv4(*W, x, y, stream);
+}
+
+size_t qmoe_tiled4_bytes(int32_t rows, int32_t cols) {
+  if (rows < 1 || cols < 64 || cols % 64) return 0;
+  return tiled4_size(rows, cols);
+}
+
+// Host-side gather into the tiled order (see include/qmoe.h); rows past
+// `rows` stay zero.
+qmoe_status qmoe_repack_tiled4(const uint8_t* q, const uint16_t* scales, const uint16_t* biases,
+                               int32_t rows, int32_t cols, void* out, size_t out_bytes) {
+  if (!q || !scales || !biases || !out) return QMOE_ERR_NULL_ARG;
+  const size_t need = qmoe_tiled4_bytes(rows, cols);
+  if (need == 0) return QMOE_ERR_BAD_SHAPE;
+  if (out_bytes < need) return QMOE_ERR_WORKSPACE;
+  const int64_t CH = cols / 32, G = cols / 64, RB = (rows + 7) / 8;
+  uint8_t* o = static_cast<uint8_t*>(out);
+  std::memset(o, 0, need);
+  for (int64_t rb = 0; rb < RB; ++rb)
+    for (int64_t c = 0; c < CH; ++c)
+      for (int64_t r = 0; r < 8; ++r) {
+        const int64_t row = rb * 8 + r;
+        if (row < rows) std::memcpy(o + ((rb * CH + c) * 8 + r) * 16, q + (row * CH + c) * 16, 16);
+      }
+  uint32_t* pairs = reinterpret_cast<uint32_t*>(o + RB * CH * 8 * 16);
+  for (int64_t rb = 0; rb < RB; ++rb)
+    for (int64_t r = 0; r < 8; ++r) {
+      const int64_t row = rb * 8 + r;
+      if (row >= rows) continue;
+      for (int64_t g = 0; g < G; ++g)
+        pairs[(rb * 8 + r) * G + g] =
+            (uint32_t)scales[row * G + g] | ((uint32_t)biases[row * G + g] << 16);
+    }
+  return QMOE_OK;
+}
+
+qmoe_status qmoe_gemv_tiled4(const void* tiled, int32_t rows, int32_t cols, const uint16_t* x,
+                             float* y, int32_t row_blocks_per_wave, void* stream) {
+  if (!tiled || !x || !y) return QMOE_ERR_NULL_ARG;
+  if (qmoe_tiled4_bytes(rows, cols) == 0) return QMOE_ERR_BAD_SHAPE;
+  if (row_blocks_per_wave < 0 || row_blocks_per_wave > 2) return QMOE_ERR_BAD_SHAPE;
+  if (!gemv_tiled4_supported(cols)) return QMOE_ERR_UNSUPPORTED;
+  if (!al16(tiled) || !al16(x)) return QMOE_ERR_ALIGN;
+  return launch_gemv_tiled4(static_cast<const uint8_t*>(tiled), rows, cols, x, y,
+                            row_blocks_per_wave, stream);
 }
 
 qmoe_status qmoe_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int32_t T, int32_t H,

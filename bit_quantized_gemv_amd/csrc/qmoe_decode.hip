@@ -738,6 +738,101 @@ __global__ __launch_bounds__(kBlock) void k_gemv4(DevQ W, int rows, int cols, co
   if ((lane >> 3) == 0 && row0 + (lane & 7) < rows) y[row0 + (lane & 7)] = acc[0];
 }
 
+// =================================================== tiled 4-bit layout
+// The same affine 4-bit matrix repacked offline (qmoe_repack_tiled4) so
+// that every wave load of a row-block is one contiguous 1 KiB segment:
+//   codes  [RB][CH][8][16 B]  row-block rb, chunk c (32 codes), row r of
+//                             the block: the MLX row's bytes 16c..16c+16
+//   pairs  [RB][8][G] u32     (scale | bias << 16), fp16 bits, group g
+// RB = ceil(rows / 8), CH = cols / 32, G = cols / 64; rows past `rows` are
+// zero.  Step i of a row-block is chunks 8i..8i+8 of its 8 rows: lane
+// (r = lane & 7, p = lane >> 3) reads tile bytes 16 lane of that 1 KiB.
+// The pairs of a row-block are the kernel's LDS table as stored.
+__host__ __device__ inline size_t tiled4_code_bytes(int rows, int cols) {
+  return (size_t)cdiv(rows, kRowsPerUnit) * (cols / 32) * kRowsPerUnit * 16;
+}
+__host__ __device__ inline size_t tiled4_bytes(int rows, int cols) {
+  return tiled4_code_bytes(rows, cols) +
+         (size_t)cdiv(rows, kRowsPerUnit) * kRowsPerUnit * (cols / 64) * 4;
+}
+
+// One wave: RBW consecutive row-blocks, one after the other (one register
+// set: the next row-block's loads are issued when the previous one's math
+// is done).  Per row-block the pairs go straight from memory into the
+// wave's LDS table (global_load_lds: 16 bytes per lane at table + 16 lane,
+// no registers; the table area holds whole 64-lane writes, later lanes
+// repeat the last unit), then the codes are issued; waiting for all but
+// the SP code loads waits for the pairs (loads complete in issue order).
+// x is staged once per block, after the first row-block's loads.  The math
+// is the MLX-layout GEMV's (same operations in the same order, same bits).
+// RBW = 2 gives half the blocks for the same rows: one x staging for more
+// rows, and a grid that fits the resident slots in fewer rounds.
+template <int CHC>
+__host__ __device__ constexpr int gemv4t_table_units() { return 64 * cdiv(CHC, 64); }
+__host__ __device__ inline size_t gemv4t_lds(int cols) {
+  return gu_sb_off(cols) + (size_t)kWavesPerBlock * 64 * cdiv(cols / 32, 64) * 16;
+}
+template <int CHC, int RBW>
+__global__ __launch_bounds__(kBlock, RBW == 2 ? 4 : 1) void k_gemv4t(const uint8_t* T, int rows,
+                                                                     int cols, const uint16_t* x,
+                                                                     float* y) {
+  constexpr int CH = CHC, G = CHC / 2, SP = cdiv(CHC, kSlots);
+  constexpr int NU = cdiv(2 * G, 64);  // 16-byte units of pairs per lane and row-block
+  constexpr int kWaitPairs = (SP & 15) | (7 << 4) | (15 << 8) | ((SP >> 4) << 14);
+  extern __shared__ __align__(16) uint8_t smem[];
+  uint4* xs = reinterpret_cast<uint4*>(smem + kSysBytes);
+  float* xh = reinterpret_cast<float*>(smem + gu_xh_off(cols));
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, r = lane & 7, p = lane >> 3;
+  uint32_t* sbl = reinterpret_cast<uint32_t*>(smem + gu_sb_off(cols)) +
+                  wave * gemv4t_table_units<CHC>() * 4;
+  const int RB = cdiv(rows, kRowsPerUnit);
+  const int rb0 = (blockIdx.x * kWavesPerBlock + wave) * RBW;
+  const uint4* pairs = reinterpret_cast<const uint4*>(T + tiled4_code_bytes(rows, cols));
+  Rows4<1, SP> R;
+  auto load = [&](int j) {
+    const int rb = min(rb0 + j, RB - 1);
+#pragma unroll
+    for (int u = 0; u < NU; ++u)
+      __builtin_amdgcn_global_load_lds(
+          (const QMOE_GLOBAL void*)(pairs + (int64_t)rb * 2 * G + min(lane + 64 * u, 2 * G - 1)),
+          (__attribute__((address_space(3))) void*)(sbl + 256 * u), 16, 0, 0);
+    const uint8_t* tile = T + (size_t)rb * CH * kRowsPerUnit * 16;
+#pragma unroll
+    for (int i = 0; i < SP; ++i) {
+      const int c = min(i * kSlots + p, CH - 1);
+      R.w[0][i] = ldg16(tile + ((size_t)c * kRowsPerUnit + r) * 16);
+    }
+  };
+  auto math = [&](int j) {
+    float acc[1] = {0.f};
+    rows4_compute<1, SP>(R, xs, xh, sbl, r, G, CH, 0, CH, 0, p, acc);
+    acc[0] = rowblock_sum(acc[0]);
+    const int row = (rb0 + j) * kRowsPerUnit + r;
+    if (p == 0 && rb0 + j < RB && row < rows) y[row] = acc[0];
+  };
+  {
+    XRegs X;
+    x_load(X, x, cols);
+    load(0);
+    __builtin_amdgcn_s_waitcnt(kWaitPairs);  // x and the pairs
+    x_stage<true>(X, x, nullptr, 1.f, cols, xs, xh);
+    __syncthreads();
+    math(0);
+  }
+#pragma unroll 1
+  for (int j = 1; j < RBW; ++j) {
+    // the table is this wave's own: every lane's reads of the previous one
+    // are done before the new pairs land
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    load(j);
+    __builtin_amdgcn_s_waitcnt(kWaitPairs);
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    math(j);
+  }
+}
+
 // ============================================================= RMSNorm
 __global__ __launch_bounds__(kBlock) void k_rmsnorm(const uint16_t* x, const uint16_t* gamma,
                                                     float eps, int H, uint16_t* out) {
@@ -1454,6 +1549,31 @@ qmoe_status launch_gemv4(const qmoe_qtensor& W, const uint16_t* x, float* y, voi
     case 22: hipLaunchKernelGGL(k_gemv4<22>, dim3(blocks), dim3(kBlock), lds, S(stream), d, W.rows, W.cols, x, y); break;
     case 16: hipLaunchKernelGGL(k_gemv4<16>, dim3(blocks), dim3(kBlock), lds, S(stream), d, W.rows, W.cols, x, y); break;
     default: hipLaunchKernelGGL(k_gemv4<0>, dim3(blocks), dim3(kBlock), lds, S(stream), d, W.rows, W.cols, x, y); break;
+  }
+  return hipGetLastError() == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
+}
+
+size_t tiled4_size(int rows, int cols) { return tiled4_bytes(rows, cols); }
+
+// Compiled widths: 2816 (the layer's hidden size) and 704 (its expert
+// width); rbw: row-blocks per wave (1 or 2).
+bool gemv_tiled4_supported(int cols) { return cols == 2816 || cols == 704; }
+
+qmoe_status launch_gemv_tiled4(const uint8_t* T, int rows, int cols, const uint16_t* x, float* y,
+                               int rbw, void* stream) {
+  const int RB = cdiv(rows, kRowsPerUnit);
+  const size_t lds = gemv4t_lds(cols);
+  // measured on MI355X, one row-block per wave: width 2816 at 65,536 rows
+  // 18.0 us (0.72 of HBM peak), width 704 at 262,144 rows 17.7 us (0.74);
+  // two per wave 18.5 and 17.9 us
+  if (rbw == 0) rbw = 1;
+  const dim3 grid(cdiv(RB, kWavesPerBlock * rbw));
+  if (cols == 2816) {
+    if (rbw == 2) hipLaunchKernelGGL((k_gemv4t<88, 2>), grid, dim3(kBlock), lds, S(stream), T, rows, cols, x, y);
+    else hipLaunchKernelGGL((k_gemv4t<88, 1>), grid, dim3(kBlock), lds, S(stream), T, rows, cols, x, y);
+  } else {
+    if (rbw == 2) hipLaunchKernelGGL((k_gemv4t<22, 2>), grid, dim3(kBlock), lds, S(stream), T, rows, cols, x, y);
+    else hipLaunchKernelGGL((k_gemv4t<22, 1>), grid, dim3(kBlock), lds, S(stream), T, rows, cols, x, y);
   }
   return hipGetLastError() == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
 }

@@ -114,6 +114,36 @@ typedef struct {
 qmoe_status qmoe_gemv_affine4(const qmoe_qtensor* W, const uint16_t* x, float* y,
                               void* stream);
 
+/* Offline repack of a 4-bit affine matrix into the GPU-tiled layout, and the
+ * GEMV on it (devtrends.cc "Come eseguire un modello da 26 miliardi…",
+ * section "Senza dipendenze da llama.cpp e MLX": a Repack step converts the
+ * downloaded weights once into the engine's own layout; remio.ai
+ * "TurboFieldfare esegue Mac Gemma 4 26B in 2 GB…", section "Mac Gemma 4
+ * 26B entra nello spazio disponibile…").  Same numbers, different order:
+ *   codes  [RB][CH][8][16 B]  row-block rb (8 rows), chunk c (32 codes):
+ *                             the MLX row's code bytes 16c..16c+16
+ *   pairs  [RB][8][G] uint32  scale | bias << 16 (fp16 bits), group g
+ * RB = ceil(rows / 8), CH = cols / 32, G = cols / 64; rows past `rows` are
+ * zero.  One wave load of a row-block is then one contiguous 1 KiB.
+ * qmoe_tiled4_bytes: size of the repacked matrix (0 for invalid shapes:
+ *   rows < 1, cols < 64 or not a multiple of 64).
+ * qmoe_repack_tiled4: HOST memory in and out (an offline step, no GPU):
+ *   q [rows][cols/2] codes (low nibble first), scales and biases fp16
+ *   [rows][cols/64]; out: out_bytes >= qmoe_tiled4_bytes(rows, cols).
+ *   The caller copies `out` to the device.
+ * qmoe_gemv_tiled4: y[r] = sum_c W[r][c] x[c] from the repacked matrix on
+ *   the device (16-byte aligned), x bf16 [cols] (16-byte aligned), y fp32
+ *   [rows]; the same bits as qmoe_gemv_affine4 on the source matrix.
+ *   cols must be 2816 or 704 (the compiled widths; else
+ *   QMOE_ERR_UNSUPPORTED).  row_blocks_per_wave: 1 or 2 (rows per wave
+ *   8 or 16, one row-block after the other), 0 for the library's choice
+ *   (1). */
+size_t qmoe_tiled4_bytes(int32_t rows, int32_t cols);
+qmoe_status qmoe_repack_tiled4(const uint8_t* q, const uint16_t* scales, const uint16_t* biases,
+                               int32_t rows, int32_t cols, void* out, size_t out_bytes);
+qmoe_status qmoe_gemv_tiled4(const void* tiled, int32_t rows, int32_t cols, const uint16_t* x,
+                             float* y, int32_t row_blocks_per_wave, void* stream);
+
 /* Router of T tokens (devtrends.cc "Come eseguire un modello da 26 miliardi…",
  * section "Qual è il trucco principale dell'architettura": a router per
  * layer selects 8 experts; remio.ai "TurboFieldfare esegue Mac Gemma 4 26B
