@@ -80,6 +80,9 @@ def lib():
                                        C.c_void_p, C.c_void_p, C.c_void_p]
             L.orc_lfu_replay.restype = C.c_int64
             L.orc_lfu_replay.argtypes = [C.c_int32] * 4 + [C.c_void_p] * 4
+            L.orc_sample.restype = C.c_int32
+            L.orc_sample.argtypes = [C.c_void_p, C.c_int32, C.c_double, C.c_int32, C.c_double,
+                                     C.c_double, C.c_void_p, C.c_void_p, C.c_void_p]
             _lib = L
     return _lib
 
@@ -256,3 +259,15 @@ def lfu_replay(need: np.ndarray, n_experts: int, slots: int):
     if hits < 0:
         raise RuntimeError("LFU replay found no victim")
     return {"hits": int(hits), "hit": hit, "slot": slot, "victim": victim}
+
+
+def sample(logits: np.ndarray, temperature: float, top_k: int, top_p: float, u: float):
+    """O10: the sampled token id, the ranked top_k ids, their cumulative
+    masses over the total (fp64) and the number of kept ranks."""
+    logits = _c(logits, np.float32)
+    ranked = np.zeros(top_k, dtype=np.int32)
+    cum = np.zeros(top_k, dtype=np.float64)
+    kept = np.zeros(1, dtype=np.int32)
+    tok = lib().orc_sample(_p(logits), logits.size, float(temperature), int(top_k),
+                           float(top_p), float(u), _p(ranked), _p(cum), _p(kept))
+    return {"token": int(tok), "ranked": ranked, "cum": cum, "kept": int(kept[0])}

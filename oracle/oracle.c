@@ -414,3 +414,68 @@ done:
   free(count); free(last); free(holder); free(where); free(needed);
   return hits;
 }
+
+/* ------------------------------------------------------ O10 sampling */
+/* The token choice after the last layer.  [elsolitario] TurboFieldfare
+ * article, section "Cómo empezar": temperature 0.2, top-K 64 and top-P 0.95
+ * by default, temperature 0 for deterministic output; [pikobit] "Un modello
+ * da 26 miliardi di parametri in 2 GB di RAM, su un Mac da 8 GB": default
+ * temperature 0.2; [iitog] technical paragraph: sampling is one of the
+ * engine's kernels.
+ * Readings (the pages give the three parameters only): keep the top_k
+ * largest logits (equal logits: lower token id first), in descending order;
+ * temperature 0 chooses the first; otherwise p_j = exp((l_j - l_0) / T)
+ * over the kept ranks, the top-P cut keeps rank j while the mass of the
+ * ranks before it is below top_p of their total, and the draw u in [0, 1)
+ * picks the first kept rank whose cumulative mass exceeds u times the kept
+ * mass.  Returns the token id.  ranked (top_k ids) and cum (top_k inclusive
+ * cumulative masses over the total) may be NULL; *kept (may be NULL) gets
+ * the number of kept ranks (1 with temperature 0). */
+int32_t orc_sample(const float* logits, int32_t V, double temperature, int32_t top_k,
+                   double top_p, double u, int32_t* ranked, double* cum, int32_t* kept) {
+  if (top_k < 1 || top_k > V) return -1;
+  int32_t* id = (int32_t*)calloc((size_t)top_k, sizeof(int32_t));
+  char* taken = (char*)calloc((size_t)V, 1);
+  for (int32_t j = 0; j < top_k; ++j) {
+    int32_t best = -1;
+    for (int32_t t = 0; t < V; ++t) {
+      if (taken[t]) continue;
+      if (best < 0 || logits[t] > logits[best]) best = t;
+    }
+    taken[best] = 1;
+    id[j] = best;
+  }
+  free(taken);
+  if (ranked)
+    for (int32_t j = 0; j < top_k; ++j) ranked[j] = id[j];
+  int32_t token;
+  if (temperature == 0.0) {
+    token = id[0];
+    if (kept) *kept = 1;
+    if (cum)
+      for (int32_t j = 0; j < top_k; ++j) cum[j] = 1.0;  /* all mass on rank 0 */
+  } else {
+    double* p = (double*)malloc(sizeof(double) * (size_t)top_k);
+    double* c = (double*)malloc(sizeof(double) * (size_t)top_k);
+    const double l0 = (double)logits[id[0]];
+    double total = 0.0;
+    for (int32_t j = 0; j < top_k; ++j) {
+      p[j] = exp(((double)logits[id[j]] - l0) / temperature);
+      total += p[j];
+      c[j] = total;
+    }
+    int32_t m = 0;
+    while (m < top_k && (m == 0 ? 0.0 : c[m - 1]) < top_p * total) ++m;
+    const double target = u * c[m - 1];
+    int32_t r = 0;
+    while (r < m - 1 && !(c[r] > target)) ++r;
+    token = id[r];
+    if (kept) *kept = m;
+    if (cum)
+      for (int32_t j = 0; j < top_k; ++j) cum[j] = c[j] / total;
+    free(p);
+    free(c);
+  }
+  free(id);
+  return token;
+}
