@@ -16,12 +16,13 @@ steps cycle through them, each with its own input token.
 
 The 128-token prefill chunk (router with the Zipf prior, then the grouped
 MFMA prefill) is timed as a second, reported-only leg on the same weights;
-the standalone 4-bit GEMV on a large matrix of the decode width, the
-30-layer stack and (with --streaming) the expert pool are further
-reported-only legs.
+the standalone 4-bit GEMV on a large matrix of the decode width (MLX and
+repacked tiled layouts), token sampling, the 30-layer stack and the expert
+pool (streaming) are further reported-only legs.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
-                    [--no-prefill] [--no-gemv] [--copy-calibration]
+                    [--no-prefill] [--no-gemv] [--no-sampling] [--no-stack]
+                    [--no-streaming] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -139,6 +140,7 @@ def main():
     ap.add_argument("--no-streaming", action="store_true",
                     help="skip the expert-streaming leg (30 layers, pinned host experts, "
                          "16 device slots per layer)")
+    ap.add_argument("--no-sampling", action="store_true", help="skip the token sampling leg")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
     ap.add_argument("--phased", action="store_true",
@@ -311,6 +313,8 @@ def main():
         res["prefill"] = prefill_leg(torch, q, synth, sd, lw, layers, wl, sptr)
     if not args.no_gemv:
         res["gemv"] = gemv_leg(torch, q, sptr)
+    if not args.no_sampling:
+        res["sampling"] = sampling_leg(torch, q, sptr)
     del layers, cstructs
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
@@ -741,6 +745,49 @@ def gemv_leg(torch, q, sptr, rows: int = 65536, cols: int = 2816, copies: int = 
                            "us_per_gemv_rounds": [round(r, 3) for r in reps],
                            "achieved_GBps": gbs, "frac_of_hbm_peak": gbs / HBM_PEAK_GBS},
             "device_copy_GBps_read_plus_write": copy_gbs}
+
+
+def sampling_leg(torch, q, sptr, V: int = 262144, K: int = 64, T: float = 0.2, P: float = 0.95,
+                 n_logits: int = 64, iters: int = 2000):
+    """Token sampling (qmoe_sample) with the pages' defaults (temperature 0.2,
+    top-K 64, top-P 0.95) over a vocabulary of V logits (a reading: the
+    pages give no vocabulary size), n_logits seeded N(0, 2) logit vectors
+    resident on the GPU, seeded uniform draws.  HIP events around `iters`
+    back-to-back calls (two launches each), after as many untimed ones."""
+    import ctypes
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    lg = torch.randn(n_logits, V, device="cuda", generator=g) * 2.0
+    us_draw = np.random.default_rng(78).random(iters)
+    tok = torch.empty(1, dtype=torch.int32, device="cuda")
+    ws = torch.empty(q.qmoe_sample_workspace_bytes(V, K), dtype=torch.uint8, device="cuda")
+    fn = q.lib().qmoe_sample
+    wsb = ws.numel()
+
+    def calls():
+        for i in range(iters):
+            rc = fn(lg[i % n_logits].data_ptr(), V, ctypes.c_float(T), K, ctypes.c_float(P),
+                    ctypes.c_float(float(us_draw[i])), tok.data_ptr(), None, ws.data_ptr(), wsb,
+                    sptr)
+            if rc:
+                raise q.QmoeError("qmoe_sample", rc)
+
+    calls()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    stream = torch.cuda.current_stream()
+    e0.record(stream)
+    calls()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / iters
+    log(f"sampling V={V}: {us:.2f} us per token")
+    return {"workload": f"token sampling, vocabulary {V} (fp32 logits), temperature {T}, "
+                        f"top-K {K}, top-P {P}",
+            "entry": "qmoe_sample (two launches)", "us_per_token": us,
+            "tokens_per_s": 1e6 / us, "logit_bytes": V * 4,
+            "achieved_GBps": V * 4 / (us * 1e-6) / 1e9}
 
 
 def copy_calibration(torch, reps: int = 3):

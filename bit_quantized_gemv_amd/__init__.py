@@ -68,6 +68,10 @@ _vp = C.c_void_p
 _lib.qmoe_status_string.restype = C.c_char_p
 _lib.qmoe_status_string.argtypes = [C.c_int]
 _lib.qmoe_gemv_affine4.argtypes = [C.POINTER(_QT), _vp, _vp, _vp]
+_lib.qmoe_sample_workspace_bytes.restype = C.c_size_t
+_lib.qmoe_sample_workspace_bytes.argtypes = [C.c_int32, C.c_int32]
+_lib.qmoe_sample.argtypes = [_vp, C.c_int32, C.c_float, C.c_int32, C.c_float, C.c_float, _vp, _vp,
+                             _vp, C.c_size_t, _vp]
 _lib.qmoe_tiled4_bytes.restype = C.c_size_t
 _lib.qmoe_tiled4_bytes.argtypes = [C.c_int32, C.c_int32]
 _lib.qmoe_repack_tiled4.argtypes = [_vp, _vp, _vp, C.c_int32, C.c_int32, _vp, C.c_size_t]
@@ -125,7 +129,7 @@ for _f in ("qmoe_gemv_affine4", "qmoe_router_topk", "qmoe_expert_ffn", "qmoe_moe
            "qmoe_expert_ffn_shared", "qmoe_expert_ffn_routed", "qmoe_pool_create",
            "qmoe_pool_plan", "qmoe_pool_acquire", "qmoe_pool_stats_get",
            "qmoe_stack_table_init", "qmoe_stack_decode", "qmoe_workspace_tag_counter",
-           "qmoe_moe_decode_noalloc", "qmoe_repack_tiled4", "qmoe_gemv_tiled4",
+           "qmoe_moe_decode_noalloc", "qmoe_repack_tiled4", "qmoe_gemv_tiled4", "qmoe_sample",
            "qmoe_workspace_raise_tag_counter"):
     getattr(_lib, _f).restype = C.c_int
 
@@ -236,6 +240,18 @@ def qmoe_gemv_affine4(W: QTensor, x, y, stream=None) -> None:
     qt = W.c()
     _check("qmoe_gemv_affine4", _lib.qmoe_gemv_affine4(C.byref(qt), _ptr(x), _ptr(y),
                                                         _stream(stream)))
+
+
+def qmoe_sample_workspace_bytes(V: int, top_k: int) -> int:
+    return int(_lib.qmoe_sample_workspace_bytes(V, top_k))
+
+
+def qmoe_sample(logits, V: int, temperature: float, top_k: int, top_p: float, u: float, token,
+                ranked, ws, stream=None) -> None:
+    _check("qmoe_sample", _lib.qmoe_sample(_ptr(logits), V, float(temperature), top_k,
+                                            float(top_p), float(u), _ptr(token), _ptr(ranked),
+                                            _ptr(ws), ws.numel() * ws.element_size(),
+                                            _stream(stream)))
 
 
 def qmoe_tiled4_bytes(rows: int, cols: int) -> int:

@@ -17,7 +17,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqmoe.so")
 TRACE_LIB = os.path.join(PKG, "libqmoe_trace.so")
-SOURCES = ["qmoe_api.hip", "qmoe_decode.hip", "qmoe_router.hip", "qmoe_prefill.hip", "qmoe_pool.hip"]
+SOURCES = ["qmoe_api.hip", "qmoe_decode.hip", "qmoe_router.hip", "qmoe_prefill.hip", "qmoe_pool.hip",
+           "qmoe_sample.hip"]
 ARCH = "gfx950"
 
 

@@ -22,6 +22,10 @@ static __device__ __align__(256) uint8_t scratch[kScratchBytes];
 namespace qmoe {
 qmoe_status launch_gemv4(const qmoe_qtensor& W, const uint16_t* x, float* y, void* stream);
 size_t tiled4_size(int rows, int cols);
+size_t sample_ws_bytes(int V, int K);
+bool sample_supported(int V, int K);
+qmoe_status launch_sample(const float* logits, int V, float temperature, int K, float top_p,
+                          float u, int32_t* token, int32_t* ranked, uint8_t* ws, void* stream);
 bool gemv_tiled4_supported(int cols);
 qmoe_status launch_gemv_tiled4(const uint8_t* T, int rows, int cols, const uint16_t* x, float* y,
                                int rbw, void* stream);
@@ -170,6 +174,26 @@ qmoe_status qmoe_gemv_affine4(const qmoe_qtensor* W, const uint16_t* x, float* y
   if (W->cols > QMOE_MAX_HIDDEN) return QMOE_ERR_UNSUPPORTED;
   if (!al16(x)) return QMOE_ERR_ALIGN;
   return launch_gemv4(*W, x, y, stream);
+}
+
+size_t qmoe_sample_workspace_bytes(int32_t V, int32_t top_k) {
+  if (V < 1 || top_k < 1) return 0;
+  return sample_ws_bytes(V, top_k);
+}
+
+qmoe_status qmoe_sample(const float* logits, int32_t V, float temperature, int32_t top_k,
+                        float top_p, float u, int32_t* token, int32_t* ranked, void* ws,
+                        size_t ws_bytes, void* stream) {
+  if (!logits || !token || !ws) return QMOE_ERR_NULL_ARG;
+  if (V < 1 || top_k < 1 || top_k > V) return QMOE_ERR_BAD_SHAPE;
+  if (!(temperature >= 0.f) || !(top_p > 0.f && top_p <= 1.f) || !(u >= 0.f && u < 1.f))
+    return QMOE_ERR_BAD_SHAPE;
+  if (!sample_supported(V, top_k)) return QMOE_ERR_UNSUPPORTED;
+  if (ws_bytes < sample_ws_bytes(V, top_k)) return QMOE_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % 8 || reinterpret_cast<uintptr_t>(logits) % 4)
+    return QMOE_ERR_ALIGN;
+  return launch_sample(logits, V, temperature, top_k, top_p, u, token, ranked,
+                       static_cast<uint8_t*>(ws), stream);
 }
 
 size_t qmoe_tiled4_bytes(int32_t rows, int32_t cols) {

@@ -138,6 +138,28 @@ qmoe_status qmoe_gemv_affine4(const qmoe_qtensor* W, const uint16_t* x, float* y
  *   QMOE_ERR_UNSUPPORTED).  row_blocks_per_wave: 1 or 2 (rows per wave
  *   8 or 16, one row-block after the other), 0 for the library's choice
  *   (1). */
+/* The token choice after the last layer (elsolitario.org, TurboFieldfare
+ * article, section "Cómo empezar": temperature 0.2, top-K 64, top-P 0.95 by
+ * default, temperature 0 for a deterministic choice; iitog.ru
+ * "TurboFieldfare: движок с открытым кодом…", technical paragraph: a
+ * sampling kernel).  Keep the top_k largest logits (equal logits: lower
+ * token id first), in descending order.  temperature 0: token = rank 0.
+ * Otherwise p_j = exp((l_j - l_0) / temperature) over the kept ranks; rank j
+ * stays while the mass of the ranks before it is below top_p of the total;
+ * the draw u in [0, 1) (the caller's uniform variate) takes the first kept
+ * rank whose cumulative mass exceeds u times the kept mass (sums in rank
+ * order, fp32).
+ * logits: fp32 [V] on the device (finite).  token: int32 [1] on the device.
+ * ranked: int32 [top_k] on the device (the kept-set candidates in rank
+ * order) or NULL.  1 <= V <= 1,048,576; 1 <= top_k <= min(64, V);
+ * 0 < top_p <= 1; temperature >= 0; 0 <= u < 1; else QMOE_ERR_BAD_SHAPE
+ * (QMOE_ERR_UNSUPPORTED for V or top_k past the limits).
+ * ws: at least qmoe_sample_workspace_bytes(V, top_k) bytes. */
+size_t qmoe_sample_workspace_bytes(int32_t V, int32_t top_k);
+qmoe_status qmoe_sample(const float* logits, int32_t V, float temperature, int32_t top_k,
+                        float top_p, float u, int32_t* token, int32_t* ranked, void* ws,
+                        size_t ws_bytes, void* stream);
+
 size_t qmoe_tiled4_bytes(int32_t rows, int32_t cols);
 qmoe_status qmoe_repack_tiled4(const uint8_t* q, const uint16_t* scales, const uint16_t* biases,
                                int32_t rows, int32_t cols, void* out, size_t out_bytes);

@@ -154,3 +154,24 @@ def test_one_hip_runtime_whatever_the_import_order():
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr
     assert r.stdout.split()[0] == "1", r.stdout
+
+
+def test_sample_validation_before_launch():
+    """qmoe_sample rejects bad arguments on the host (the pointers below are
+    never read)."""
+    import bit_quantized_gemv_amd as q
+
+    lib = q.lib()
+    ws = 1 << 20
+    call = lambda V, T, K, P, U, wsb=ws: lib.qmoe_sample(0x1000, V, T, K, P, U, 0x2000, None,
+                                                          0x3000, wsb, None)
+    assert call(262144, 0.2, 65, 0.95, 0.5) == 3    # QMOE_ERR_UNSUPPORTED: top_k > 64
+    assert call(32, 0.2, 64, 0.95, 0.5) == 2        # QMOE_ERR_BAD_SHAPE: top_k > V
+    assert call(1 << 21, 0.2, 64, 0.95, 0.5) == 3   # past the vocabulary limit
+    assert call(1000, -0.1, 64, 0.95, 0.5) == 2     # negative temperature
+    assert call(1000, 0.2, 64, 0.0, 0.5) == 2       # top_p must be > 0
+    assert call(1000, 0.2, 64, 1.5, 0.5) == 2       # top_p <= 1
+    assert call(1000, 0.2, 64, 0.95, 1.0) == 2      # u < 1
+    assert call(262144, 0.2, 64, 0.95, 0.5, 100) == 4  # QMOE_ERR_WORKSPACE
+    assert q.qmoe_sample_workspace_bytes(262144, 64) == 64 * 64 * 8
+    assert q.qmoe_sample_workspace_bytes(1 << 20, 64) == 256 * 64 * 8
