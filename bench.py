@@ -17,12 +17,13 @@ steps cycle through them, each with its own input token.
 The 128-token prefill chunk (router with the Zipf prior, then the grouped
 MFMA prefill) is timed as a second, reported-only leg on the same weights;
 the standalone 4-bit GEMV on a large matrix of the decode width (MLX and
-repacked tiled layouts), token sampling, the 30-layer stack and the expert
-pool (streaming) are further reported-only legs.
+repacked tiled layouts), token sampling, the 30-layer stack, the expert
+pool (streaming from pinned host memory) and the file-backed expert tier
+are further reported-only legs.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
                     [--no-prefill] [--no-gemv] [--no-sampling] [--no-stack]
-                    [--no-streaming] [--copy-calibration]
+                    [--no-streaming] [--no-file-tier] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -141,6 +142,8 @@ def main():
                     help="skip the expert-streaming leg (30 layers, pinned host experts, "
                          "16 device slots per layer)")
     ap.add_argument("--no-sampling", action="store_true", help="skip the token sampling leg")
+    ap.add_argument("--no-file-tier", action="store_true",
+                    help="skip the file-backed expert tier leg (8 layers read from a file)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for counter scaling)")
     ap.add_argument("--phased", action="store_true",
@@ -322,6 +325,14 @@ def main():
         res["stack"] = stack_leg(torch, q, synth, sd, sptr)
     if not args.no_streaming:
         res["streaming"] = streaming_leg(torch, q, synth, sd)
+    if not args.no_file_tier:
+        # reported only, and it depends on the host's storage: a failure is
+        # recorded in its entry instead of ending the run
+        try:
+            res["file_tier"] = file_tier_leg(torch, q, synth, sd)
+        except Exception as exc:  # noqa: BLE001
+            log(f"file tier leg failed: {exc!r}")
+            res["file_tier"] = {"error": repr(exc)}
     if args.copy_calibration:
         copy_calibration(torch)
     if not args.no_cpu_baseline:
@@ -788,6 +799,115 @@ def sampling_leg(torch, q, sptr, V: int = 262144, K: int = 64, T: float = 0.2, P
             "entry": "qmoe_sample (two launches)", "us_per_token": us,
             "tokens_per_s": 1e6 / us, "logit_bytes": V * 4,
             "achieved_GBps": V * 4 / (us * 1e-6) / 1e9}
+
+
+def file_tier_leg(torch, q, synth, sd, n_layers: int = 8, steps: int = 256, threads: int = 8):
+    """The file-backed expert tier: the first n_layers layers of the
+    streaming workload (hidden 2816, 128 experts, top-8, 16 device slots per
+    layer, Zipf(1.1) prior), every routed expert in an expert-major file
+    (4 KiB-aligned strides), read on a miss by `threads` workers into pinned
+    staging, then copied to the layer's slots on a side stream while the
+    shared expert runs.  O_DIRECT when the file system takes it; otherwise
+    buffered reads after the file's pages are dropped from the page cache
+    (posix_fadvise DONTNEED after fsync).  Storage GB/s = bytes read / time
+    in reads; effective = bytes read / run time."""
+    import tempfile
+
+    st = synth.WORKLOADS["streaming_decode"]
+    L, E, K, H, S = n_layers, st.n_experts, st.top_k, st.hidden, st.slots
+    log(f"file tier: generating {L} layers")
+    lws = [synth.make_layer(st, l) for l in range(L)]
+    blob = lws[0].layout.nbytes
+    stride = -(-blob // 4096) * 4096
+    tmpdir = tempfile.mkdtemp(prefix="qmoe_ft_", dir=os.environ.get("TMPDIR") or "/tmp")
+    path = os.path.join(tmpdir, "experts.bin")
+    pad = np.zeros(stride - blob, dtype=np.uint8)
+    with open(path, "wb") as f:
+        for lw in lws:
+            for e in range(E):
+                f.write(lw.blobs[e].tobytes())
+                f.write(pad.tobytes())
+            lw.blobs = lw.blobs[:1]  # the file now holds the experts
+        f.flush()
+        os.fsync(f.fileno())
+    fd = os.open(path, os.O_RDONLY)
+    os.posix_fadvise(fd, 0, 0, os.POSIX_FADV_DONTNEED)
+    os.close(fd)
+    direct = True
+    try:
+        tier = q.FileTier(path, L, E, blob, stride, threads=threads, direct=True)
+    except q.QmoeError:
+        direct = False
+        tier = q.FileTier(path, L, E, blob, stride, threads=threads, direct=False)
+    arenas = [torch.zeros((S, blob), dtype=torch.uint8, device="cuda") for _ in range(L)]
+    dls = [sd.DeviceLayer(lw, blobs=arenas[l]) for l, lw in enumerate(lws)]
+    pool = q.Pool(L, E, S, blob, None, [a.data_ptr() for a in arenas])
+    maps = [torch.zeros(E, dtype=torch.int32, device="cuda") for _ in range(L)]
+    X = torch.from_numpy(synth.make_tokens(st, steps, stream=6).view(np.int16)).cuda()
+    compute = torch.cuda.current_stream()
+    copy = torch.cuda.Stream()
+    rws = torch.zeros(q.qmoe_router_workspace_bytes(E, 1), dtype=torch.uint8, device="cuda")
+    idx = torch.empty(K, dtype=torch.int32, device="cuda")
+    w = torch.empty(K, dtype=torch.float32, device="cuda")
+    idx_h = torch.empty(K, dtype=torch.int32, pin_memory=True)
+    h = torch.empty(H, dtype=torch.int16, device="cuda")
+    buf = [torch.empty(H, dtype=torch.int16, device="cuda") for _ in range(2)]
+    ev_idx = torch.cuda.Event()
+    ready = torch.cuda.Event()
+    ready.record(copy)
+    ws = dls[0].layer.new_workspace(1)
+    half = None
+    t0 = time.perf_counter()
+    for t in range(steps):
+        x = X[t]
+        for l, dl in enumerate(dls):
+            Ly = dl.layer
+            q.qmoe_rmsnorm(x, dl.gamma, 1e-6, 1, H, h)
+            q.qmoe_router_topk(Ly.router, dl.logit_bias, h, 1, K, idx, w, None, rws)
+            idx_h.copy_(idx, non_blocking=True)
+            ev_idx.record(compute)
+            q.qmoe_expert_ffn_shared(Ly, h, ws)
+            ev_idx.synchronize()
+            pool.acquire_file(tier, l, idx_h.data_ptr(), K, maps[l], copy, ready.cuda_event)
+            compute.wait_event(ready)
+            out = buf[l & 1]
+            q.qmoe_expert_ffn_routed(Ly, h, idx, w, maps[l], x, out, ws)
+            x = out
+        if t == steps // 2 - 1:
+            torch.cuda.synchronize()
+            half = (time.perf_counter(), pool.stats(), tier.stats())
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    if q.qmoe_workspace_status(ws) != 0:
+        raise SystemExit("device wait failure in the file tier leg")
+    ps, fs = pool.stats(), tier.stats()
+    th, ph, fh = half
+    whits, wmiss = ps.hits - ph.hits, ps.misses - ph.misses
+    res = {"workload": f"first {L} layers of the streaming workload (hidden 2816, 128 experts, "
+                       f"top-8, 16 device slots per layer, Zipf(1.1) prior), routed experts in "
+                       f"an expert-major file of {L * E * stride / 1e9:.2f} GB",
+           "steps": steps, "reader_threads": threads,
+           "io": "O_DIRECT" if direct else "buffered, page cache dropped after writing",
+           "tokens_per_s": steps / (t1 - t0), "layer_steps_per_s": steps * L / (t1 - t0),
+           "hit_rate": ps.hits / (ps.hits + ps.misses),
+           "hit_rate_warm": whits / max(1, whits + wmiss),
+           "reads": fs.reads, "read_bytes": fs.read_bytes,
+           "storage_GBps_in_reads": fs.read_bytes / max(1, fs.read_ns),
+           "storage_GBps_in_reads_warm": (fs.read_bytes - fh.read_bytes) /
+                                         max(1, fs.read_ns - fh.read_ns),
+           "read_share_of_run": fs.read_ns * 1e-9 / (t1 - t0),
+           "effective_GBps": fs.read_bytes / (t1 - t0) / 1e9}
+    log(f"file tier ({res['io']}): {res['tokens_per_s']:.1f} tokens/s over {L} layers, hit rate "
+        f"{res['hit_rate']:.3f}, {res['storage_GBps_in_reads']:.2f} GB/s in reads, reads "
+        f"{100 * res['read_share_of_run']:.0f}% of the run")
+    tier.close()
+    pool.close()
+    del dls, arenas
+    os.remove(path)
+    os.rmdir(tmpdir)
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
 
 
 def copy_calibration(torch, reps: int = 3):

@@ -108,6 +108,20 @@ _lib.qmoe_pool_acquire.argtypes = [_vp, C.c_int32, _vp, C.c_int32, _vp, _vp, _vp
 _lib.qmoe_pool_stats_get.argtypes = [_vp, C.POINTER(PoolStats)]
 _lib.qmoe_pool_destroy.argtypes = [_vp]
 _lib.qmoe_pool_destroy.restype = None
+
+
+class FileTierStats(C.Structure):
+    _fields_ = [("reads", C.c_int64), ("read_bytes", C.c_int64), ("read_ns", C.c_int64),
+                ("last_errno", C.c_int32)]
+
+
+_lib.qmoe_file_tier_open.argtypes = [C.c_char_p, C.c_int32, C.c_int32, C.c_size_t, C.c_size_t,
+                                     C.c_int32, C.c_int32, C.c_int32, C.POINTER(_vp)]
+_lib.qmoe_pool_acquire_file.argtypes = [_vp, _vp, C.c_int32, _vp, C.c_int32, _vp, _vp, _vp,
+                                        C.POINTER(PoolStats)]
+_lib.qmoe_file_tier_stats_get.argtypes = [_vp, C.POINTER(FileTierStats)]
+_lib.qmoe_file_tier_close.argtypes = [_vp]
+_lib.qmoe_file_tier_close.restype = None
 _lib.qmoe_rmsnorm.argtypes = [_vp, _vp, C.c_float, C.c_int32, C.c_int32, _vp, _vp]
 _lib.qmoe_workspace_bytes.restype = C.c_size_t
 _lib.qmoe_workspace_bytes.argtypes = [C.POINTER(_Layer), C.c_int32]
@@ -127,7 +141,8 @@ for _f in ("qmoe_gemv_affine4", "qmoe_router_topk", "qmoe_expert_ffn", "qmoe_moe
            "qmoe_moe_decode_phased", "qmoe_prefill_grouped", "qmoe_rmsnorm",
            "qmoe_workspace_status", "qmoe_prefill_dispatch_offsets", "qmoe_moe_decode_timed",
            "qmoe_expert_ffn_shared", "qmoe_expert_ffn_routed", "qmoe_pool_create",
-           "qmoe_pool_plan", "qmoe_pool_acquire", "qmoe_pool_stats_get",
+           "qmoe_pool_plan", "qmoe_pool_acquire", "qmoe_pool_stats_get", "qmoe_file_tier_open",
+           "qmoe_pool_acquire_file", "qmoe_file_tier_stats_get",
            "qmoe_stack_table_init", "qmoe_stack_decode", "qmoe_workspace_tag_counter",
            "qmoe_moe_decode_noalloc", "qmoe_repack_tiled4", "qmoe_gemv_tiled4", "qmoe_sample",
            "qmoe_workspace_raise_tag_counter"):
@@ -312,7 +327,8 @@ class Pool:
     """The host-resident expert pool (qmoe_pool_*).  ``host_blobs``: one
     pinned host address per (layer, expert), layer-major; ``arenas``: one
     device address per layer (``slots`` blobs each).  Both None: a
-    planning-only pool."""
+    planning-only pool; ``arenas`` alone: a file-backed pool (filled by
+    acquire_file)."""
 
     def __init__(self, layers: int, experts: int, slots: int, blob_bytes: int,
                  host_blobs=None, arenas=None):
@@ -320,8 +336,10 @@ class Pool:
         hb = ar = None
         if host_blobs is not None:
             self._hb = (_vp * (layers * experts))(*host_blobs)
+            hb = self._hb
+        if arenas is not None:
             self._ar = (_vp * layers)(*arenas)
-            hb, ar = self._hb, self._ar
+            ar = self._ar
         h = _vp()
         _check("qmoe_pool_create", _lib.qmoe_pool_create(layers, experts, slots, blob_bytes,
                                                           hb, ar, C.byref(h)))
@@ -348,6 +366,14 @@ class Pool:
             ready_event, C.byref(st)))
         return st
 
+    def acquire_file(self, tier: "FileTier", layer: int, host_idx_ptr: int, k: int,
+                     dev_expert_slot, copy_stream, ready_event: int) -> PoolStats:
+        st = PoolStats()
+        _check("qmoe_pool_acquire_file", _lib.qmoe_pool_acquire_file(
+            self._h, tier._h, layer, host_idx_ptr, k, _ptr(dev_expert_slot),
+            _stream(copy_stream), ready_event, C.byref(st)))
+        return st
+
     def stats(self) -> PoolStats:
         st = PoolStats()
         _check("qmoe_pool_stats_get", _lib.qmoe_pool_stats_get(self._h, C.byref(st)))
@@ -356,6 +382,32 @@ class Pool:
     def close(self) -> None:
         if getattr(self, "_h", None):
             _lib.qmoe_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        self.close()
+
+
+class FileTier:
+    """The file-backed expert tier (qmoe_file_tier_*): blobs of an
+    expert-major file, read by ``threads`` workers into pinned staging."""
+
+    def __init__(self, path: str, layers: int, experts: int, blob_bytes: int, stride: int,
+                 threads: int = 8, max_misses: int = 8, direct: bool = False):
+        h = _vp()
+        _check("qmoe_file_tier_open", _lib.qmoe_file_tier_open(
+            path.encode(), layers, experts, blob_bytes, stride, threads, max_misses,
+            1 if direct else 0, C.byref(h)))
+        self._h = h
+
+    def stats(self) -> FileTierStats:
+        st = FileTierStats()
+        _check("qmoe_file_tier_stats_get", _lib.qmoe_file_tier_stats_get(self._h, C.byref(st)))
+        return st
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            _lib.qmoe_file_tier_close(self._h)
             self._h = None
 
     def __del__(self):

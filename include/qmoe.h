@@ -408,6 +408,8 @@ typedef struct {
 
 /* host_blobs and dev_slot_arena may both be NULL: a planning-only pool
  * (bookkeeping without copies, usable without a GPU; see qmoe_pool_plan).
+ * dev_slot_arena without host_blobs: a file-backed pool (filled only by
+ * qmoe_pool_acquire_file).
  * Allocates host memory only (bookkeeping and two pinned expert -> slot
  * staging maps per layer). */
 qmoe_status qmoe_pool_create(int32_t layers, int32_t experts, int32_t slots,
@@ -434,6 +436,45 @@ qmoe_status qmoe_pool_acquire(qmoe_pool* pool, int32_t layer, const int32_t* hos
                               void* ready, qmoe_pool_stats* st);
 qmoe_status qmoe_pool_stats_get(const qmoe_pool* pool, qmoe_pool_stats* st);
 void qmoe_pool_destroy(qmoe_pool* pool);
+
+/* File-backed expert tier (devtrends.cc "Come eseguire un modello da 26
+ * miliardi…", section "Qual è il trucco principale dell'architettura": the
+ * CPU compares the router's choice with the cache and issues bounded
+ * parallel reads for the missing experts while the shared expert computes;
+ * remio.ai "TurboFieldfare esegue Mac Gemma 4 26B in 2 GB…", section
+ * "L'affermazione dei 2 GB trasforma la larghezza di banda dell'SSD nel
+ * nuovo vincolo": storage bandwidth becomes the constraint).
+ *
+ * The file is expert-major: the blob of (layer, e) (blob_bytes, the same
+ * bytes as a host blob of the pool) at byte offset (layer * experts + e) *
+ * stride, stride >= blob_bytes and a multiple of 4096.  `threads` worker
+ * threads (1..64) pread whole strides into pinned staging buffers (two sets
+ * of max_misses strides, 1 <= max_misses <= 8, used in turn); with direct
+ * != 0 the file is opened O_DIRECT and one stride is read at once to check
+ * that the file system takes it (QMOE_ERR_UNSUPPORTED if not).
+ * Errors: QMOE_ERR_BAD_SHAPE for a missing or short file or bad sizes,
+ * QMOE_ERR_ALIGN for a stride not a multiple of 4096.
+ *
+ * qmoe_pool_acquire_file: as qmoe_pool_acquire for a pool created with
+ * dev_slot_arena and host_blobs == NULL (a file-backed pool): one LFU step,
+ * then the missing blobs are read from the file (the call returns after the
+ * reads; QMOE_ERR_HIP if a read failed) and copied host -> device on
+ * copy_stream, then the map and `ready`.  k <= max_misses.  Calls on one
+ * tier must not overlap. */
+typedef struct qmoe_file_tier qmoe_file_tier;
+typedef struct {
+  int64_t reads, read_bytes; /* cumulative blobs and bytes read (whole strides) */
+  int64_t read_ns;           /* wall time spent in the reads (all workers busy or done) */
+  int32_t last_errno;        /* errno of the last failed read (-1: end of file), else 0 */
+} qmoe_file_tier_stats;
+qmoe_status qmoe_file_tier_open(const char* path, int32_t layers, int32_t experts,
+                                size_t blob_bytes, size_t stride, int32_t threads,
+                                int32_t max_misses, int32_t direct, qmoe_file_tier** out);
+qmoe_status qmoe_pool_acquire_file(qmoe_pool* pool, qmoe_file_tier* tier, int32_t layer,
+                                   const int32_t* host_idx, int32_t k, int32_t* dev_expert_slot,
+                                   void* copy_stream, void* ready, qmoe_pool_stats* st);
+qmoe_status qmoe_file_tier_stats_get(const qmoe_file_tier* tier, qmoe_file_tier_stats* st);
+void qmoe_file_tier_close(qmoe_file_tier* tier);
 
 #ifdef __cplusplus
 }

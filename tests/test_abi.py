@@ -175,3 +175,27 @@ def test_sample_validation_before_launch():
     assert call(262144, 0.2, 64, 0.95, 0.5, 100) == 4  # QMOE_ERR_WORKSPACE
     assert q.qmoe_sample_workspace_bytes(262144, 64) == 64 * 64 * 8
     assert q.qmoe_sample_workspace_bytes(1 << 20, 64) == 256 * 64 * 8
+
+
+def test_file_tier_validation_before_any_gpu_call(tmp_path):
+    """qmoe_file_tier_open checks its file and sizes before it allocates
+    pinned memory or starts threads."""
+    import ctypes as C
+
+    import bit_quantized_gemv_amd as q
+
+    lib = q.lib()
+    h = C.c_void_p()
+    missing = str(tmp_path / "none.bin").encode()
+    assert lib.qmoe_file_tier_open(missing, 2, 4, 8192, 8192, 2, 8, 0, C.byref(h)) == 2
+    assert lib.qmoe_file_tier_open(missing, 2, 4, 4000, 8000, 2, 8, 0, C.byref(h)) == 5  # stride
+    short = tmp_path / "short.bin"
+    short.write_bytes(b"\0" * (2 * 4 * 8192 - 1))
+    assert lib.qmoe_file_tier_open(str(short).encode(), 2, 4, 8192, 8192, 2, 8, 0,
+                                   C.byref(h)) == 2
+    assert lib.qmoe_file_tier_open(str(short).encode(), 2, 4, 8192, 8192, 0, 8, 0,
+                                   C.byref(h)) == 2  # threads
+    assert lib.qmoe_file_tier_open(str(short).encode(), 2, 4, 8192, 8192, 2, 9, 0,
+                                   C.byref(h)) == 2  # max_misses > 8
+    assert lib.qmoe_file_tier_open(str(short).encode(), 2, 4, 9000, 8192, 2, 8, 0,
+                                   C.byref(h)) == 2  # stride < blob

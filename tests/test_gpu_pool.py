@@ -15,9 +15,10 @@ from tests.helpers import (bf16_to_f64, log, rel_l2, routing_bound, routing_cert
 pytestmark = pytest.mark.gpu
 
 
-def _flow(torch, q, WL, dls, X, pool=None, slot_maps=None, trace=None):
-    """RMSNorm -> router -> shared gate/up -> (pool acquire) -> routed part,
-    layer after layer, token after token.  Returns every layer's output."""
+def _flow(torch, q, WL, dls, X, pool=None, slot_maps=None, trace=None, tier=None):
+    """RMSNorm -> router -> shared gate/up -> (pool acquire, from the file
+    tier if one is given) -> routed part, layer after layer, token after
+    token.  Returns every layer's output."""
     H, K = WL.hidden, WL.top_k
     compute = torch.cuda.current_stream()
     copy = torch.cuda.Stream()
@@ -47,7 +48,11 @@ def _flow(torch, q, WL, dls, X, pool=None, slot_maps=None, trace=None):
             if pool is not None:
                 ev_idx.synchronize()
                 smap = slot_maps[l]
-                st = pool.acquire(l, idx_h.data_ptr(), K, smap, copy, ready.cuda_event)
+                if tier is None:
+                    st = pool.acquire(l, idx_h.data_ptr(), K, smap, copy, ready.cuda_event)
+                else:
+                    st = pool.acquire_file(tier, l, idx_h.data_ptr(), K, smap, copy,
+                                           ready.cuda_event)
                 compute.wait_event(ready)
             out = torch.empty(H, dtype=torch.int16, device="cuda")
             q.qmoe_expert_ffn_routed(L, h, idx_d, w_d, smap, x, out, ws)
@@ -150,3 +155,53 @@ def test_pool_streaming_equals_resident_and_oracle(name):
     pool.close()
 
 
+def test_file_tier_streaming_equals_resident(tmp_path):
+    """The routed experts read from an expert-major file (4 KiB-aligned
+    strides, 8 reader threads) into the 16-slot pool: bit-identical to the
+    resident run, one read per miss, and the same hits and misses as the
+    pinned-host pool's LFU.  O_DIRECT when the file system takes it."""
+    import torch
+
+    import bit_quantized_gemv_amd as q
+
+    WL = synth.WORKLOADS["tiny_streaming_decode"]
+    layers = [synth.make_layer(WL, l) for l in range(WL.layers)]
+    E, K, S = WL.n_experts, WL.top_k, WL.slots
+    blob = layers[0].layout.nbytes
+    stride = -(-blob // 4096) * 4096
+    path = tmp_path / "experts.bin"
+    with open(path, "wb") as f:
+        for lw in layers:
+            for e in range(E):
+                f.write(lw.blobs[e].tobytes())
+                f.write(b"\0" * (stride - blob))
+    X = synth.make_tokens(WL, WL.tokens, stream=93)
+    prior = [synth.zipf_prior(WL, l) for l in range(WL.layers)]
+    res_dls = [synth.device.DeviceLayer(lw, logit_bias=prior[l]) for l, lw in enumerate(layers)]
+    ref = _flow(torch, q, WL, res_dls, X)
+    arenas = [torch.zeros((S, blob), dtype=torch.uint8, device="cuda") for _ in layers]
+    dls = [synth.device.DeviceLayer(lw, logit_bias=prior[l], blobs=arenas[l])
+           for l, lw in enumerate(layers)]
+    for direct in (True, False):
+        try:
+            tier = q.FileTier(str(path), WL.layers, E, blob, stride, threads=8, direct=direct)
+        except q.QmoeError:
+            assert direct, "buffered open must work"
+            log("file system refuses O_DIRECT: buffered reads only")
+            continue
+        pool = q.Pool(WL.layers, E, S, blob, None, [a.data_ptr() for a in arenas])
+        maps = [torch.zeros(E, dtype=torch.int32, device="cuda") for _ in layers]
+        try:
+            got = _flow(torch, q, WL, dls, X, pool=pool, slot_maps=maps, tier=tier)
+        except q.QmoeError:
+            raise AssertionError(f"read failed, errno {tier.stats().last_errno}")
+        for t in range(len(X)):
+            for l in range(WL.layers):
+                assert np.array_equal(got[t][l], ref[t][l]), (direct, t, l)
+        ps, fs = pool.stats(), tier.stats()
+        assert fs.reads == ps.misses and fs.read_bytes == ps.misses * stride
+        assert ps.hits + ps.misses == len(X) * WL.layers * K
+        log(f"file tier (direct={direct}): {ps.misses} reads, "
+            f"{fs.read_bytes / max(1, fs.read_ns) :.2f} GB/s in reads")
+        tier.close()
+        pool.close()
