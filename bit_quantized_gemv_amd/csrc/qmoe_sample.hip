@@ -20,8 +20,9 @@
 //          0..3 the top-K of four waves' each, wave 0 the top-K of theirs
 //          in rank order, then the softmax, the cut and the draw
 // A key is (order value of the logit) << 32 | ~id: one unsigned order for
-// "larger logit, then lower id", unique per token; missing entries are 0,
-// below every real key.
+// "larger logit, then lower id", unique per token; missing entries get keys
+// of order 0 (below every real key), each a different one, so every key of
+// a selection is unique.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -40,10 +41,14 @@ constexpr int kSmpMaxBlocks = kSmpFinalWaves * kSmpPerWave / 64;  // K <= 64 key
 __device__ __forceinline__ uint64_t smp_key(float l, uint32_t id) {
   return ((uint64_t)topk_ord(l) << 32) | (uint32_t)~id;
 }
+// Key of a missing entry number u: order value 0 (below every logit), and
+// distinct for distinct u (u < 2^30), so that all keys of a selection are
+// unique.  Numbering: token ids past V; 2^21 + position for padding.
+__device__ __forceinline__ uint64_t smp_pad(uint32_t u) { return (uint64_t)(uint32_t)~u; }
+constexpr uint32_t kPadBase = 1u << 21;
 
 // One wave: the K (<= 64) largest of the NV * 64 keys k[m] (lane + 64 m),
-// written to out[0..K) in descending order.  Keys are unique except the
-// zero keys of missing entries, which tie by position.
+// written to out[0..K) in descending order.  The keys are unique.
 //   1. T, bit by bit from the top: keep a bit when at least K keys are >=
 //      the prefix with it; when exactly K are, those are the K largest and
 //      the search ends (real keys part after a few dozen bits at most);
@@ -54,10 +59,7 @@ template <int NV>
 __device__ void wave_topk_keys(const uint64_t (&k)[NV], int K, uint64_t* xch, uint64_t* out,
                                int lane) {
   uint64_t T = 0;
-  uint32_t real = 0;  // with at most K real keys, all of them and zeros: T = 0
-#pragma unroll
-  for (int m = 0; m < NV; ++m) real += (uint32_t)__popcll(__ballot(k[m] != 0ull));
-  for (int b = real > (uint32_t)K ? 63 : -1; b >= 0; --b) {
+  for (int b = 63; b >= 0; --b) {
     const uint64_t c = T | (1ull << b);
     uint32_t n = 0;
 #pragma unroll
@@ -84,16 +86,12 @@ __device__ void wave_topk_keys(const uint64_t (&k)[NV], int K, uint64_t* xch, ui
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   {
-    // every lane reads all 64 slots, with no branch between the reads (the
-    // slots past K hold stale keys; a mask drops them)
+    // rank = keys greater (unique keys); every lane reads all 64 slots with
+    // no branch between the reads (past K: stale keys, masked)
     const uint64_t kj = xch[lane];
     uint32_t r = 0;
 #pragma unroll 16
-    for (int i = 0; i < 64; ++i) {
-      const uint64_t ki = xch[i];
-      const uint32_t before = (uint32_t)(ki > kj) | ((uint32_t)(ki == kj) & (uint32_t)(i < lane));
-      r += before & (uint32_t)(i < K);
-    }
+    for (int i = 0; i < 64; ++i) r += (uint32_t)(xch[i] > kj) & (uint32_t)(i < K);
     if (lane < K) out[r] = kj;
   }
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -110,9 +108,10 @@ __global__ __launch_bounds__(kSmpBlock) void k_sample_local(const float* logits,
 #pragma unroll
   for (int m = 0; m < NV; ++m) {
     const int64_t i = base + lane + 64 * m;
-    k[m] = i < V ? smp_key(logits[i], (uint32_t)i) : 0ull;
+    k[m] = i < V ? smp_key(logits[i], (uint32_t)i) : smp_pad((uint32_t)i);
   }
-  wtop[wave * 64 + lane] = 0ull;  // ranks >= K stay missing
+  // ranks >= K stay missing (distinct per block, wave and lane)
+  wtop[wave * 64 + lane] = smp_pad(kPadBase + (blockIdx.x * 4 + wave) * 64 + lane);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   wave_topk_keys<NV>(k, K, xch[wave], wtop + wave * 64, lane);
   __syncthreads();
@@ -132,13 +131,15 @@ __global__ __launch_bounds__(kSmpFinalWaves * 64) void k_sample_final(
   __shared__ uint64_t wtop[kSmpFinalWaves * 64];
   __shared__ uint64_t top[64];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // padding numbers past the local blocks' (at most 256 * 256 of them)
+  constexpr uint32_t kPadFinal = kPadBase + 256u * 256u;
   uint64_t k[NV0];
 #pragma unroll
   for (int m = 0; m < NV0; ++m) {
     const int i = (wave * NV0 + m) * 64 + lane;
-    k[m] = i < n ? cand[i] : 0ull;
+    k[m] = i < n ? cand[i] : smp_pad(kPadFinal + (uint32_t)i);
   }
-  wtop[wave * 64 + lane] = 0ull;
+  wtop[wave * 64 + lane] = smp_pad(kPadFinal + 16384u + wave * 64 + lane);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   wave_topk_keys<NV0>(k, K, xch[wave], wtop + wave * 64, lane);
   __syncthreads();
@@ -151,7 +152,7 @@ __global__ __launch_bounds__(kSmpFinalWaves * 64) void k_sample_final(
   }
   __syncthreads();
   if (wave < 4) {
-    wtop[wave * 64 + lane] = 0ull;
+    wtop[wave * 64 + lane] = smp_pad(kPadFinal + 16384u + 1024u + wave * 64 + lane);
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     wave_topk_keys<4>(k2, K, xch[wave], wtop + wave * 64, lane);
   }
