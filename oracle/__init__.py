@@ -6,7 +6,9 @@ baseline leg of the benchmark may import this package; the product path
 ``oracle.c`` (plain C, fp64, no shared code with the HIP library); this file
 only marshals numpy arrays into it.
 
-Every oracle function has a pin in ``tests/test_oracle_pins.py``.  Parity is
+Every oracle function has a pin in ``tests/test_oracle_pins.py``,
+``tests/test_sample_pins.py`` (sampling) or ``tests/test_attn_pins.py``
+(decode attention, RoPE, the fp16 encoder).  Parity is
 unpinned for: the bit order of MLX codes inside a word (no trained MLX weights
 are loaded; both sides read the same generator output) and the Zipf prior's
 scale (a workload choice).
@@ -83,6 +85,12 @@ def lib():
             L.orc_sample.restype = C.c_int32
             L.orc_sample.argtypes = [C.c_void_p, C.c_int32, C.c_double, C.c_int32, C.c_double,
                                      C.c_double, C.c_void_p, C.c_void_p, C.c_void_p]
+            L.orc_double_to_half.restype = C.c_uint16
+            L.orc_double_to_half.argtypes = [C.c_double]
+            L.orc_rope.argtypes = [C.c_void_p, C.c_int32, C.c_int64, C.c_double, C.c_void_p]
+            L.orc_attn_step.restype = C.c_int
+            L.orc_attn_step.argtypes = [C.c_int32, C.c_int32, C.c_int32, C.c_int64, C.c_double,
+                                        C.c_double, C.c_int64] + [C.c_void_p] * 6
             _lib = L
     return _lib
 
@@ -271,3 +279,35 @@ def sample(logits: np.ndarray, temperature: float, top_k: int, top_p: float, u: 
     tok = lib().orc_sample(_p(logits), logits.size, float(temperature), int(top_k),
                            float(top_p), float(u), _p(ranked), _p(cum), _p(kept))
     return {"token": int(tok), "ranked": ranked, "cum": cum, "kept": int(kept[0])}
+
+
+def double_to_half(v: float) -> int:
+    return int(lib().orc_double_to_half(float(v)))
+
+
+def rope(x: np.ndarray, pos: int, base: float) -> np.ndarray:
+    """RoPE of one head vector (fp64), pairs (i, i + D/2)."""
+    x = _c(x, np.float64)
+    out = np.zeros_like(x)
+    lib().orc_rope(_p(x), x.size, int(pos), float(base), _p(out))
+    return out
+
+
+def attn_step(q: np.ndarray, k: np.ndarray, v: np.ndarray, khist: np.ndarray,
+              vhist: np.ndarray, pos: int, window: int, scale: float, base: float) -> np.ndarray:
+    """O11: one decode attention step of the token at time ``pos``.
+
+    q [Hq][D], k and v [Hkv][D] (fp32); khist and vhist [times][Hkv][D] fp16
+    bits in time order, modified in place (time ``pos`` is written).  Returns
+    the output [Hq][D] in fp64."""
+    q, k, v = _c(q, np.float32), _c(k, np.float32), _c(v, np.float32)
+    Hq, D = q.shape
+    Hkv = k.shape[0]
+    assert khist.dtype == np.uint16 and khist.flags.c_contiguous and khist.shape[0] > pos
+    assert vhist.dtype == np.uint16 and vhist.flags.c_contiguous and vhist.shape == khist.shape
+    out = np.zeros((Hq, D), dtype=np.float64)
+    rc = lib().orc_attn_step(Hq, Hkv, D, int(window), float(scale), float(base), int(pos),
+                             _p(q), _p(k), _p(v), _p(khist), _p(vhist), _p(out))
+    if rc:
+        raise ValueError("orc_attn_step: bad shape")
+    return out

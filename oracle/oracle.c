@@ -479,3 +479,112 @@ int32_t orc_sample(const float* logits, int32_t V, double temperature, int32_t t
   free(id);
   return token;
 }
+
+/* ------------------------------------------- decode attention, FP16 KV */
+/* double -> IEEE binary16, round to nearest, ties to even, in one step.  The
+ * fp16 quantum for |v| in [2^E, 2^(E+1)) is 2^(E-10); below 2^-14 it is the
+ * subnormal quantum 2^-24.  Results of 2^16 or more are infinite. */
+uint16_t orc_double_to_half(double v) {
+  if (isnan(v)) return 0x7e00;
+  uint16_t sign = signbit(v) ? 0x8000 : 0;
+  double a = fabs(v);
+  if (a == 0.0) return sign;
+  if (isinf(a)) return sign | 0x7c00;
+  int e2;
+  frexp(a, &e2);
+  int E = e2 - 1;
+  if (E < -14) E = -14;
+  double quantum = ldexp(1.0, E - 10);
+  double r = nearbyint(a / quantum) * quantum;
+  if (r >= 65536.0) return sign | 0x7c00;
+  if (r < ldexp(1.0, -14)) return sign | (uint16_t)(r / ldexp(1.0, -24));
+  int re2;
+  double m = frexp(r, &re2);
+  int be = re2 - 1 + 15;
+  int frac = (int)(m * 2048.0) - 1024; /* 11 significant bits -> 10 fraction */
+  return sign | (uint16_t)(be << 10) | (uint16_t)frac;
+}
+
+/* Rotary position embedding of one head vector x[D] for the token at time
+ * pos ([iitog] technical paragraph and [devtrends] section "Senza
+ * dipendenze da llama.cpp e MLX": RoPE is one of the engine's kernels).
+ * Reading (the pages name the operation only): element i and element
+ * i + D/2 form a plane, i < D/2, rotated by the angle pos * base^(-2i/D)
+ * in the positive sense:
+ *   out[i]       = x[i] cos(a) - x[i + D/2] sin(a)
+ *   out[i + D/2] = x[i + D/2] cos(a) + x[i] sin(a). */
+void orc_rope(const double* x, int32_t D, int64_t pos, double base, double* out) {
+  const int32_t h = D / 2;
+  for (int32_t i = 0; i < h; ++i) {
+    const double a = (double)pos * pow(base, -2.0 * (double)i / (double)D);
+    const double c = cos(a), s = sin(a);
+    const double x0 = x[i], x1 = x[i + h];
+    out[i] = x0 * c - x1 * s;
+    out[i + h] = x1 * c + x0 * s;
+  }
+}
+
+/* One decode step of attention for the token at time pos over an FP16 key
+ * and value history ([iitog] technical paragraph: the KV cache is FP16, 25
+ * layers attend over a sliding window kept in a bounded circular store and
+ * 5 layers over the whole context kept in a linear one; [remio] section
+ * "Mac Gemma 4 26B entra nello spazio disponibile…" and [pikobit]: a
+ * 4,096-token cache).
+ *   q [Hq][D], k, v [Hkv][D]: this token's projections (fp32);
+ *   khist, vhist [time][Hkv][D] fp16 bits: entries of times before pos are
+ *     read; this step writes time pos: fp16 of RoPE(k) and fp16 of v;
+ *   out [Hq][D]: the attention output.
+ * Readings: head h attends with key/value head h / (Hq / Hkv); the times
+ * attended are max(0, pos - window + 1) .. pos, or 0 .. pos with window 0;
+ * the query is RoPE(q) unrounded; score(t) = scale * <RoPE(q_h), K[t]>;
+ * out_h = sum_t softmax(score)_t V[t].  Returns 0, or -1 on bad shapes. */
+int orc_attn_step(int32_t Hq, int32_t Hkv, int32_t D, int64_t window, double scale,
+                  double base, int64_t pos, const float* q, const float* k, const float* v,
+                  uint16_t* khist, uint16_t* vhist, double* out) {
+  if (Hq < 1 || Hkv < 1 || Hq % Hkv || D < 2 || D % 2 || pos < 0 || window < 0) return -1;
+  const int32_t G = Hq / Hkv;
+  double* x = (double*)malloc(sizeof(double) * (size_t)D);
+  double* r = (double*)malloc(sizeof(double) * (size_t)D);
+  /* this token's key and value into the history */
+  for (int32_t g = 0; g < Hkv; ++g) {
+    for (int32_t d = 0; d < D; ++d) x[d] = (double)k[(int64_t)g * D + d];
+    orc_rope(x, D, pos, base, r);
+    uint16_t* kd = khist + (pos * Hkv + g) * (int64_t)D;
+    uint16_t* vd = vhist + (pos * Hkv + g) * (int64_t)D;
+    for (int32_t d = 0; d < D; ++d) {
+      kd[d] = orc_double_to_half(r[d]);
+      vd[d] = orc_double_to_half((double)v[(int64_t)g * D + d]);
+    }
+  }
+  const int64_t t0 = (window > 0 && pos - window + 1 > 0) ? pos - window + 1 : 0;
+  const int64_t n = pos - t0 + 1;
+  double* sc = (double*)malloc(sizeof(double) * (size_t)n);
+  for (int32_t hq = 0; hq < Hq; ++hq) {
+    const int32_t g = hq / G;
+    for (int32_t d = 0; d < D; ++d) x[d] = (double)q[(int64_t)hq * D + d];
+    orc_rope(x, D, pos, base, r);
+    double m = -INFINITY;
+    for (int64_t j = 0; j < n; ++j) {
+      const uint16_t* kt = khist + ((t0 + j) * Hkv + g) * (int64_t)D;
+      double s = 0.0;
+      for (int32_t d = 0; d < D; ++d) s += r[d] * orc_half_to_double(kt[d]);
+      sc[j] = scale * s;
+      if (sc[j] > m) m = sc[j];
+    }
+    double z = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+      sc[j] = exp(sc[j] - m);
+      z += sc[j];
+    }
+    double* o = out + (int64_t)hq * D;
+    for (int32_t d = 0; d < D; ++d) o[d] = 0.0;
+    for (int64_t j = 0; j < n; ++j) {
+      const uint16_t* vt = vhist + ((t0 + j) * Hkv + g) * (int64_t)D;
+      for (int32_t d = 0; d < D; ++d) o[d] += sc[j] / z * orc_half_to_double(vt[d]);
+    }
+  }
+  free(sc);
+  free(x);
+  free(r);
+  return 0;
+}

@@ -201,3 +201,78 @@ def test_stack_residual_stream_grows_and_stays_finite(stack):
         a, b = bf16_to_f64(xs[l]), bf16_to_f64(xs[l + 1])
         assert np.all(np.isfinite(b))
         assert not np.array_equal(a, b)
+
+
+FULL_SAMPLE = 64
+
+
+def test_stack_full_length(stack, stack_kernel):
+    """The stack workload at its stated length, 256 tokens (the token vectors
+    the stack benchmark times).  Every token goes through the one-launch
+    stack decode and through 30 one-layer launches, which must agree bit for
+    bit in every layer output, routing and combine weight.  All 7,680
+    routings are checked against the fp64 router on the device's layer
+    input (same top-8 with weights within 1e-5, or a certified near-tie with
+    weights within their bound), and a seeded sample of 64 (token, layer)
+    pairs runs the oracle's whole layer on the device's layer input."""
+    import torch
+
+    import bit_quantized_gemv_amd as q
+
+    n, K = STACK.layers, STACK.top_k
+    X = synth.make_tokens(STACK, STACK.tokens, stream=3)
+    ws = stack[0][2].layer.new_workspace(1)
+    xin = np.empty((STACK.tokens, n + 1, STACK.hidden), dtype=np.uint16)
+    gidx = np.empty((STACK.tokens, n, K), dtype=np.int32)
+    gw = np.empty((STACK.tokens, n, K), dtype=np.float32)
+    for t in range(STACK.tokens):
+        lo, idx, w, out = _run_stack_kernel(torch, stack_kernel, X[t])
+        xs, routing = _run_gpu(torch, q, stack, X[t], ws)
+        for l in range(n):
+            assert np.array_equal(lo[l], xs[l + 1]), (t, l, "layer output differs")
+            assert np.array_equal(idx[l], routing[l][0]), (t, l)
+            assert np.array_equal(w[l].view(np.uint32), routing[l][1].view(np.uint32)), (t, l)
+        assert np.array_equal(out, xs[-1])
+        xin[t] = np.stack(xs)
+        gidx[t], gw[t] = idx, w
+    assert q.qmoe_workspace_status(ws) == 0
+    assert q.qmoe_workspace_status(stack_kernel.ws) == 0
+    log(f"{STACK.tokens} tokens x {n} layers: one-launch stack == one-layer launches")
+
+    def route(job):
+        t, l = job
+        lw, ol, _ = stack[l]
+        x = xin[t, l]
+        lg = ol.router_logits(oracle.rmsnorm(x, lw.gamma))
+        oidx, ow = oracle.topk_softmax(lg, K)
+        if list(oidx) == list(gidx[t, l]) and np.all(np.abs(gw[t, l] - ow) <= 1e-5 * ow):
+            return 0
+        B = routing_bound(lw.router, x, lg, gamma=lw.gamma)
+        assert weights_consistent(B, lg, gidx[t, l], gw[t, l]), (t, l, "combine weights")
+        if list(oidx) != list(gidx[t, l]):
+            assert routing_certified(B, lg, gidx[t, l]), (t, l, "routing flip not certified")
+            return 1
+        return 0
+
+    jobs = [(t, l) for t in range(STACK.tokens) for l in range(n)]
+    with ThreadPoolExecutor(max_workers=THREADS) as ex:
+        flips = sum(ex.map(route, jobs))
+    log(f"  {len(jobs)} routings against the fp64 router: certified near-tie flips {flips}")
+
+    rng = np.random.default_rng(2560)
+    pick = rng.choice(len(jobs), size=FULL_SAMPLE, replace=False)
+    sample = [jobs[i] for i in pick] + [(0, 0), (STACK.tokens - 1, n - 1)]
+
+    def layer(job):
+        t, l = job
+        lw, ol, _ = stack[l]
+        r = ol.forward(xin[t, l], residual=True)
+        if list(r["idx"]) != list(gidx[t, l]):  # a flip certified above
+            r = ol.forward(xin[t, l], residual=True, force_idx=gidx[t, l],
+                           force_w=gw[t, l].astype(np.float64))
+        return rel_l2(bf16_to_f64(xin[t, l + 1]), bf16_to_f64(r["out"]))
+
+    with ThreadPoolExecutor(max_workers=THREADS) as ex:
+        errs = list(ex.map(layer, sample))
+    log(f"  {len(sample)} sampled (token, layer) pairs: worst layer relL2 {max(errs):.2e}")
+    assert max(errs) <= 2e-3
