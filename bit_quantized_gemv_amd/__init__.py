@@ -72,6 +72,12 @@ _lib.qmoe_sample_workspace_bytes.restype = C.c_size_t
 _lib.qmoe_sample_workspace_bytes.argtypes = [C.c_int32, C.c_int32]
 _lib.qmoe_sample.argtypes = [_vp, C.c_int32, C.c_float, C.c_int32, C.c_float, C.c_float, _vp, _vp,
                              _vp, C.c_size_t, _vp]
+_lib.qmoe_attn_workspace_bytes.restype = C.c_size_t
+_lib.qmoe_attn_workspace_bytes.argtypes = [C.c_void_p]
+_lib.qmoe_attn_decode.argtypes = [C.c_void_p, _vp, _vp, _vp, C.c_int32, _vp, _vp, _vp, _vp,
+                                  C.c_size_t, _vp]
+_lib.qmoe_attn_workspace_status.argtypes = [_vp, C.c_size_t, C.c_int32, C.POINTER(C.c_int32),
+                                            _vp]
 _lib.qmoe_tiled4_bytes.restype = C.c_size_t
 _lib.qmoe_tiled4_bytes.argtypes = [C.c_int32, C.c_int32]
 _lib.qmoe_repack_tiled4.argtypes = [_vp, _vp, _vp, C.c_int32, C.c_int32, _vp, C.c_size_t]
@@ -267,6 +273,36 @@ def qmoe_sample(logits, V: int, temperature: float, top_k: int, top_p: float, u:
                                             float(top_p), float(u), _ptr(token), _ptr(ranked),
                                             _ptr(ws), ws.numel() * ws.element_size(),
                                             _stream(stream)))
+
+
+class AttnShape(C.Structure):
+    """qmoe_attn_shape: head counts, head width, cache slots, circular or
+    linear store, RoPE base and score scale."""
+    _fields_ = [("n_heads", C.c_int32), ("n_kv_heads", C.c_int32), ("head_dim", C.c_int32),
+                ("slots", C.c_int32), ("circular", C.c_int32), ("rope_base", C.c_float),
+                ("scale", C.c_float)]
+
+
+def qmoe_attn_workspace_bytes(shape: AttnShape) -> int:
+    return int(_lib.qmoe_attn_workspace_bytes(C.byref(shape)))
+
+
+def qmoe_attn_decode(shape: AttnShape, q, k, v, pos: int, k_cache, v_cache, out, ws,
+                     stream=None) -> None:
+    _check("qmoe_attn_decode", _lib.qmoe_attn_decode(
+        C.byref(shape), _ptr(q), _ptr(k), _ptr(v), int(pos), _ptr(k_cache), _ptr(v_cache),
+        _ptr(out), _ptr(ws), 0 if ws is None else ws.numel() * ws.element_size(),
+        _stream(stream)))
+
+
+def qmoe_attn_workspace_status(ws, n_kv_heads: int, stream=None) -> int:
+    """The attention workspace's error word (0: every merge completed).  A
+    nonzero word raises QmoeError after the workspace has been zeroed."""
+    code = C.c_int32(0)
+    _check("qmoe_attn_workspace_status", _lib.qmoe_attn_workspace_status(
+        _ptr(ws), ws.numel() * ws.element_size(), int(n_kv_heads), C.byref(code),
+        _stream(stream)))
+    return int(code.value)
 
 
 def qmoe_tiled4_bytes(rows: int, cols: int) -> int:

@@ -18,7 +18,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqmoe.so")
 TRACE_LIB = os.path.join(PKG, "libqmoe_trace.so")
 SOURCES = ["qmoe_api.hip", "qmoe_decode.hip", "qmoe_router.hip", "qmoe_prefill.hip", "qmoe_pool.hip",
-           "qmoe_sample.hip"]
+           "qmoe_sample.hip", "qmoe_attn.hip"]
 ARCH = "gfx950"
 
 

@@ -2,6 +2,7 @@
 // argument validation, workspace sizing, and dispatch to the launchers.
 // Nothing here allocates, frees or synchronises (qmoe_workspace_status
 // excepted, which reads one word back).
+#include <cmath>
 #include <cstring>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -26,6 +27,12 @@ size_t sample_ws_bytes(int V, int K);
 bool sample_supported(int V, int K);
 qmoe_status launch_sample(const float* logits, int V, float temperature, int K, float top_p,
                           float u, int32_t* token, int32_t* ranked, uint8_t* ws, void* stream);
+bool attn_supported(int D, int G);
+size_t attn_ws_bytes(int Hq, int Hkv, int D, int S);
+size_t attn_ctl_bytes(int Hkv);
+qmoe_status launch_attn(const float* q, const float* k, const float* v, int Hq, int Hkv, int D,
+                        int S, bool circular, int pos, float rope_base, float scale, uint16_t* kc,
+                        uint16_t* vc, uint16_t* out, void* ws, void* stream);
 bool gemv_tiled4_supported(int cols);
 qmoe_status launch_gemv_tiled4(const uint8_t* T, int rows, int cols, const uint16_t* x, float* y,
                                int rbw, void* stream);
@@ -194,6 +201,56 @@ qmoe_status qmoe_sample(const float* logits, int32_t V, float temperature, int32
     return QMOE_ERR_ALIGN;
   return launch_sample(logits, V, temperature, top_k, top_p, u, token, ranked,
                        static_cast<uint8_t*>(ws), stream);
+}
+
+static bool attn_shape_ok(const qmoe_attn_shape* s) {
+  return s->n_heads >= 1 && s->n_kv_heads >= 1 && s->n_heads % s->n_kv_heads == 0 &&
+         s->head_dim >= 2 && s->slots >= 1 && (s->circular == 0 || s->circular == 1) &&
+         s->rope_base > 1.f && std::isfinite(s->rope_base) && std::isfinite(s->scale);
+}
+
+size_t qmoe_attn_workspace_bytes(const qmoe_attn_shape* s) {
+  if (!s || !attn_shape_ok(s)) return 0;
+  return attn_ws_bytes(s->n_heads, s->n_kv_heads, s->head_dim, s->slots);
+}
+
+qmoe_status qmoe_attn_decode(const qmoe_attn_shape* s, const float* q, const float* k,
+                             const float* v, int32_t pos, uint16_t* k_cache, uint16_t* v_cache,
+                             uint16_t* out, void* ws, size_t ws_bytes, void* stream) {
+  if (!s || !q || !k || !v || !k_cache || !v_cache || !out || !ws) return QMOE_ERR_NULL_ARG;
+  if (!attn_shape_ok(s) || pos < 0 || (!s->circular && pos >= s->slots))
+    return QMOE_ERR_BAD_SHAPE;
+  if (!attn_supported(s->head_dim, s->n_heads / s->n_kv_heads)) return QMOE_ERR_UNSUPPORTED;
+  if ((int64_t)s->n_kv_heads * s->slots * s->head_dim > ((int64_t)1 << 40)) return QMOE_ERR_UNSUPPORTED;
+  if (ws_bytes < attn_ws_bytes(s->n_heads, s->n_kv_heads, s->head_dim, s->slots))
+    return QMOE_ERR_WORKSPACE;
+  const uintptr_t al = reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache) |
+                       reinterpret_cast<uintptr_t>(ws);
+  if (al % 16 || reinterpret_cast<uintptr_t>(q) % 4 || reinterpret_cast<uintptr_t>(k) % 4 ||
+      reinterpret_cast<uintptr_t>(v) % 4 || reinterpret_cast<uintptr_t>(out) % 2)
+    return QMOE_ERR_ALIGN;
+  return launch_attn(q, k, v, s->n_heads, s->n_kv_heads, s->head_dim, s->slots, s->circular != 0,
+                     pos, s->rope_base, s->scale, k_cache, v_cache, out, ws, stream);
+}
+
+qmoe_status qmoe_attn_workspace_status(void* ws, size_t ws_bytes, int32_t n_kv_heads,
+                                       int32_t* device_code, void* stream) {
+  if (!ws || !device_code) return QMOE_ERR_NULL_ARG;
+  if (n_kv_heads < 1) return QMOE_ERR_BAD_SHAPE;
+  if (ws_bytes < attn_ctl_bytes(n_kv_heads)) return QMOE_ERR_WORKSPACE;
+  uint32_t v = 0;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (hipMemcpyAsync(&v, ws, 4, hipMemcpyDeviceToHost, st) != hipSuccess) return QMOE_ERR_HIP;
+  if (hipStreamSynchronize(st) != hipSuccess) return QMOE_ERR_HIP;
+  *device_code = (int32_t)v;
+  if (v != 0) {
+    // a merge gave up: partial words of the unfinished call may remain;
+    // the whole workspace starts afresh
+    if (hipMemsetAsync(ws, 0, ws_bytes, st) != hipSuccess) return QMOE_ERR_HIP;
+    if (hipStreamSynchronize(st) != hipSuccess) return QMOE_ERR_HIP;
+    return QMOE_ERR_DEVICE;
+  }
+  return QMOE_OK;
 }
 
 size_t qmoe_tiled4_bytes(int32_t rows, int32_t cols) {

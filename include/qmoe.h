@@ -476,6 +476,57 @@ qmoe_status qmoe_pool_acquire_file(qmoe_pool* pool, qmoe_file_tier* tier, int32_
 qmoe_status qmoe_file_tier_stats_get(const qmoe_file_tier* tier, qmoe_file_tier_stats* st);
 void qmoe_file_tier_close(qmoe_file_tier* tier);
 
+/* Decode attention over an FP16 key/value cache, with RoPE (iitog.ru
+ * "TurboFieldfare: движок с открытым кодом…", technical paragraph: attention
+ * and RoPE kernels, an FP16 KV cache, 25 sliding-window layers in a bounded
+ * circular store and 5 full-attention layers in a linear one; remio.ai
+ * "TurboFieldfare esegue Mac Gemma 4 26B in 2 GB…", section "Mac Gemma 4 26B
+ * entra nello spazio disponibile…": a 4,096-token cache).  Head shapes are
+ * not on the pages: they are arguments.
+ *
+ * One call is the token at time pos (0-based):
+ *   q' = RoPE(q), k' = RoPE(k): element i and element i + D/2 (i < D/2)
+ *     rotated by the angle pos * rope_base^(-2i/D) in the positive sense
+ *     (x_i cos - x_{i+D/2} sin, x_{i+D/2} cos + x_i sin), computed in fp64;
+ *   slot = pos mod S (circular) or pos (linear) receives fp16(k') in
+ *     k_cache and fp16(v) in v_cache (round to nearest even);
+ *   query head h attends with key/value head h / (Hq / Hkv) over the tokens
+ *     in the cache: times pos - S + 1 .. pos (circular; 0 .. pos while pos
+ *     < S) or 0 .. pos (linear): score_t = scale * <q'_h, K_t> (fp32),
+ *     out_h = sum_t softmax(score)_t V_t, written as bf16.
+ * q: fp32 [Hq][D]; k, v: fp32 [Hkv][D] (the projections of this token);
+ * k_cache, v_cache: fp16 [Hkv][S][D], owned by the caller, 16-byte aligned;
+ *   slots that hold no token of the window are neither read nor written;
+ * out: bf16 [Hq][D].  All on the device.
+ * Supported: head_dim 128 with Hq / Hkv in {1, 2, 4}, head_dim 256 with
+ * Hq / Hkv in {1, 2} (else QMOE_ERR_UNSUPPORTED); Hkv divides Hq; S >= 1;
+ * pos >= 0, and pos < S for a linear cache (else QMOE_ERR_BAD_SHAPE);
+ * rope_base > 1.  ws: at least qmoe_attn_workspace_bytes(shape) bytes, 16-
+ * byte aligned: control words (an error word, one epoch per key/value head)
+ * and the partial results of the splits of the cache, tagged with the
+ * epoch.  The workspace must be zero-filled before its first call; one fill
+ * serves every later call, of any shape.  Calls that share a cache or a
+ * workspace run in stream order.
+ * qmoe_attn_workspace_status: reads the error word (in *device_code),
+ * nonzero when an in-kernel wait for another block's partial gave up (the
+ * output of that call is not valid); then the whole workspace is zeroed
+ * and QMOE_ERR_DEVICE returned.  Synchronises the stream. */
+typedef struct {
+  int32_t n_heads;     /* Hq: query heads */
+  int32_t n_kv_heads;  /* Hkv: key/value heads, divides Hq */
+  int32_t head_dim;    /* D */
+  int32_t slots;       /* S: cache capacity in tokens */
+  int32_t circular;    /* 1: sliding window of S tokens; 0: linear, pos < S */
+  float rope_base;     /* RoPE frequency base */
+  float scale;         /* score scale (e.g. 1 / sqrt(D)) */
+} qmoe_attn_shape;
+size_t qmoe_attn_workspace_bytes(const qmoe_attn_shape* shape);
+qmoe_status qmoe_attn_decode(const qmoe_attn_shape* shape, const float* q, const float* k,
+                             const float* v, int32_t pos, uint16_t* k_cache, uint16_t* v_cache,
+                             uint16_t* out, void* ws, size_t ws_bytes, void* stream);
+qmoe_status qmoe_attn_workspace_status(void* ws, size_t ws_bytes, int32_t n_kv_heads,
+                                       int32_t* device_code, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -329,6 +329,47 @@ def dirichlet_routing(wl: Workload, n: int, stream: int = 0) -> Tuple[np.ndarray
     return idx, w
 
 
+# ------------------------------------------------------ decode attention
+@dataclasses.dataclass(frozen=True)
+class AttnWorkload:
+    """Shapes of a decode-attention workload.  The pages give the layer
+    split (25 sliding-window layers, 5 full-attention layers), an FP16
+    cache and a 4,096-token context; head counts, head width, window length
+    and RoPE base are not on them and are stated choices."""
+
+    wid: int
+    name: str
+    n_heads: int         # Hq
+    n_kv_heads: int      # Hkv
+    head_dim: int        # D
+    window: int          # slots of a sliding-window layer's circular store
+    context: int         # slots of a full layer's linear store
+    sliding_layers: int
+    full_layers: int
+    rope_base: float = 10000.0
+
+
+ATTN_WORKLOADS: Dict[str, AttnWorkload] = {
+    "attn30_decode": AttnWorkload(20, "attn30_decode", 16, 8, 256, 1024, 4096, 25, 5),
+    "tiny_attn": AttnWorkload(21, "tiny_attn", 4, 2, 128, 48, 160, 2, 1),
+}
+
+
+def attn_inputs(aw: AttnWorkload, slots: int, layer: int = 0, stream: int = 0):
+    """One token's projections and a filled cache: q fp32 [Hq][D], k and v
+    fp32 [Hkv][D], all N(0,1); key and value caches fp16 bits [Hkv][slots][D],
+    N(0,1) in every slot (a rotated Gaussian key is again Gaussian, so the
+    stored keys need no rotation of their own)."""
+    rng = np.random.Generator(np.random.PCG64(seed(aw.wid, layer, 8) + 100000 * stream))
+    Hq, Hkv, D = aw.n_heads, aw.n_kv_heads, aw.head_dim
+    q = rng.normal(size=(Hq, D)).astype(np.float32)
+    k = rng.normal(size=(Hkv, D)).astype(np.float32)
+    v = rng.normal(size=(Hkv, D)).astype(np.float32)
+    kc = to_fp16_bits(rng.normal(size=(Hkv, slots, D)))
+    vc = to_fp16_bits(rng.normal(size=(Hkv, slots, D)))
+    return q, k, v, kc, vc
+
+
 def random_qmat(rows: int, cols: int, bits: int, seed_: int) -> QMat:
     return draw_qmat(np.random.Generator(np.random.PCG64(seed_)), rows, cols, bits)
 
@@ -343,4 +384,5 @@ __all__ = [
     "seed", "draw_qmat", "blob_layout", "pack_blob", "blob_views", "make_layer",
     "make_tokens", "zipf_prior", "router_logit_spread", "dirichlet_routing",
     "to_fp16_bits", "to_bf16_bits", "bf16_bits_to_f32", "random_qmat", "random_bf16",
+    "AttnWorkload", "ATTN_WORKLOADS", "attn_inputs",
 ]

@@ -199,3 +199,40 @@ def test_file_tier_validation_before_any_gpu_call(tmp_path):
                                    C.byref(h)) == 2  # max_misses > 8
     assert lib.qmoe_file_tier_open(str(short).encode(), 2, 4, 9000, 8192, 2, 8, 0,
                                    C.byref(h)) == 2  # stride < blob
+
+
+def test_attn_validation_before_launch():
+    """qmoe_attn_decode rejects bad shapes, positions and buffers on the host
+    (the pointers below are never read)."""
+    import bit_quantized_gemv_amd as q
+
+    lib = q.lib()
+
+    def shape(Hq=16, Hkv=8, D=256, S=4096, circ=0, base=10000.0, scale=0.0625):
+        return q.AttnShape(Hq, Hkv, D, S, circ, base, scale)
+
+    ws = 1 << 24
+    P = (0x1000, 0x2000, 0x3000)
+
+    def call(s, pos=5, wsb=ws, kc=0x10000, out=0x30000, qp=P[0]):
+        return lib.qmoe_attn_decode(C.byref(s), qp, P[1], P[2], pos, kc, 0x20000, out, 0x40000,
+                                    wsb, None)
+
+    assert call(shape(), qp=None) == 1                  # QMOE_ERR_NULL_ARG
+    assert call(shape(Hq=12)) == 2                      # Hkv does not divide Hq
+    assert call(shape(), pos=-1) == 2                   # negative position
+    assert call(shape(S=16), pos=16) == 2               # a linear cache is full
+    assert call(shape(base=1.0)) == 2                   # RoPE base
+    assert call(shape(D=64)) == 3                       # QMOE_ERR_UNSUPPORTED: head width
+    assert call(shape(Hq=32, Hkv=8)) == 3               # four query heads per group at D = 256
+    assert call(shape(), wsb=100) == 4                  # QMOE_ERR_WORKSPACE
+    assert call(shape(), kc=0x10008) == 5               # QMOE_ERR_ALIGN
+    # control words (64 bytes, then 8 epoch words per key/value head,
+    # rounded to 256) and the largest split count's partials: S / 32 splits
+    # of Hq (D + 2) tagged 8-byte words
+    assert q.qmoe_attn_workspace_bytes(shape()) == 512 + 128 * 16 * 258 * 8
+    code = C.c_int32(0)
+    assert lib.qmoe_attn_workspace_status(None, 1024, 8, C.byref(code), None) == 1
+    assert lib.qmoe_attn_workspace_status(0x1000, 1024, 0, C.byref(code), None) == 2
+    assert lib.qmoe_attn_workspace_status(0x1000, 256, 8, C.byref(code), None) == 4
+    assert q.qmoe_attn_workspace_bytes(shape(Hq=12)) == 0
