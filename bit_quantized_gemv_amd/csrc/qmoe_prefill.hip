@@ -256,12 +256,18 @@ constexpr int kPfWaves = kBlock / 64;
 
 // LDS of a block: the A rows of two K-steps (double buffer), the A row
 // offsets, and per wave and matrix the codes of one pair of K-steps (the
-// wave's 16 weight rows × 128 bytes, 16-byte slots swizzled per row).
-template <int NM>
+// wave's 16 weight rows × 128 bytes, 16-byte slots swizzled per row).  With
+// SB, per wave and matrix also the scales and biases of the wave's 16 rows
+// over all K/64 groups: [16][G] scales, then [16][G] biases, filled once per
+// pass (whole 64-lane writes of 16 bytes: 1536 halves for G <= 48).
+constexpr int kPfSbMaxG = 48;
+constexpr int kPfSbHalves = 1536;
+template <int NM, bool SB>
 struct PfShared {
   _Float16 a[2][kPfMaxM * kPfAStride];
   int32_t rows[kPfMaxM];  // element offset of each A row from the A base
   u4v_t w[kPfWaves][NM][16 * 8];
+  uint16_t sb[kPfWaves][NM][SB ? kPfSbHalves : 1];
 };
 
 // Slot of 16-byte chunk c of row r (r < 16) in a wave's code tile: rows are
@@ -352,8 +358,8 @@ struct PfA {
 };
 // Byte offsets (from the A base) of this thread's A rows, read from
 // sh.rows once per pass.
-template <int NMS, int NM>
-__device__ __forceinline__ void pf_rows(uint32_t (&roff)[NMS], const PfShared<NM>& sh, int Mc) {
+template <int NMS, int NM, bool SB>
+__device__ __forceinline__ void pf_rows(uint32_t (&roff)[NMS], const PfShared<NM, SB>& sh, int Mc) {
   const int r0 = threadIdx.x >> 4;
 #pragma unroll
   for (int i = 0; i < NMS; ++i) roff[i] = 2u * (uint32_t)sh.rows[min(r0 + 16 * i, Mc - 1)];
@@ -375,19 +381,23 @@ __device__ __forceinline__ void pf_store_a(const PfA<NMS>& A, _Float16* buf) {
   for (int i = 0; i < NMS; ++i) *reinterpret_cast<u4v_t*>(dst + 16 * i * kPfAStride) = A.v[i];
 }
 
-// MFMAs of one K-step: the lane's codes (16 bytes of row n = l%16 per
+// MFMAs of one K-step kb: the lane's codes (16 bytes of row n = l%16 per
 // matrix, half h of the pair in the wave's code tile), dequantized with
-// the group's scale and bias, against the staged A rows.
-template <int NM, int NMS>
+// the group's scale and bias (from the wave's LDS table with SB, else as
+// loaded into B), against the staged A rows.
+template <int NM, int NMS, bool SB>
 __device__ __forceinline__ void pf_mma(const u4v_t (*wl)[16 * 8], int h, const PfSB<NM>& B,
+                                       const uint16_t (*tb)[SB ? kPfSbHalves : 1], int kb, int K,
                                        const _Float16* buf, f4_t (&acc)[NMS][NM]) {
   const int lane = threadIdx.x & 63, m = lane & 15, j = lane >> 4;
+  const int G = K / 64, g = min(64 * kb + 16 * j, K / 2 - 16) >> 5;
   h8_t Bf[NM][4];
 #pragma unroll
   for (int k = 0; k < NM; ++k) {
     const u4v_t q = wl[k][pf_wslot(m, 4 * h + j)];
-    const _Float16 sv = __builtin_bit_cast(_Float16, (uint16_t)B.s[k]);
-    const _Float16 bv = __builtin_bit_cast(_Float16, (uint16_t)B.b[k]);
+    const _Float16 sv = __builtin_bit_cast(_Float16, SB ? tb[k][m * G + g] : (uint16_t)B.s[k]);
+    const _Float16 bv =
+        __builtin_bit_cast(_Float16, SB ? tb[k][16 * G + m * G + g] : (uint16_t)B.b[k]);
     const h2_t s2 = {sv, sv}, b2 = {bv, bv};
     Bf[k][0] = dequant_word(q.x, s2, b2);
     Bf[k][1] = dequant_word(q.y, s2, b2);
@@ -430,9 +440,9 @@ __device__ __forceinline__ void pf_mma(const u4v_t (*wl)[16 * 8], int h, const P
 // only.
 // rows(): writes sh.rows[0..Mc) and ends with a block barrier; it runs
 // after the first weight loads are issued, so its reads overlap them.
-template <int NM, int NMS, typename Rows>
+template <int NM, int NMS, bool SB, typename Rows>
 __device__ __forceinline__ void pf_pass(const DevQ (&W)[NM], int n_wave0, int K, int Mc,
-                                        const _Float16* abase, PfShared<NM>& sh,
+                                        const _Float16* abase, PfShared<NM, SB>& sh,
                                         f4_t (&acc)[NMS][NM], Rows rows) {
   constexpr int AD = NMS <= 2 ? 4 : 2;
 #pragma unroll
@@ -445,8 +455,26 @@ __device__ __forceinline__ void pf_pass(const DevQ (&W)[NM], int n_wave0, int K,
   const PfGOff go = pf_goff(n_wave0, K);
   const PfSOff so = pf_soff(n_wave0 + ((threadIdx.x & 63) & 15), K);
   PfWG<NM> G0, G1;
-  PfSB<NM> S0, S1, S2, S3;
+  PfSB<NM> S0, S1, S2, S3;  // without SB: scales and biases, four steps ahead
   PfA<NMS> R[AD];  // R[(s + 1) % AD] holds A(s + 1) when step s begins
+  if constexpr (SB) {
+    // the table: 16-byte units of the wave's rows' scales, then biases,
+    // straight into LDS (no registers); issued first, so the waits below
+    // for later loads cover them (loads complete in issue order)
+    const int lane = threadIdx.x & 63, G = K / 64, nu = 4 * G;
+#pragma unroll
+    for (int k = 0; k < NM; ++k)
+      for (int i = 0; i < cdiv(nu, 64); ++i) {
+        const int u = min(64 * i + lane, nu - 1);
+        const uint8_t* src =
+            u < 2 * G ? reinterpret_cast<const uint8_t*>(W[k].s) + (size_t)n_wave0 * G * 2 + 16 * u
+                      : reinterpret_cast<const uint8_t*>(W[k].b) + (size_t)n_wave0 * G * 2 +
+                            16 * (u - 2 * G);
+        __builtin_amdgcn_global_load_lds(
+            (const QMOE_GLOBAL void*)src,
+            (__attribute__((address_space(3))) void*)(&sh.sb[wave][k][512 * i]), 16, 0, 0);
+      }
+  }
   // prologue: the loads of a virtual iteration before the first, in the
   // loop's own order (G0; per step t the A set it refills, then S_t; G1
   // before step 2), so that at the loop head the waits counted along both
@@ -455,7 +483,7 @@ __device__ __forceinline__ void pf_pass(const DevQ (&W)[NM], int n_wave0, int K,
   pf_load_wg<NM>(G0, W, go, 0);
   rows();
   uint32_t roff[NMS];
-  pf_rows<NMS, NM>(roff, sh, Mc);
+  pf_rows<NMS, NM, SB>(roff, sh, Mc);
   PfA<NMS> A0;
   pf_load_a<NMS>(A0, abase, roff, 0);
   // step t of the virtual iteration loads A(t + 1 - (4 - AD)) when that is
@@ -463,7 +491,7 @@ __device__ __forceinline__ void pf_pass(const DevQ (&W)[NM], int n_wave0, int K,
   auto pro = [&](int t, PfSB<NM>& S) {
     const int ia = t + 1 - (4 - AD);
     if (ia >= 1) pf_load_a<NMS>(R[(t + 1) % AD], abase, roff, min(ia, nkb - 1));
-    pf_load_sb<NM>(S, W, so, t);
+    if constexpr (!SB) pf_load_sb<NM>(S, W, so, t);
   };
   pro(0, S0);
   pro(1, S1);
@@ -478,8 +506,9 @@ __device__ __forceinline__ void pf_pass(const DevQ (&W)[NM], int n_wave0, int K,
     PfA<NMS>& X = R[(t + 1) % AD];
     pf_store_a<NMS>(X, sh.a[(t + 1) & 1]);
     pf_load_a<NMS>(X, abase, roff, min(kb + t + 1 + AD, nkb - 1));
-    if (t == 0 || kb + t < nkb) pf_mma<NM, NMS>(wl, t & 1, S, sh.a[t & 1], acc);
-    pf_load_sb<NM>(S, W, so, kb + t + 4);
+    if (t == 0 || kb + t < nkb)
+      pf_mma<NM, NMS, SB>(wl, t & 1, S, sh.sb[wave], kb + t, K, sh.a[t & 1], acc);
+    if constexpr (!SB) pf_load_sb<NM>(S, W, so, kb + t + 4);
     __syncthreads();
   };
   for (int kb = 0; kb < nkb; kb += 4) {
@@ -566,8 +595,9 @@ __device__ __forceinline__ bool pf_unit(const int32_t* items, int T, int tsh, in
 // gate/up: one block per unit (1-D grid); a unit of the shared expert
 // covers token rows [row0, row0 + M) of X, one of expert e the sorted pair
 // rows [row0, row0 + M).
+template <bool SB>
 __global__ __launch_bounds__(kBlock, 2) void k_pf_gu(PfArgs a) {
-  __shared__ PfShared<2> sh;
+  __shared__ PfShared<2, SB> sh;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   PfUnit u;
   if (!pf_unit(a.items, a.T, a.Is / kPfRows, a.I / kPfRows, u)) return;
@@ -602,22 +632,23 @@ __global__ __launch_bounds__(kBlock, 2) void k_pf_gu(PfArgs a) {
   };
   if (Mc <= 16) {
     f4_t acc[1][2];
-    pf_pass<2, 1>(W, n - (lane & 15), a.H, Mc, a.xh, sh, acc, rows);
+    pf_pass<2, 1, SB>(W, n - (lane & 15), a.H, Mc, a.xh, sh, acc, rows);
     pf_gu_store<1>(acc, out, ld, u.row0, Mc, n);
   } else if (Mc <= 32) {
     f4_t acc[2][2];
-    pf_pass<2, 2>(W, n - (lane & 15), a.H, Mc, a.xh, sh, acc, rows);
+    pf_pass<2, 2, SB>(W, n - (lane & 15), a.H, Mc, a.xh, sh, acc, rows);
     pf_gu_store<2>(acc, out, ld, u.row0, Mc, n);
   } else {
     f4_t acc[4][2];
-    pf_pass<2, 4>(W, n - (lane & 15), a.H, Mc, a.xh, sh, acc, rows);
+    pf_pass<2, 4, SB>(W, n - (lane & 15), a.H, Mc, a.xh, sh, acc, rows);
     pf_gu_store<4>(acc, out, ld, u.row0, Mc, n);
   }
 }
 
 // down: one block per unit (1-D grid), H / 64 tiles per item.
+template <bool SB>
 __global__ __launch_bounds__(kBlock, 3) void k_pf_down(PfArgs a) {
-  __shared__ PfShared<1> sh;
+  __shared__ PfShared<1, SB> sh;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   PfUnit u;
   if (!pf_unit(a.items, a.T, a.H / kPfRows, a.H / kPfRows, u)) return;
@@ -640,15 +671,15 @@ __global__ __launch_bounds__(kBlock, 3) void k_pf_down(PfArgs a) {
   };
   if (Mc <= 16) {
     f4_t acc[1][1];
-    pf_pass<1, 1>(W, n - (lane & 15), Kd, Mc, src, sh, acc, rows);
+    pf_pass<1, 1, SB>(W, n - (lane & 15), Kd, Mc, src, sh, acc, rows);
     pf_down_store<1>(acc, out, a.H, u.row0, Mc, n);
   } else if (Mc <= 32) {
     f4_t acc[2][1];
-    pf_pass<1, 2>(W, n - (lane & 15), Kd, Mc, src, sh, acc, rows);
+    pf_pass<1, 2, SB>(W, n - (lane & 15), Kd, Mc, src, sh, acc, rows);
     pf_down_store<2>(acc, out, a.H, u.row0, Mc, n);
   } else {
     f4_t acc[4][1];
-    pf_pass<1, 4>(W, n - (lane & 15), Kd, Mc, src, sh, acc, rows);
+    pf_pass<1, 4, SB>(W, n - (lane & 15), Kd, Mc, src, sh, acc, rows);
     pf_down_store<4>(acc, out, a.H, u.row0, Mc, n);
   }
 }
@@ -728,8 +759,15 @@ qmoe_status launch_prefill(const qmoe_moe_layer& L, const uint16_t* X, int T, co
   const int nr = pf_max_items(E, K, T) - nsh;
   const int gu_blocks = nsh * (Is / kPfRows) + nr * (I / kPfRows);
   const int dn_blocks = (nsh + nr) * (H / kPfRows);
-  hipLaunchKernelGGL(k_pf_gu, dim3(gu_blocks), dim3(kBlock), 0, S(stream), a);
-  hipLaunchKernelGGL(k_pf_down, dim3(dn_blocks), dim3(kBlock), 0, S(stream), a);
+  // scales and biases from an LDS table where a row's groups fit it
+  if (H / 64 <= kPfSbMaxG)
+    hipLaunchKernelGGL(k_pf_gu<true>, dim3(gu_blocks), dim3(kBlock), 0, S(stream), a);
+  else
+    hipLaunchKernelGGL(k_pf_gu<false>, dim3(gu_blocks), dim3(kBlock), 0, S(stream), a);
+  if ((I > Is ? I : Is) / 64 <= kPfSbMaxG)
+    hipLaunchKernelGGL(k_pf_down<true>, dim3(dn_blocks), dim3(kBlock), 0, S(stream), a);
+  else
+    hipLaunchKernelGGL(k_pf_down<false>, dim3(dn_blocks), dim3(kBlock), 0, S(stream), a);
   hipLaunchKernelGGL(k_pf_combine, dim3((H / 8 + kBlock - 1) / kBlock, T), dim3(kBlock), 0,
                      S(stream), K, H, w, pos_of, a.y, a.y_sh, residual, out);
   return hipGetLastError() == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;

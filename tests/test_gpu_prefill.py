@@ -169,6 +169,21 @@ def test_prefill_odd_widths(torch_cuda, q, T):
     _check_rows(got, _oracle_rows_forced(ol, X, idx, w, residual=True))
 
 
+def test_prefill_wide_widths(torch_cuda, q):
+    """Hidden and shared widths of 3200 (50 scale groups per row, more than
+    the GEMMs' LDS scale tables hold): both GEMMs take their scales and
+    biases with per-step loads instead; forced routing, residual."""
+    torch = torch_cuda
+    wl = synth.WORKLOADS["wide_prefill"]
+    lw = synth.make_layer(wl, 0)
+    ol, dl = oracle.OracleLayer(lw), synth.device.DeviceLayer(lw)
+    log("prefill wide widths T=5")
+    X = synth.make_tokens(wl, wl.tokens, stream=75)
+    idx, w = synth.dirichlet_routing(wl, wl.tokens, stream=35)
+    got, _ = _prefill(torch, q, dl.layer, X, idx, w, residual=True)
+    _check_rows(got, _oracle_rows_forced(ol, X, idx, w, residual=True))
+
+
 def test_prefill_hot_and_repeated_experts(torch_cuda, q, tiny_layer):
     """Every token on the same 8 experts (128 rows each), then one expert
     repeated 8 times per token (1024 rows, more than one pass of 128)."""
