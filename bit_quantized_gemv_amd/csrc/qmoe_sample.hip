@@ -12,13 +12,13 @@
 // cumulative mass exceeds u times the kept mass.  Sums in rank order, fp32.
 //
 // Two launches:
-//   local  block b takes 4096 logits (1024 for V <= 16,384): each wave the
-//          top-K of its quarter, then wave 0 the top-K of the waves' 4K;
-//          the block's K keys go to the workspace
-//   final  one block of 16 waves: each wave the top-K of its share of the
-//          blocks' keys (4 per lane up to 16,384 logits, else 16), waves
-//          0..3 the top-K of four waves' each, wave 0 the top-K of theirs
-//          in rank order, then the softmax, the cut and the draw
+//   local  block b takes 1024 logits (4096 past 262,144 logits): each wave
+//          the top-K of its quarter, then wave 0 the top-K of the waves' 4K;
+//          the block's K keys go to the workspace in rank order
+//   final  one block of 16 waves: a bound at or below the K-th largest key
+//          from the blocks' leading keys, the keys at or above it (a few
+//          hundred for smooth logits) compacted into LDS, their top-K in
+//          rank order, then the softmax, the cut and the draw
 // A key is (order value of the logit) << 32 | ~id: one unsigned order for
 // "larger logit, then lower id", unique per token; missing entries get keys
 // of order 0 (below every real key), each a different one, so every key of
@@ -123,28 +123,25 @@ __global__ __launch_bounds__(kSmpBlock) void k_sample_local(const float* logits,
   }
 }
 
-template <int NV0>
-__global__ __launch_bounds__(kSmpFinalWaves * 64) void k_sample_final(
-    const uint64_t* cand, int n, int K, float temperature, float top_p, float u, int32_t* token,
-    int32_t* ranked) {
-  __shared__ uint64_t xch[kSmpFinalWaves][64];
-  __shared__ uint64_t wtop[kSmpFinalWaves * 64];
-  __shared__ uint64_t top[64];
+// The top-K of n keys read through load(i) (i < n <= 16 * 64 * NV0), in
+// rank order into top[0..K), by every thread of the 16-wave block: each
+// wave the top-K of its share, waves 0..3 the top-K of four waves' each,
+// wave 0 the top-K of theirs.  Missing entries get pad keys numbered from
+// pad0 (16384 + 2048 numbers).
+template <int NV0, typename Load>
+__device__ void block_topk(Load load, int n, int K, uint32_t pad0, uint64_t (*xch)[64],
+                           uint64_t* wtop, uint64_t* top) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  // padding numbers past the local blocks' (at most 256 * 256 of them)
-  constexpr uint32_t kPadFinal = kPadBase + 256u * 256u;
   uint64_t k[NV0];
 #pragma unroll
   for (int m = 0; m < NV0; ++m) {
     const int i = (wave * NV0 + m) * 64 + lane;
-    k[m] = i < n ? cand[i] : smp_pad(kPadFinal + (uint32_t)i);
+    k[m] = i < n ? load(i) : smp_pad(pad0 + (uint32_t)i);
   }
-  wtop[wave * 64 + lane] = smp_pad(kPadFinal + 16384u + wave * 64 + lane);
+  wtop[wave * 64 + lane] = smp_pad(pad0 + 16384u + wave * 64 + lane);
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
   wave_topk_keys<NV0>(k, K, xch[wave], wtop + wave * 64, lane);
   __syncthreads();
-  // a tree: waves 0..3 each take the top-K of four waves' K, then wave 0 of
-  // theirs (keys of 256 per wave at each level)
   uint64_t k2[4];
   if (wave < 4) {
 #pragma unroll
@@ -152,15 +149,112 @@ __global__ __launch_bounds__(kSmpFinalWaves * 64) void k_sample_final(
   }
   __syncthreads();
   if (wave < 4) {
-    wtop[wave * 64 + lane] = smp_pad(kPadFinal + 16384u + 1024u + wave * 64 + lane);
+    wtop[wave * 64 + lane] = smp_pad(pad0 + 16384u + 1024u + wave * 64 + lane);
     __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
     wave_topk_keys<4>(k2, K, xch[wave], wtop + wave * 64, lane);
   }
   __syncthreads();
-  if (wave != 0) return;
+  if (wave == 0) {
 #pragma unroll
-  for (int m = 0; m < 4; ++m) k2[m] = wtop[m * 64 + lane];
-  wave_topk_keys<4>(k2, K, xch[0], top, lane);
+    for (int m = 0; m < 4; ++m) k2[m] = wtop[m * 64 + lane];
+    wave_topk_keys<4>(k2, K, xch[0], top, lane);
+  }
+  __syncthreads();
+}
+
+// Final block (16 waves) over the nb blocks' K keys each (nb <= 256, each
+// block's keys in rank order):
+//   1. a bound M at or below the K-th largest key: with nb >= K, the K-th
+//      largest of the blocks' first keys (K blocks each hold a key >= it);
+//      else the smallest of the blocks' j-th keys, j = ceil(K / nb) (every
+//      block holds j keys >= it);
+//   2. the keys >= M (at least K of them) compacted into LDS;
+//   3. their top-K: one wave when they fit in 256, else the tree.  There
+//      are at most K * K = 4096: with nb >= K only the K blocks whose first
+//      key is >= M hold keys >= M; else there are nb * K < K * K keys;
+// then the softmax, the top-P cut and the draw on wave 0.
+constexpr int kSmpSurvCap = 4096;
+__global__ __launch_bounds__(kSmpFinalWaves * 64) void k_sample_final(
+    const uint64_t* cand, int nb, int K, float temperature, float top_p, float u, int32_t* token,
+    int32_t* ranked) {
+  __shared__ uint64_t xch[kSmpFinalWaves][64];
+  __shared__ uint64_t wtop[kSmpFinalWaves * 64];
+  __shared__ uint64_t top[64];
+  __shared__ uint64_t surv[kSmpSurvCap];
+  __shared__ uint64_t bound;
+  __shared__ uint32_t nsurv;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  // pad numbers past the local blocks' (at most 256 * 256 of them)
+  constexpr uint32_t kPadFinal = kPadBase + 256u * 256u;
+  const int n = nb * K;
+  if (threadIdx.x == 0) nsurv = 0;
+  // every key this thread filters in 2., loaded before the bound's search
+  constexpr int kPer = kSmpMaxBlocks * 64 / (kSmpFinalWaves * 64);  // nb * K <= 256 * 64
+  uint64_t x[kPer];
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int i = r * kSmpFinalWaves * 64 + (int)threadIdx.x;
+    x[r] = i < n ? cand[i] : 0ull;
+  }
+  // 1. the bound
+  if (nb >= K) {
+    if (wave == 0) {
+      uint64_t k[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int b = lane + 64 * m;
+        k[m] = b < nb ? cand[(int64_t)b * K] : smp_pad(kPadFinal + (uint32_t)b);
+      }
+      wave_topk_keys<4>(k, K, xch[0], top, lane);
+      if (lane == 0) bound = top[K - 1];
+    }
+  } else if (wave == 0) {
+    const int j = (K + nb - 1) / nb;
+    uint64_t mn = ~0ull;
+    for (int b = lane; b < nb; b += 64) {
+      const uint64_t x = cand[(int64_t)b * K + j - 1];
+      mn = x < mn ? x : mn;
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const uint64_t y = __shfl_xor(mn, o);
+      mn = y < mn ? y : mn;
+    }
+    if (lane == 0) bound = mn;
+  }
+  __syncthreads();
+  // 2. the keys >= bound, one LDS count per wave and pass
+  const uint64_t M = bound;
+#pragma unroll
+  for (int r = 0; r < kPer; ++r) {
+    const int i = r * kSmpFinalWaves * 64 + (int)threadIdx.x;
+    const bool keep = i < n && x[r] >= M;
+    const uint64_t bal = __ballot(keep);
+    if (bal == 0) continue;  // wave-uniform
+    uint32_t base = 0;
+    if (lane == 0) base = atomicAdd(&nsurv, (uint32_t)__popcll(bal));
+    base = __shfl(base, 0);
+    const uint32_t p = base + (uint32_t)__popcll(bal & ((1ull << lane) - 1ull));
+    if (keep) surv[p] = x[r];  // p < K * K <= kSmpSurvCap (see 3.)
+  }
+  __syncthreads();
+  // 3. their top-K
+  const int S = (int)nsurv;
+  if (S <= 256) {
+    if (wave == 0) {
+      uint64_t k[4];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const int i = lane + 64 * m;
+        k[m] = i < S ? surv[i] : smp_pad(kPadFinal + 20000u + (uint32_t)i);
+      }
+      wave_topk_keys<4>(k, K, xch[0], top, lane);
+    }
+    __syncthreads();
+  } else {
+    block_topk<4>([&](int i) { return surv[i]; }, S, K, kPadFinal + 20000u, xch, wtop, top);
+  }
+  if (wave != 0) return;
   // lane r holds rank r
   const uint64_t key = lane < K ? top[lane] : 0ull;
   const int32_t id = (int32_t)~(uint32_t)key;
@@ -188,9 +282,10 @@ __global__ __launch_bounds__(kSmpFinalWaves * 64) void k_sample_final(
   if (lane == 0) *token = tok;
 }
 
-// Logits per phase-one block: 4096 (16 per lane; the longest search runs
-// in parallel over the blocks), 1024 for small vocabularies.
-static int sample_per_block(int V) { return V <= 16 * 1024 ? 1024 : kSmpPerBlock; }
+// Logits per phase-one block: 1024 (4 per lane) up to 262,144 logits (256
+// blocks), 4096 (16 per lane) past that, so that at most 256 blocks feed
+// the final block.
+static int sample_per_block(int V) { return V <= 256 * 1024 ? 1024 : kSmpPerBlock; }
 
 size_t sample_ws_bytes(int V, int K) {
   return (size_t)cdiv(V, sample_per_block(V)) * (size_t)K * sizeof(uint64_t);
@@ -210,13 +305,8 @@ qmoe_status launch_sample(const float* logits, int V, float temperature, int K, 
     hipLaunchKernelGGL(k_sample_local<4>, dim3(nb), dim3(kSmpBlock), 0, st, logits, V, K, cand);
   else
     hipLaunchKernelGGL(k_sample_local<16>, dim3(nb), dim3(kSmpBlock), 0, st, logits, V, K, cand);
-  // the final block's first stage: 4 keys per lane while they fit
-  if (nb * K <= kSmpFinalWaves * 256)
-    hipLaunchKernelGGL(k_sample_final<4>, dim3(1), dim3(kSmpFinalWaves * 64), 0, st, cand,
-                       nb * K, K, temperature, top_p, u, token, ranked);
-  else
-    hipLaunchKernelGGL(k_sample_final<16>, dim3(1), dim3(kSmpFinalWaves * 64), 0, st, cand,
-                       nb * K, K, temperature, top_p, u, token, ranked);
+  hipLaunchKernelGGL(k_sample_final, dim3(1), dim3(kSmpFinalWaves * 64), 0, st, cand, nb, K,
+                     temperature, top_p, u, token, ranked);
   return hipGetLastError() == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
 }
 

@@ -173,7 +173,7 @@ def test_sample_validation_before_launch():
     assert call(1000, 0.2, 64, 1.5, 0.5) == 2       # top_p <= 1
     assert call(1000, 0.2, 64, 0.95, 1.0) == 2      # u < 1
     assert call(262144, 0.2, 64, 0.95, 0.5, 100) == 4  # QMOE_ERR_WORKSPACE
-    assert q.qmoe_sample_workspace_bytes(262144, 64) == 64 * 64 * 8
+    assert q.qmoe_sample_workspace_bytes(262144, 64) == 256 * 64 * 8
     assert q.qmoe_sample_workspace_bytes(1 << 20, 64) == 256 * 64 * 8
 
 

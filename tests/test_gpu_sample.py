@@ -102,3 +102,19 @@ def test_sample_temperature_zero_is_argmax(torch_cuda, q):
     lg[123457] = 50.0
     for u in (0.0, 0.5, 0.99):
         assert _run(torch, q, lg, 0.0, 64, 0.95, u)[0] == 123457
+
+
+@pytest.mark.parametrize("V", [262144, 9000, 300])
+def test_sample_bound_and_filter_extremes(torch_cuda, q, V):
+    """Inputs that leave the most keys at or above the final block's bound:
+    equal logits (every block's keys tie; the bound keeps up to K * K of
+    them) and logits rising with the token id within each block of 1024
+    (every block's leading keys alike)."""
+    torch = torch_cuda
+    for lg in (np.full(V, 0.75, dtype=np.float32),
+               (np.arange(V) % 1024).astype(np.float32) * 1e-3):
+        for u in (0.05, 0.7):
+            tok, ranked = _run(torch, q, lg, 0.2, 64, 0.95, u)
+            ref = oracle.sample(lg, 0.2, 64, 0.95, u)
+            assert np.array_equal(ranked, ref["ranked"])
+            assert tok == ref["token"] or _certified(ref, 0.2, 0.95, u, tok)
