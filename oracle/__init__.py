@@ -270,7 +270,7 @@ def lfu_replay(need: np.ndarray, n_experts: int, slots: int):
 
 
 def sample(logits: np.ndarray, temperature: float, top_k: int, top_p: float, u: float):
-    """O10: the sampled token id, the ranked top_k ids, their cumulative
+    """The sampled token id, the ranked top_k ids, their cumulative
     masses over the total (fp64) and the number of kept ranks."""
     logits = _c(logits, np.float32)
     ranked = np.zeros(top_k, dtype=np.int32)
@@ -295,7 +295,7 @@ def rope(x: np.ndarray, pos: int, base: float) -> np.ndarray:
 
 def attn_step(q: np.ndarray, k: np.ndarray, v: np.ndarray, khist: np.ndarray,
               vhist: np.ndarray, pos: int, window: int, scale: float, base: float) -> np.ndarray:
-    """O11: one decode attention step of the token at time ``pos``.
+    """One decode attention step of the token at time ``pos``.
 
     q [Hq][D], k and v [Hkv][D] (fp32); khist and vhist [times][Hkv][D] fp16
     bits in time order, modified in place (time ``pos`` is written).  Returns

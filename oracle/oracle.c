@@ -124,7 +124,7 @@ uint16_t orc_double_to_bf16(double v) {
   return sign | (uint16_t)(be << 7) | (uint16_t)frac;
 }
 
-/* ------------------------------------------------------ O1/O2: codes */
+/* ------------------------------------------------------------ codes */
 /* Code j of a word occupies bits [j*b, (j+1)*b), least significant first;
  * column c of row r lives in word c/(32/b) of that row. */
 static int orc_code(const uint32_t* q, int64_t row, int64_t cols, int bits,
@@ -181,7 +181,7 @@ void orc_qgemv(const uint32_t* q, const uint16_t* s, const uint16_t* b,
   orc_qgemv_m(&m, rows, cols, bits, x, y);
 }
 
-/* ----------------------------------------------------------- O3 RMSNorm */
+/* -------------------------------------------------------------- RMSNorm */
 /* h_i = bf16( x_i * gamma_i / sqrt(mean(x^2) + eps) ). */
 void orc_rmsnorm(const uint16_t* x, const uint16_t* gamma, int64_t H,
                  double eps, uint16_t* h) {
@@ -203,7 +203,7 @@ double orc_gelu_tanh(double z) {
   return 0.5 * z * (1.0 + tanh(k * (z + 0.044715 * z * z * z)));
 }
 
-/* --------------------------------------------------- O4 routing top-k */
+/* ------------------------------------------------------ routing top-k */
 /* Keep the k largest logits, ordered by descending logit and, among equal
  * logits, ascending expert index; their weights are the softmax over the
  * kept logits (the same numbers as a softmax over all E followed by
@@ -243,7 +243,7 @@ void orc_router_logits(const orc_layer* L, const uint16_t* h, double* logits) {
   free(hd);
 }
 
-/* ------------------------------------------------------------- O5 FFN */
+/* ---------------------------------------------------------------- FFN */
 /* y = W_down (gelu(W_gate h) * (W_up h)), all in double. */
 static void orc_ffn(const orc_qmat* g, const orc_qmat* u, const orc_qmat* d,
                     int32_t H, int32_t I, const double* h, double* y) {
@@ -265,7 +265,7 @@ void orc_expert_ffn(const orc_qmat* g, const orc_qmat* u, const orc_qmat* d,
   free(hd);
 }
 
-/* ------------------------------------------------ O3..O6 one MoE layer */
+/* ------------------------------------------------------ one MoE layer */
 /* One token through one layer.
  *   x        bf16 [H]: layer input
  *   residual nonzero: out = bf16(x + y), else out = bf16(y)
@@ -321,7 +321,7 @@ int orc_layer_forward(const orc_layer* L, const uint16_t* x, int residual,
   return 0;
 }
 
-/* ------------------------------------------- O7 prefill expert dispatch */
+/* ---------------------------------------------- prefill expert dispatch */
 /* Group the T*K (token, rank) pairs of a chunk by expert, stably: by
  * expert, then token, then rank.  counts[E], offsets[E+1] (exclusive
  * prefix of counts), perm[T*K] holds flat pair indices t*K + j. */
@@ -337,7 +337,7 @@ void orc_dispatch(const int32_t* idx, int32_t T, int32_t K, int32_t E,
       if (idx[p] == e) perm[n++] = p;
 }
 
-/* ---------------------------------------------------- O9 LFU replay */
+/* -------------------------------------------------------- LFU replay */
 /* Per-layer expert cache with `slots` device slots and least-frequently-used
  * replacement ([devtrends] "Qual è il trucco principale dell'architettura";
  * [remio] "Mac Gemma 4 26B entra nello spazio disponibile…").
@@ -415,7 +415,7 @@ done:
   return hits;
 }
 
-/* ------------------------------------------------------ O10 sampling */
+/* ---------------------------------------------------------- sampling */
 /* The token choice after the last layer.  [elsolitario] TurboFieldfare
  * article, section "Cómo empezar": temperature 0.2, top-K 64 and top-P 0.95
  * by default, temperature 0 for deterministic output; [pikobit] "Un modello

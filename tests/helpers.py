@@ -123,7 +123,7 @@ def routing_certified(bound, logits64, gidx) -> bool:
     """True when the device's ranking gidx (top-k in rank order, every other
     expert below the last) is consistent with the fp64 logits moved by at
     most `bound` each: for every expert a the device ranks above b,
-    l_b - l_a <= bound_a + bound_b (SURVEY's P6 certificate)."""
+    l_b - l_a <= bound_a + bound_b."""
     lg = np.asarray(logits64, np.float64)
     B = np.asarray(bound, np.float64)
     sel = [int(e) for e in gidx]

@@ -1,5 +1,5 @@
 """GPU parity of the token sampling step (qmoe_sample) against the fp64
-oracle (O10), through the C ABI.  The kept candidates (top-K ids in rank
+oracle, through the C ABI.  The kept candidates (top-K ids in rank
 order) are integer work on the same fp32 logits: bit-exact.  The drawn token
 is decided in fp32 on the GPU and fp64 in the oracle: equal, or the draw or
 the top-P cut lies within the fp32 rounding of a cumulative mass

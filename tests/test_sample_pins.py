@@ -1,4 +1,4 @@
-"""Pins of the oracle's sampling step (O10) against closed forms: the
+"""Pins of the oracle's sampling step against closed forms: the
 defaults of the pages (elsolitario.org, TurboFieldfare article, section
 "Cómo empezar": temperature 0.2, top-K 64, top-P 0.95; temperature 0 is
 deterministic) and cases whose answer follows from the definition alone.
