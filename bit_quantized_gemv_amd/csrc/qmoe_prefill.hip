@@ -583,13 +583,19 @@ __device__ __forceinline__ bool pf_unit(const int32_t* items, int T, int tsh, in
     const int b2 = b - nsh * tsh;
     it = nsh + b2 / tr;
     tile = b2 - (it - nsh) * tr;
-    if (it >= items[0]) return false;
   }
-  u.e = items[1 + 3 * it];
-  u.row0 = items[2 + 3 * it];
-  u.M = items[3 + 3 * it];
+  // one round trip: the item's words are read together with the item count
+  // (the list has room for every item the grid can name)
+  // (the empty asm uses all four before the compare: the compiler would
+  // otherwise read the item's words only after it, a second round trip)
+  const int n = items[0];
+  const int e = items[1 + 3 * it], row0 = items[2 + 3 * it], M = items[3 + 3 * it];
+  asm volatile("" ::"s"(n), "s"(e), "s"(row0), "s"(M));
+  u.e = e;
+  u.row0 = row0;
+  u.M = M;
   u.n0 = tile * kPfRows;
-  return true;
+  return it < n;
 }
 
 // gate/up: one block per unit (1-D grid); a unit of the shared expert
