@@ -107,11 +107,11 @@ struct AttnArgs {
 // Merging block m of key/value head g (launched after the head's split
 // blocks, so it never waits for a block that is not yet running): outputs
 // 64 m .. 64 m + 63 of the head's group (head t / D, dim t % D).  Thread
-// (j = tid / 64, o = tid % 64) takes splits j, j + 4, ...  First a cheap
-// poll of one word per split (a max word, tag checked) until every split
-// has published; then every word it needs, 8 splits per round trip with
-// the tags checked in plain arithmetic (any stale word: load again); the
-// four split groups meet in LDS.  The epoch word (g, m) is this block's
+// (j = tid / 64, o = tid % 64) takes splits j, j + 4, ...: every word it
+// needs, 8 splits per round trip, with the tags checked in plain arithmetic
+// (any stale word: load the batch again), so the wait for a late split and
+// the read of its words are the same loads; the four split groups meet in
+// LDS.  The epoch word (g, m) is this block's
 // own: it reads it first and writes the next value last; every merging
 // block of every call that splits steps its word once, so the words of a
 // head stay equal to the one the split blocks read, (g, 0).
@@ -127,20 +127,8 @@ __device__ void attn_merge(const AttnArgs& a, int g, int m) {
   const uint64_t* gp = a.part + (int64_t)g * a.nsplit * G * (D + 2);
   bool failed = false;
   if (mine) {
-    // 1. every split has published (one max word each)
-    const int h0 = (m * kOut) / D;
-    for (int spin = 0;; ++spin) {
-      uint32_t bad = 0;
-      for (int sp = threadIdx.x; sp < a.nsplit; sp += kAttnWaves * 64)
-        bad |= (uint32_t)(ld_dev(gp + ((int64_t)sp * G + h0) * (D + 2) + D) >> 32) ^ tag;
-      if (!__syncthreads_or(bad != 0)) break;
-      if (spin >= kAttnSpinLimit) {
-        failed = true;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(4);
-    }
-    // 2. the words, merged online over this thread's splits
+    // the words, merged online over this thread's splits; each batch
+    // polls its own words until all carry this call's tag
     const int tt = t < G * D ? t : 0;
     const int row = (tt / D) * (D + 2), d = tt % D;
     float M = -INFINITY, on = 0.f, ln = 0.f;
@@ -166,7 +154,7 @@ __device__ void attn_merge(const AttnArgs& a, int g, int m) {
           failed = true;
           break;
         }
-        __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_s_sleep(4);
       }
       float Mb = M;
 #pragma unroll
@@ -188,7 +176,7 @@ __device__ void attn_merge(const AttnArgs& a, int g, int m) {
     gl[j][o] = ln;
     go[j][o] = on;
   }
-  __syncthreads();
+  const bool any_failed = __syncthreads_or(failed);
   if (mine && j == 0 && t < G * D) {
     float Mt = -INFINITY;
 #pragma unroll
@@ -204,7 +192,7 @@ __device__ void attn_merge(const AttnArgs& a, int g, int m) {
     a.out[(int64_t)(g * G) * D + t] = f32_to_bf16(on / ln);
   }
   if (threadIdx.x == 0) {
-    if (failed) st_dev(a.ctl + kAttnErr, 1u);
+    if (any_failed) st_dev(a.ctl + kAttnErr, 1u);
     st_dev(ep, tag);
   }
 }
