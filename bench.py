@@ -105,10 +105,12 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(lw, X):
+def cpu_baseline(lw, X, Xp=None, prior=None):
     """The fp64 oracle (as it stands) on a bounded sample of tokens of the
     same layer: one thread over a few tokens, then every host core (one
-    token per thread) over a larger sample."""
+    token per thread) over a larger sample; with Xp, also one whole prefill
+    chunk (the chunk's tokens through the layer with the Zipf log-prior on
+    the router logits, one token per thread)."""
     import oracle
 
     L = oracle.OracleLayer(lw)
@@ -124,11 +126,22 @@ def cpu_baseline(lw, X):
     t0 = time.perf_counter()
     oracle.forward_many(L, X[:n], threads=threads)
     dt = time.perf_counter() - t0
-    return {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "value_1thread": one, "cpu_model": cpu_model(), "host_cores": cores,
-            "sample": f"{n} decode tokens of one layer (same shapes and weights) on {threads} "
-                      f"threads, one token per thread; 1-thread figure over {n1} tokens; "
-                      f"fp64 scalar C oracle"}
+    res = {"value": n / dt, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+           "value_1thread": one, "cpu_model": cpu_model(), "host_cores": cores,
+           "sample": f"{n} decode tokens of one layer (same shapes and weights) on {threads} "
+                     f"threads, one token per thread; 1-thread figure over {n1} tokens; "
+                     f"fp64 scalar C oracle"}
+    if Xp is not None:
+        P = oracle.OracleLayer(lw, logit_bias=prior)
+        t0 = time.perf_counter()
+        oracle.forward_many(P, Xp, threads=cores)
+        dt = time.perf_counter() - t0
+        res["prefill"] = {"tokens_per_s": Xp.shape[0] / dt, "us_per_chunk": dt * 1e6,
+                          "cores": min(cores, Xp.shape[0]),
+                          "sample": f"one {Xp.shape[0]}-token prefill chunk (the prefill leg's "
+                                    f"tokens and Zipf(1.1) log-prior) on {min(cores, Xp.shape[0])} "
+                                    f"threads, one token per thread"}
+    return res
 
 
 def main():
@@ -345,7 +358,9 @@ def main():
         copy_calibration(torch)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        res["cpu_baseline"] = cpu_baseline(lw, X)
+        pw = synth.WORKLOADS["prefill128"]
+        res["cpu_baseline"] = cpu_baseline(lw, X, synth.make_tokens(pw, PF_TOKENS, stream=2),
+                                           synth.zipf_prior(pw, 0))
     torch.cuda.synchronize()
     print(json.dumps(res), flush=True)
 
