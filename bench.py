@@ -664,14 +664,50 @@ def streaming_leg(torch, q, synth, sd, steps: int = 512):
            "warm": f"second half of the run ({warm_tokens} tokens)",
            "overlap_basis": "(t_serialized - t_overlapped) / (t_serialized - t_resident), "
                             "same tokens and LFU decisions"}
+    res["h2d_ceiling_GBps"] = h2d_ceiling(torch, host.view(-1), blob)
     log(f"streaming: {res['tokens_per_s']:.1f} tokens/s, hit rate {res['hit_rate']:.3f} "
         f"(warm {res['hit_rate_warm']:.3f}), H2D {res['h2d_GBps']:.1f} GB/s, overlap "
         f"{res['overlap_achieved']:.2f} (resident {res['tokens_per_s_resident']:.0f}, "
-        f"serialized {res['tokens_per_s_serialized_copies']:.0f} tokens/s)")
+        f"serialized {res['tokens_per_s_serialized_copies']:.0f} tokens/s); pinned-copy "
+        f"ceiling {res['h2d_ceiling_GBps']}")
     del dls, arenas, host
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
+
+
+def h2d_ceiling(torch, host, blob: int, n: int = 96, reps: int = 3):
+    """Practical host -> device ceiling: pinned copies of one expert blob
+    (the pool's unit), on one stream and as two halves on two streams (as
+    the pool issues them), and 64 MB copies; best of `reps` rounds of n
+    copies, wall clock."""
+    big = 64 << 20
+    dev = torch.empty(max(n * blob, 8 * big), dtype=torch.uint8, device="cuda")
+    streams = [torch.cuda.Stream() for _ in range(2)]
+
+    def rate(size, count, lanes):
+        best = 0.0
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(count):
+                o = i * size
+                if lanes == 1:
+                    with torch.cuda.stream(streams[0]):
+                        dev[o:o + size].copy_(host[o:o + size], non_blocking=True)
+                else:
+                    h = size // 2
+                    for k, (a, b) in enumerate(((o, o + h), (o + h, o + size))):
+                        with torch.cuda.stream(streams[k]):
+                            dev[a:b].copy_(host[a:b], non_blocking=True)
+            torch.cuda.synchronize()
+            best = max(best, count * size / (time.perf_counter() - t0) / 1e9)
+        return round(best, 1)
+
+    out = {"blob_one_stream": rate(blob, n, 1), "blob_halves_two_streams": rate(blob, n, 2),
+           "64MB_one_stream": rate(big, 8, 1)}
+    del dev
+    return out
 
 
 def gemv_leg(torch, q, sptr, rows: int = 65536, cols: int = 2816, copies: int = 8,
