@@ -212,11 +212,11 @@ __global__ __launch_bounds__(1024) void k_pf_dispatch(const int32_t* idx, int n,
 // One block: 64 weight rows (wave w: rows n0 + 16w + l%16) of NM matrices
 // against up to 64 rows of A (an item: one expert's tokens), K in steps of
 // 128 codes.  Per step the block stages its A rows (fp16, prepared layout)
-// in LDS once for all four waves; each wave stages its 16 weight rows in a
-// code tile of its own (pf_pass), from which lane (n = l%16, j = l/16)
-// takes codes [128kb + 32j, +32) of its row as 4 words; word t feeds MFMA t
-// (K slots 8j..8j+7), dequantized to fp16 in the order
-// (q0,q2,q4,q6,q1,q3,q5,q7).
+// in LDS once for all four waves; lane (n = l%16, j = l/16) of a wave loads
+// codes [128kb + 32j, +32) of its weight row straight into registers as 4
+// words (the four lanes j of a row read 64 contiguous bytes, and the two
+// steps of a pair the row's whole 128-byte line); word t feeds MFMA t (K
+// slots 8j..8j+7), dequantized to fp16 in the order (q0,q2,q4,q6,q1,q3,q5,q7).
 __device__ __forceinline__ h8_t dequant_word(uint32_t v, h2_t s2, h2_t b2) {
   const uint32_t lo = v & 0x0F0F0F0Fu, hi = (v >> 4) & 0x0F0F0F0Fu;
   h2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 512.0f, false);  // q0, q2
@@ -255,66 +255,49 @@ typedef unsigned int u4v_t __attribute__((ext_vector_type(4)));
 constexpr int kPfWaves = kBlock / 64;
 
 // LDS of a block: the A rows of two K-steps (double buffer), the A row
-// offsets, and per wave and matrix the codes of one pair of K-steps (the
-// wave's 16 weight rows × 128 bytes, 16-byte slots swizzled per row).  With
-// SB, per wave and matrix also the scales and biases of the wave's 16 rows
-// over all K/64 groups: [16][G] scales, then [16][G] biases, filled once per
-// pass (whole 64-lane writes of 16 bytes: 1536 halves for G <= 48).
+// offsets, and with SB, per wave and matrix the scales and biases of the
+// wave's 16 rows over all K/64 groups: [16][G] scales, then [16][G] biases,
+// filled once per pass (whole 64-lane writes of 16 bytes: 1536 halves for
+// G <= 48).
 constexpr int kPfSbMaxG = 48;
 constexpr int kPfSbHalves = 1536;
 template <int NM, bool SB>
 struct PfShared {
   _Float16 a[2][kPfMaxM * kPfAStride];
   int32_t rows[kPfMaxM];  // element offset of each A row from the A base
-  u4v_t w[kPfWaves][NM][16 * 8];
   uint16_t sb[kPfWaves][NM][SB ? kPfSbHalves : 1];
 };
 
-// Slot of 16-byte chunk c of row r (r < 16) in a wave's code tile: rows are
-// 128 bytes, so a plain layout puts the same chunk of every row in the same
-// banks; the rotation by r + r/8 spreads the 16 rows of one MFMA fragment
-// read over distinct slots (both for 8 and for 16 lanes per LDS cycle).
-__device__ __forceinline__ int pf_wslot(int r, int c) { return r * 8 + (c ^ ((r + (r >> 3)) & 7)); }
-
-// Codes of one pair of K-steps (256 codes = 128 bytes per row), loaded as
-// whole 128-byte lines: lane l takes chunk l%8 of rows l/8 and 8 + l/8 of
-// the wave's 16 rows.  Past the end of a row the last chunk is re-read:
+// Codes of one pair of K-steps (2p, 2p + 1) for this lane, in the layout
+// the MFMAs take: v[k][h] = codes [128 (2p + h) + 32 j, +32) of row n of
+// matrix k (16 bytes).  Past the end of a row the last chunk is re-read:
 // finite values whose products meet zero A columns.
 template <int NM>
 struct PfWG {
   u4v_t v[NM][2];
 };
 struct PfGOff {
-  uint32_t row0, row1;  // byte offsets of the lane's two rows
-  uint32_t c16;         // 16 (l % 8)
-  uint32_t qmax;        // last 16-byte chunk of a row: K/2 - 16
+  uint32_t row;   // byte offset of the lane's row
+  uint32_t j16;   // 16 j: the lane's bytes within a step
+  uint32_t qmax;  // last 16-byte chunk of a row: K/2 - 16
 };
 __device__ __forceinline__ PfGOff pf_goff(int n_wave0, int K) {
   const int lane = threadIdx.x & 63;
   PfGOff o;
-  o.row0 = (uint32_t)(n_wave0 + (lane >> 3)) * (uint32_t)(K / 2);
-  o.row1 = (uint32_t)(n_wave0 + 8 + (lane >> 3)) * (uint32_t)(K / 2);
-  o.c16 = 16u * (uint32_t)(lane & 7);
+  o.row = (uint32_t)(n_wave0 + (lane & 15)) * (uint32_t)(K / 2);
+  o.j16 = 16u * (uint32_t)(lane >> 4);
   o.qmax = (uint32_t)(K / 2 - 16);
   return o;
 }
 template <int NM>
 __device__ __forceinline__ void pf_load_wg(PfWG<NM>& G, const DevQ (&W)[NM], const PfGOff& o,
-                                           int bs) {
-  const uint32_t off = min(128u * (uint32_t)bs + o.c16, o.qmax);
+                                           int p) {
+  const uint32_t o0 = min(128u * (uint32_t)p + o.j16, o.qmax);
+  const uint32_t o1 = min(128u * (uint32_t)p + 64u + o.j16, o.qmax);
 #pragma unroll
   for (int k = 0; k < NM; ++k) {
-    G.v[k][0] = *reinterpret_cast<const u4v_t*>(W[k].q + (o.row0 + off));
-    G.v[k][1] = *reinterpret_cast<const u4v_t*>(W[k].q + (o.row1 + off));
-  }
-}
-template <int NM>
-__device__ __forceinline__ void pf_store_wg(const PfWG<NM>& G, u4v_t (*wl)[16 * 8]) {
-  const int lane = threadIdx.x & 63, r = lane >> 3, c = lane & 7;
-#pragma unroll
-  for (int k = 0; k < NM; ++k) {
-    wl[k][pf_wslot(r, c)] = G.v[k][0];
-    wl[k][pf_wslot(r + 8, c)] = G.v[k][1];
+    G.v[k][0] = *reinterpret_cast<const u4v_t*>(W[k].q + (o.row + o0));
+    G.v[k][1] = *reinterpret_cast<const u4v_t*>(W[k].q + (o.row + o1));
   }
 }
 
@@ -382,11 +365,11 @@ __device__ __forceinline__ void pf_store_a(const PfA<NMS>& A, _Float16* buf) {
 }
 
 // MFMAs of one K-step kb: the lane's codes (16 bytes of row n = l%16 per
-// matrix, half h of the pair in the wave's code tile), dequantized with
+// matrix, half h of the pair in C), dequantized with
 // the group's scale and bias (from the wave's LDS table with SB, else as
 // loaded into B), against the staged A rows.
 template <int NM, int NMS, bool SB>
-__device__ __forceinline__ void pf_mma(const u4v_t (*wl)[16 * 8], int h, const PfSB<NM>& B,
+__device__ __forceinline__ void pf_mma(const PfWG<NM>& C, int h, const PfSB<NM>& B,
                                        const uint16_t (*tb)[SB ? kPfSbHalves : 1], int kb, int K,
                                        const _Float16* buf, f4_t (&acc)[NMS][NM]) {
   const int lane = threadIdx.x & 63, m = lane & 15, j = lane >> 4;
@@ -394,7 +377,7 @@ __device__ __forceinline__ void pf_mma(const u4v_t (*wl)[16 * 8], int h, const P
   h8_t Bf[NM][4];
 #pragma unroll
   for (int k = 0; k < NM; ++k) {
-    const u4v_t q = wl[k][pf_wslot(m, 4 * h + j)];
+    const u4v_t q = C.v[k][h];
     const _Float16 sv = __builtin_bit_cast(_Float16, SB ? tb[k][m * G + g] : (uint16_t)B.s[k]);
     const _Float16 bv =
         __builtin_bit_cast(_Float16, SB ? tb[k][16 * G + m * G + g] : (uint16_t)B.b[k]);
@@ -420,43 +403,53 @@ __device__ __forceinline__ void pf_mma(const u4v_t (*wl)[16 * 8], int h, const P
   }
 }
 
+// Depth of the pipeline: pairs of K-steps whose codes are held in registers
+// (kPfPD), and A row sets loaded ahead for up to 32 rows and for more.
+// 2 kPfPD must be a multiple of both.  (Deeper settings, 3 or 4 pairs and
+// 4 or 8 A sets, measured no faster on the 128-token chunk.)
+constexpr int kPfPD = 2;
+constexpr int kPfADSmall = 4;
+constexpr int kPfADBig = 2;
+
 // C = A W^T over one pass of Mc <= 64 A rows (sh.rows[0..Mc) set: element
 // offsets of rows of pad128(K) columns, the padding zero), K columns, for
 // the wave's 16 weight rows from n_wave0 on; acc[ms][k]: lane l holds rows
 // 16ms + 4(l/16) + r, column n_wave0 + l%16.
 //
-// Pipeline, per iteration four K-steps kb..kb+3 (two pairs):
-//  - codes: each pair of steps is loaded as whole lines into registers
-//    (two alternating sets, four steps ahead) and written to the wave's
-//    code tile in LDS right before its first step;
-//  - scales and biases: per step, four steps ahead (four sets);
+// Pipeline, per iteration SPI = 2 PD K-steps:
+//  - codes: pair i of the iteration in register set G[i], which takes pair
+//    i + PD once both of its steps are done;
+//  - scales and biases (without SB): per step, NSS steps ahead (NSS sets);
 //  - A rows: in AD register sets, loaded AD + 1 steps ahead and stored, AD
 //    steps after their loads were issued, to the LDS buffer of the next
-//    step (two alternating buffers, one barrier per step).  AD is 4 for up
-//    to 32 rows and 2 for more (bounded registers).
+//    step (two alternating buffers, one barrier per step).
 // Loads and stores are unconditional (past the last step they re-read the
-// last one); only the MFMAs of steps past the last are skipped, by a
-// uniform branch.  So every wait for a load in flight waits for that load
-// only.
+// last one), so every wait for a load in flight waits for that load only;
+// the last iteration stops after step nkb - 1 (a uniform branch).  Loads
+// complete in issue order, so a code load is complete at the latest when
+// the A load issued after it is needed: AD steps bound the codes' lead too.
 // rows(): writes sh.rows[0..Mc) and ends with a block barrier; it runs
 // after the first weight loads are issued, so its reads overlap them.
 template <int NM, int NMS, bool SB, typename Rows>
 __device__ __forceinline__ void pf_pass(const DevQ (&W)[NM], int n_wave0, int K, int Mc,
                                         const _Float16* abase, PfShared<NM, SB>& sh,
                                         f4_t (&acc)[NMS][NM], Rows rows) {
-  constexpr int AD = NMS <= 2 ? 4 : 2;
+  constexpr int PD = kPfPD;
+  constexpr int SPI = 2 * PD;
+  constexpr int AD = NMS <= 2 ? kPfADSmall : kPfADBig;
+  static_assert(SPI % AD == 0, "A sets must divide the steps of an iteration");
+  constexpr int NSS = SPI % 4 == 0 ? 4 : (SPI % 3 == 0 ? 3 : 2);
 #pragma unroll
   for (int ms = 0; ms < NMS; ++ms)
 #pragma unroll
     for (int k = 0; k < NM; ++k) acc[ms][k] = f4_t{0.f, 0.f, 0.f, 0.f};
   const int nkb = (K + 127) / 128;
   const int wave = threadIdx.x >> 6;
-  u4v_t(*wl)[16 * 8] = sh.w[wave];
   const PfGOff go = pf_goff(n_wave0, K);
   const PfSOff so = pf_soff(n_wave0 + ((threadIdx.x & 63) & 15), K);
-  PfWG<NM> G0, G1;
-  PfSB<NM> S0, S1, S2, S3;  // without SB: scales and biases, four steps ahead
-  PfA<NMS> R[AD];  // R[(s + 1) % AD] holds A(s + 1) when step s begins
+  PfWG<NM> G[PD];
+  PfSB<NM> S[NSS];  // without SB: scales and biases, NSS steps ahead
+  PfA<NMS> R[AD];   // R[(s + 1) % AD] holds A(s + 1) when step s begins
   if constexpr (SB) {
     // the table: 16-byte units of the wave's rows' scales, then biases,
     // straight into LDS (no registers); issued first, so the waits below
@@ -476,54 +469,44 @@ __device__ __forceinline__ void pf_pass(const DevQ (&W)[NM], int n_wave0, int K,
       }
   }
   // prologue: the loads of a virtual iteration before the first, in the
-  // loop's own order (G0; per step t the A set it refills, then S_t; G1
-  // before step 2), so that at the loop head the waits counted along both
-  // incoming paths agree: codes of pairs 0 and 1, scales and biases of
-  // steps 0..3, A(1)..A(AD) into R[t % AD]; A(0) goes to LDS buffer 0.
-  pf_load_wg<NM>(G0, W, go, 0);
+  // loop's own order (per step t the A set it refills, then its scales;
+  // after each pair's second step that pair's codes), so that at the loop
+  // head the waits counted along both incoming paths agree: codes of pairs
+  // 0..PD-1 (pair 0 first of all, before rows()), scales and biases of
+  // steps 0..NSS-1, A(1)..A(AD); A(0) goes to LDS buffer 0.
+  pf_load_wg<NM>(G[0], W, go, 0);
   rows();
   uint32_t roff[NMS];
   pf_rows<NMS, NM, SB>(roff, sh, Mc);
   PfA<NMS> A0;
   pf_load_a<NMS>(A0, abase, roff, 0);
-  // step t of the virtual iteration loads A(t + 1 - (4 - AD)) when that is
-  // >= 1 (AD = 4: A(1..4); AD = 2: A(1), A(2) in steps 2 and 3)
-  auto pro = [&](int t, PfSB<NM>& S) {
-    const int ia = t + 1 - (4 - AD);
+#pragma unroll
+  for (int t = 0; t < SPI; ++t) {
+    const int ia = t + 1 + AD - SPI;
     if (ia >= 1) pf_load_a<NMS>(R[(t + 1) % AD], abase, roff, min(ia, nkb - 1));
-    if constexpr (!SB) pf_load_sb<NM>(S, W, so, t);
-  };
-  pro(0, S0);
-  pro(1, S1);
-  pf_load_wg<NM>(G1, W, go, 1);
-  pro(2, S2);
-  pro(3, S3);
+    if constexpr (!SB)
+      if (t >= SPI - NSS) pf_load_sb<NM>(S[t % NSS], W, so, t - (SPI - NSS));
+    if ((t & 1) && (t >> 1) > 0) pf_load_wg<NM>(G[t >> 1], W, go, t >> 1);
+  }
   pf_store_a<NMS>(A0, sh.a[0]);
   __syncthreads();
   // one step s = kb + t: A(s + 1) to the other buffer, A(s + 1 + AD) into
-  // the set just freed, the MFMAs on A(s), scales and biases of s + 4
-  auto step = [&](int kb, int t, PfSB<NM>& S) {
+  // the set just freed, the MFMAs on A(s), scales and biases of s + NSS
+  auto step = [&](int kb, int t, PfSB<NM>& Sx, const PfWG<NM>& C) {
     PfA<NMS>& X = R[(t + 1) % AD];
     pf_store_a<NMS>(X, sh.a[(t + 1) & 1]);
     pf_load_a<NMS>(X, abase, roff, min(kb + t + 1 + AD, nkb - 1));
-    if (t == 0 || kb + t < nkb)
-      pf_mma<NM, NMS, SB>(wl, t & 1, S, sh.sb[wave], kb + t, K, sh.a[t & 1], acc);
-    if constexpr (!SB) pf_load_sb<NM>(S, W, so, kb + t + 4);
+    pf_mma<NM, NMS, SB>(C, t & 1, Sx, sh.sb[wave], kb + t, K, sh.a[t & 1], acc);
+    if constexpr (!SB) pf_load_sb<NM>(Sx, W, so, kb + t + NSS);
     __syncthreads();
   };
-  for (int kb = 0; kb < nkb; kb += 4) {
-    const int bs = kb >> 1;
-    // pair bs: its codes to the wave's tile, then the codes of pair bs + 2
-    pf_store_wg<NM>(G0, wl);
-    pf_load_wg<NM>(G0, W, go, bs + 2);
-    step(kb, 0, S0);
-    step(kb, 1, S1);
-    // pair bs + 1 (the tile's reads of pair bs are issued: LDS operations
-    // of one wave run in order)
-    pf_store_wg<NM>(G1, wl);
-    pf_load_wg<NM>(G1, W, go, bs + 3);
-    step(kb, 2, S2);
-    step(kb, 3, S3);
+  for (int kb = 0; kb < nkb; kb += SPI) {
+#pragma unroll
+    for (int t = 0; t < SPI; ++t) {
+      if (t > 0 && kb + t >= nkb) break;
+      step(kb, t, S[t % NSS], G[t >> 1]);
+      if (t & 1) pf_load_wg<NM>(G[t >> 1], W, go, (kb >> 1) + (t >> 1) + PD);
+    }
   }
 }
 
