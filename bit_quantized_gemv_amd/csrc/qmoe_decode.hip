@@ -36,8 +36,9 @@
 // exchanged values travel as device-coherent stores/loads; small values
 // that many blocks poll (router logits, flags, gate/up activations) are
 // written in a few replicas so that pollers spread over memory channels.
-// No cache fences; the only atomics are the completion counts that advance
-// the tag counter at the end of a call.
+// No cache fences; the only atomics are the counts that advance the tag
+// counter (every block's registration in a fused one-layer call, the last
+// role's completion counts otherwise).
 //
 // Every weight and scale load is unconditional (out-of-range chunks re-read
 // a valid address and only the arithmetic is predicated) and, for the model
@@ -130,6 +131,8 @@ struct DecodeArgs {
   uint32_t ntags;           // tag values the call uses (advance of the tag counter)
   int heal;                 // 1: a failed wait is cleared by the call's last block (no
                             // caller can read the error word of this workspace)
+  int early;                // 1: the first shared block advances the tag counter once
+                            // every block has registered (see early_advance)
 };
 constexpr int kCntNone = 0, kCntS = 1, kCntD = 2;
 
@@ -227,12 +230,77 @@ __device__ void call_done(const DecodeArgs& a, int i, int n, uint32_t gen, uint3
   }
 }
 
-// One full wave: wait until flags[0..n) all equal `epoch`.  Every poll reads
-// all n flags at once (a few loads per lane), so the wait ends one round
-// trip after the last flag is raised.
 constexpr int kPollSleep = 1;  // s_sleep units (64 cycles) between polls: a poll is a round trip
                                // already (decode step: 0, 1, 2, 6 units gave 19.79, 19.81,
                                // 19.85, 20.02 us)
+
+// Early advance of the tag counter (a one-layer call with every role in one
+// launch and shared blocks): each block, once it has used the call's tag
+// (so that its read of the counter is complete), adds 1 to the done count
+// of its group (block index % kGenRep), without waiting for the atomic; the
+// first shared block, after its own publication, waits until the groups'
+// counts add up to the launch's blocks, zeroes them and advances the
+// counter.  Every block has read the counter by then, so the advance is the
+// same one the output blocks' completion count would make at the end, but
+// it is off the call's critical path: the output blocks end right after
+// their stores.  Near the top of the counter's range the restart must wait
+// until no block reads the control area any more: such a call counts at the
+// end as the other modes do.
+__device__ __forceinline__ bool early_on(const DecodeArgs& a, uint32_t gen) {
+  return a.early && gen + a.ntags < ctl::kGenLimit;
+}
+__device__ __forceinline__ void call_register(const DecodeArgs& a, uint32_t epoch,
+                                              int tid = threadIdx.x) {
+  if (tid == 0) {
+    uint32_t one = 1u;
+    asm volatile("" : "+v"(one) : "v"(epoch));  // issued after the tag's load returned
+    uint32_t* c = reinterpret_cast<uint32_t*>(a.ws + a.wl.ctl + ctl::kCntBase +
+                                              64 * (ctl::kCntDone + blockIdx.x % ctl::kGenRep));
+    (void)__hip_atomic_fetch_add(c, one, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+// The first shared block, whole block: wait (bounded) for every block's
+// registration, then zero the counts and raise the counter by the call's
+// tags.  A wait that gives up sets the error word (code 5) and leaves the
+// counter (qmoe_workspace_status restarts the control area).
+__device__ void early_advance(const DecodeArgs& a, uint32_t gen, int tid = threadIdx.x) {
+  if (tid == 0) {
+    uint8_t* c = a.ws + a.wl.ctl;
+    uint32_t* cnt = reinterpret_cast<uint32_t*>(c + ctl::kCntBase + 64 * ctl::kCntDone);
+    uint32_t* err = reinterpret_cast<uint32_t*>(c) + ctl::kError;
+    const uint32_t total = gridDim.x;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    bool ok = true;
+    for (int it = 0;; ++it) {
+      uint32_t v[ctl::kGenRep], n = 0;  // every load issued before the sum
+#pragma unroll
+      for (int g = 0; g < ctl::kGenRep; ++g) v[g] = ld_dev(cnt + 16 * g);
+#pragma unroll
+      for (int g = 0; g < ctl::kGenRep; ++g) n += v[g];
+      if (n == total) break;
+      if ((it & 15) == 15) {
+        if (ld_dev(err) != 0 || __builtin_amdgcn_s_memrealtime() - t0 > kWaitTicks) {
+          if (ld_dev(err) == 0) st_dev(err, 5u);
+          ok = false;
+          break;
+        }
+      }
+      __builtin_amdgcn_s_sleep(kPollSleep);
+    }
+    if (ok) {
+#pragma unroll
+      for (int g = 0; g < ctl::kGenRep; ++g) {
+        st_dev(cnt + 16 * g, 0u);
+        st_dev(reinterpret_cast<uint32_t*>(c + ctl::kGenBase + ctl::kGenStride * g),
+               gen + a.ntags);
+      }
+    }
+  }
+}
+
+// One full wave: wait until flags[0..n) all equal `epoch`.  Every poll reads
+// all n flags at once (a few loads per lane), so the wait ends one round
+// trip after the last flag is raised.
 __device__ bool wave_wait_flags(const uint32_t* flags, int n, uint32_t epoch, uint32_t* ctlw,
                                 uint32_t code, int tid = threadIdx.x) {
   const int lane = tid & 63;
@@ -1065,6 +1133,7 @@ __device__ bool role_gate_up(const DecodeArgs& a, int expert_rank, int rb, int r
     __syncthreads();
     QMOE_STAMP(sys, 2);
     if (!block_routing<NV>(a, epoch, sys, false, tid)) return false;
+    if (!STK && early_on(a, epoch - 1u)) call_register(a, epoch, tid);
     QMOE_STAMP(sys, 3);
     const int s = reinterpret_cast<int32_t*>(sys + kSysSlot)[expert_rank];
     m[0] = devq_at(mi ? a.up : a.gate, s);
@@ -1258,6 +1327,7 @@ __device__ bool role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
   QMOE_STAMP(sys, 1);
   // 2. routing, then at once the routed-down weights
   if (!block_routing<NV>(a, epoch, sys, b == 0, t)) return false;
+  if (!STK && early_on(a, epoch - 1u)) call_register(a, epoch, t);
   QMOE_STAMP(sys, 2);
   const int32_t* slot_s = reinterpret_cast<const int32_t*>(sys + kSysSlot);
   const float* w_s = reinterpret_cast<const float*>(sys + kSysW);
@@ -1375,8 +1445,10 @@ __global__ __launch_bounds__(kBlock) void k_moe_step(DecodeArgs a) {
   const uint32_t gen = load_gen(a.ws, a.wl.ctl);
   const uint32_t epoch = gen + 1;
   const int rb = a.role0 + blockIdx.x;
+  const bool early = early_on(a, gen);
   if (rb < a.nR) {
     role_router<HC, false>(a, rb, smem, epoch);
+    if (early) call_register(a, epoch);
   } else if (rb < a.nR + a.nS) {
     const int s = rb - a.nR;
     // (a block whose wait gave up publishes all the same, so that its
@@ -1385,6 +1457,10 @@ __global__ __launch_bounds__(kBlock) void k_moe_step(DecodeArgs a) {
     block_publish(a, s, epoch);
     QMOE_STAMP(sys, 5);
     (void)ok;
+    if (early) {
+      call_register(a, epoch);
+      if (s == 0) early_advance(a, gen);
+    }
     if (a.cnt == kCntS) call_done(a, s, a.nS, gen, sys);
   } else if (rb < a.nR + a.nS + a.nG) {
     const int gb = rb - a.nR - a.nS;
@@ -1395,7 +1471,7 @@ __global__ __launch_bounds__(kBlock) void k_moe_step(DecodeArgs a) {
     uint32_t held = 0;
     const int d = rb - a.nR - a.nS - a.nG;
     role_down<IC, ISC, NV, false>(a, d, smem, epoch, t_start, held, nullptr);
-    if (a.cnt == kCntD) call_done(a, d, a.nD, gen, sys);
+    if (a.cnt == kCntD && !early) call_done(a, d, a.nD, gen, sys);
   }
 #ifdef QMOE_TRACE
   QMOE_STAMP(sys, 9);
@@ -1664,11 +1740,13 @@ qmoe_status launch_moe_step(const qmoe_moe_layer& L, const uint16_t* x, const in
   a.s_done = 0;
   a.dwait = 0;
   a.dtag = 0;
-  // one tag per call; the blocks of the call's last role advance the
-  // workspace's tag counter when all of them are done
+  // one tag per call; the workspace's tag counter advances once every block
+  // of the call has read it (early_advance in a fused call, else the
+  // completion count of the call's last role)
   a.ntags = 1;
   a.cnt = kCntD;
   a.heal = heal;
+  a.early = 0;
   if (mode == kStepShared || mode == kStepRouted) {
     if (mode == kStepRouted && !idx_in) return QMOE_ERR_NULL_ARG;
     if (mode == kStepShared) {
@@ -1684,6 +1762,7 @@ qmoe_status launch_moe_step(const qmoe_moe_layer& L, const uint16_t* x, const in
   }
   if (!phased) {
     a.role0 = 0;
+    a.early = !heal && a.nS > 0;
     launch_step(a, a.nR + a.nS + a.nG + a.nD, lds, stream, e0, e1);
     return hipGetLastError() == hipSuccess ? QMOE_OK : QMOE_ERR_HIP;
   }

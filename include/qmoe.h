@@ -302,7 +302,7 @@ qmoe_status qmoe_workspace_status(void* ws, size_t ws_bytes, int32_t* device_cod
  * match flag and tag words against values above every value already in
  * the workspace: a one-layer call (qmoe_moe_decode, _timed, _phased,
  * qmoe_expert_ffn, the split FFN calls) uses counter + 1, a stack call of n
- * layers counter + 1 .. counter + n, and the call's last block raises the
+ * layers counter + 1 .. counter + n, and one block of the call raises the
  * counter by that many once every block of the call has read it.  So no
  * word left by an earlier call, of any shape or mode, matches a later
  * call's, whatever else ran in between.  A zero-filled workspace starts at
