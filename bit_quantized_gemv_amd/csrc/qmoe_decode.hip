@@ -1133,14 +1133,19 @@ __device__ bool role_gate_up(const DecodeArgs& a, int expert_rank, int rb, int r
     __syncthreads();
     QMOE_STAMP(sys, 2);
     if (!block_routing<NV>(a, epoch, sys, false, tid)) return false;
-    if (!STK && early_on(a, epoch - 1u)) call_register(a, epoch, tid);
     QMOE_STAMP(sys, 3);
     const int s = reinterpret_cast<int32_t*>(sys + kSysSlot)[expert_rank];
     m[0] = devq_at(mi ? a.up : a.gate, s);
     m[1] = rows_below(m[0], H);
     dst = (size_t)a.Is + (size_t)expert_rank * a.I;
+    // (the registration after the weight loads, which it would otherwise
+    // hold back when the memory pipeline is full)
     rows4_run<2, HC / 64>(m, row0, rows, H, half * CWh, CWh, xs, xh, sbl,
-                          [&] { QMOE_STAMP(sys, 1); }, acc, tid);
+                          [&] {
+                            QMOE_STAMP(sys, 1);
+                            if (!STK && early_on(a, epoch - 1u)) call_register(a, epoch, tid);
+                          },
+                          acc, tid);
   }
   QMOE_STAMP(sys, 4);
   if ((lane >> 3) == 0) {
@@ -1327,7 +1332,6 @@ __device__ bool role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
   QMOE_STAMP(sys, 1);
   // 2. routing, then at once the routed-down weights
   if (!block_routing<NV>(a, epoch, sys, b == 0, t)) return false;
-  if (!STK && early_on(a, epoch - 1u)) call_register(a, epoch, t);
   QMOE_STAMP(sys, 2);
   const int32_t* slot_s = reinterpret_cast<const int32_t*>(sys + kSysSlot);
   const float* w_s = reinterpret_cast<const float*>(sys + kSysW);
@@ -1335,6 +1339,9 @@ __device__ bool role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
     const int k = t / CHk, c = t - k * CHk;
     dtask_load(T, devq_at(a.down, slot_s[k]), row0, CHk, c);
   }
+  // (after the routed-down loads, which it would otherwise hold back when
+  // the memory pipeline is full)
+  if (!STK && early_on(a, epoch - 1u)) call_register(a, epoch, t);
   if constexpr (kOnePass) {
     // 3-4. two passes through one copy of the wait / staging / accumulate
     //    code: pass 0 takes the shared activations once the S blocks are
@@ -1433,7 +1440,14 @@ __device__ void trace_flush(uint32_t* sys, uint32_t gen) {
 #endif
 
 template <int HC, int IC, int ISC, int EC>
+// (trace builds: bounded to the VGPRs of four waves per SIMD, which the
+// plain build meets by itself, so that every block is resident at once in
+// both and the timeline measures the same schedule)
+#ifdef QMOE_TRACE
+__global__ __launch_bounds__(kBlock, 4) void k_moe_step(DecodeArgs a) {
+#else
 __global__ __launch_bounds__(kBlock) void k_moe_step(DecodeArgs a) {
+#endif
   constexpr int NV = EC ? cdiv(EC, 64) : QMOE_MAX_EXPERTS / 64;
   extern __shared__ __align__(16) uint8_t smem[];
   uint32_t* sys = reinterpret_cast<uint32_t*>(smem);
