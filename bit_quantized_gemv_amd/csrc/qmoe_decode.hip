@@ -1331,7 +1331,7 @@ __device__ bool role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
   if (kOnePass && !routed) dtask_load(T, a.shd, row0, CHs, min(t - nrt, CHs - 1));
   QMOE_STAMP(sys, 1);
   // 2. routing, then at once the routed-down weights
-  if (!block_routing<NV>(a, epoch, sys, b == 0, t)) return false;
+  if (!block_routing<NV>(a, epoch, sys, false, t)) return false;
   QMOE_STAMP(sys, 2);
   const int32_t* slot_s = reinterpret_cast<const int32_t*>(sys + kSysSlot);
   const float* w_s = reinterpret_cast<const float*>(sys + kSysW);
@@ -1339,9 +1339,14 @@ __device__ bool role_down(const DecodeArgs& a, int b, uint8_t* smem, uint32_t ep
     const int k = t / CHk, c = t - k * CHk;
     dtask_load(T, devq_at(a.down, slot_s[k]), row0, CHk, c);
   }
-  // (after the routed-down loads, which it would otherwise hold back when
+  // (the registration and block 0's copy of the routing for the caller
+  // after the routed-down loads, which they would otherwise hold back when
   // the memory pipeline is full)
   if (!STK && early_on(a, epoch - 1u)) call_register(a, epoch, t);
+  if (b == 0 && t < K) {
+    if (a.idx_out) a.idx_out[t] = reinterpret_cast<const int32_t*>(sys + kSysIdx)[t];
+    if (a.w_out) a.w_out[t] = w_s[t];
+  }
   if constexpr (kOnePass) {
     // 3-4. two passes through one copy of the wait / staging / accumulate
     //    code: pass 0 takes the shared activations once the S blocks are
