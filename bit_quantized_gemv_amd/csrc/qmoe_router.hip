@@ -12,9 +12,10 @@
 // product is exact: D_g comes from two v_mfma_f32_16x16x32_bf16 per group of
 // 64 columns (fp32 accumulation), X_g from the same instruction with a ones
 // operand, and the per-group scale and bias are applied in fp32 on the
-// vector units.  A block owns a tile of 16 tokens x 16 experts; its 8 waves
-// split the groups, and their partial tiles are summed in a fixed order.
-// The last block of a token tile (a counter) runs the top-k of its tokens.
+// vector units.  A block owns a tile of 8 tokens x 16 experts (the MFMA's
+// 16 A rows hold the 8 tokens twice); its 8 waves split the groups, and
+// their partial tiles are summed in a fixed order.  The last block of a
+// token tile (a counter) runs the top-k of its tokens, one per wave.
 #include <hip/hip_runtime.h>
 
 #include "qmoe_common.h"
@@ -25,7 +26,8 @@ namespace qmoe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float rt_f4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kRtTile = 16;                // tokens and experts per tile
+constexpr int kRtTile = 16;                // experts per tile (MFMA rows and columns)
+constexpr int kRtTokTile = 8;              // tokens per tile: one per wave in the top-k
 constexpr int kRtWaves = 8;                // waves per block: the groups split 8 ways
 constexpr int kRtThreads = kRtWaves * 64;
 constexpr int kRtGP = 6;                   // groups per wave per pass (loads issued at once)
@@ -57,12 +59,12 @@ __global__ __launch_bounds__(kRtThreads) void k_router_mma(DevQ Wr, const float*
   __shared__ uint32_t last;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int n = lane & 15, j = lane >> 4;
-  const int e0 = blockIdx.x * kRtTile, t0 = blockIdx.y * kRtTile;
+  const int e0 = blockIdx.x * kRtTile, t0 = blockIdx.y * kRtTokTile;
   const int G = H / 64;
   const int g0 = wave * G / kRtWaves, g1 = (wave + 1) * G / kRtWaves;
   // this lane's A row (token) and B column (expert); past the end: a valid
   // row whose results are not stored
-  const int ta = min(t0 + n, T - 1), eb = min(e0 + n, E - 1);
+  const int ta = min(t0 + (n & (kRtTokTile - 1)), T - 1), eb = min(e0 + n, E - 1);
   const uint16_t* xr = x + (size_t)ta * H;
   const uint8_t* qr = Wr.q + (size_t)eb * H;
   const QMOE_GLOBAL uint16_t* sr = gptr(Wr.s + (size_t)eb * G);
@@ -115,7 +117,7 @@ __global__ __launch_bounds__(kRtThreads) void k_router_mma(DevQ Wr, const float*
 #pragma unroll
     for (int q = 0; q < kRtWaves; ++q) v += part[q][threadIdx.x];
     const int t = t0 + m, e = e0 + c;
-    if (t < T && e < E) {
+    if (m < kRtTokTile && t < T && e < E) {
       if (lbias) v += gptr(lbias)[e];
       st_dev(logits_ws + (size_t)t * E + e, v);
       if (logits_out) logits_out[(size_t)t * E + e] = v;
@@ -133,7 +135,8 @@ __global__ __launch_bounds__(kRtThreads) void k_router_mma(DevQ Wr, const float*
   }
   __syncthreads();
   if (!last) return;
-  for (int t = t0 + wave; t < min(T, t0 + kRtTile); t += kRtWaves) {
+  static_assert(kRtTokTile == kRtWaves, "one token per wave");
+  for (int t = t0 + wave; t < min(T, t0 + kRtTokTile); t += kRtWaves) {
     float v[NV];
 #pragma unroll
     for (int m = 0; m < NV; ++m) {
@@ -150,7 +153,7 @@ static void launch_router_nv(const qmoe_qtensor& Wr, const float* lbias, const u
                              int K, int32_t* idx, float* w, float* logits, float* lw, uint32_t* c,
                              hipStream_t st) {
   const int E = Wr.rows, H = Wr.cols;
-  dim3 grid(cdiv(E, kRtTile), cdiv(T, kRtTile));
+  dim3 grid(cdiv(E, kRtTile), cdiv(T, kRtTokTile));
   hipLaunchKernelGGL(k_router_mma<NV>, grid, dim3(kRtThreads), 0, st, devq(Wr), lbias, x, T, E, H,
                      K, idx, w, logits, lw, c);
 }
