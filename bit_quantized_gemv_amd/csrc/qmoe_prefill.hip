@@ -107,7 +107,8 @@ __device__ __forceinline__ void pf_prep_word(const uint16_t* X, int T, int H, _F
 // earlier waves (per-wave counts, prefix over waves) + earlier lanes of its
 // wave with the same expert (ballot match on the bits of the expert id).
 //
-// It also writes the GEMMs' work list, items = [n_items, (e, row0, M)...]:
+// It also writes the GEMMs' work list, items = [n_items | n_pairs << 16,
+// (e, row0, M)...]:
 // first the shared expert's chunks of kPfMaxM token rows (e = -1, row0 =
 // first token), then the experts' chunks of kPfMaxM pair rows (row0 = first
 // sorted pair), experts in order of decreasing row count (ties: lower id
@@ -128,6 +129,7 @@ __global__ __launch_bounds__(1024) void k_pf_dispatch(const int32_t* idx, int n,
   __shared__ int32_t off[QMOE_MAX_EXPERTS + 1];
   __shared__ int32_t tot[QMOE_MAX_EXPERTS];      // rows per expert
   __shared__ int32_t ist[QMOE_MAX_EXPERTS + 1];  // chunks per rank, then first item per rank
+  __shared__ int32_t npair;                       // experts with two chunks
   const int p = threadIdx.x, wave = p >> 6, lane = p & 63;
   for (int i = p; i < 16 * QMOE_MAX_EXPERTS; i += 1024) (&cnt[0][0])[i] = 0;
   __syncthreads();
@@ -157,8 +159,11 @@ __global__ __launch_bounds__(1024) void k_pf_dispatch(const int32_t* idx, int n,
   if (p == 0) off[0] = 0;
   __syncthreads();
   // experts by decreasing count: rank of expert x, its chunks at that rank
+  if (p == 0) npair = 0;
+  __syncthreads();
   int xr = 0;
   if (p < E) {
+    if (tot[p] > kPfMaxM) atomicAdd(&npair, 1);
     const int cx = tot[p];
     for (int y = 0; y < E; ++y) {
       const int cy = tot[y];
@@ -205,7 +210,9 @@ __global__ __launch_bounds__(1024) void k_pf_dispatch(const int32_t* idx, int n,
       items[3 + 3 * it] = min(cx - c * kPfMaxM, kPfMaxM);
     }
   }
-  if (p == 0) items[0] = nsh + ist[E];
+  // the item count, and in bits 16.. the experts with two chunks (they
+  // lead the experts' items: the GEMMs pair their chunks' tiles)
+  if (p == 0) items[0] = (nsh + ist[E]) | (npair << 16);
 }
 
 // ================================================================= GEMMs
@@ -240,7 +247,7 @@ struct PfArgs {
   DevQ gate, up, down, shg, shu, shd;
   const int32_t* slot;
   const int32_t* perm;   // sorted pair -> flat pair index t*K + j
-  const int32_t* items;  // [n_items, (e, row0, M) ...] (the dispatch's work list)
+  const int32_t* items;  // [n_items | n_pairs << 16, (e, row0, M) ...] (the dispatch's work list)
   const _Float16* xh;   // [T][pad128(H)] prepared input
   _Float16* act;        // [T*K][pad128(I)] routed activations (sorted order, prepared layout)
   _Float16* act_sh;     // [T][pad128(Is)]
@@ -552,32 +559,68 @@ __device__ __forceinline__ void pf_down_store(const f4_t (&acc)[NMS][1], float* 
 // Work unit of block b: (item, tile of 64 weight rows).  The shared items
 // (the first nsh) have tsh tiles each and come first; the experts' items
 // have tr tiles each.  Returns false past the last item.
+//
+// Sibling items stream the same weights: the two chunks of the shared
+// expert (T > 64), and those of each expert with more than kPfMaxM rows
+// (they lead the experts' items, which come in decreasing row count; the
+// dispatch puts their number in bits 16.. of the list's first word).  Their
+// equal tiles get blocks 8 apart: the same XCD, dispatched together, so
+// that the second read of a tile's weights can hit that XCD's L2.  A pair's
+// 2 nt units go in groups of up to 8 tiles, the first chunk's then the
+// second's.
 struct PfUnit {
   int e, row0, M, n0;
 };
-__device__ __forceinline__ bool pf_unit(const int32_t* items, int T, int tsh, int tr, PfUnit& u) {
+__device__ __forceinline__ void pf_pair_unit(int u, int nt, int& chunk, int& tile) {
+  const int g = u / 16, r = u - 16 * g;
+  const int w = min(8, nt - 8 * g);  // tiles in this group
+  chunk = r >= w ? 1 : 0;
+  tile = 8 * g + (r >= w ? r - w : r);
+}
+__device__ __forceinline__ bool pf_unit(const int32_t* items, int T, int E, int K, int tsh, int tr,
+                                        PfUnit& u) {
   const int b = blockIdx.x;
   const int nsh = (T + kPfMaxM - 1) / kPfMaxM;
-  int it, tile;
+  // it_p / tile_p: the unit as part of a sibling pair of experts' items,
+  // it_q / tile_q: as a plain one (which applies is known once the list's
+  // first word is in; both items' words are read with it)
+  int it_p, tile_p, it_q, tile_q;
+  bool routed = false;
+  int b2 = 0;
   if (b < nsh * tsh) {
-    it = b / tsh;
-    tile = b - it * tsh;
+    if (nsh == 2) {
+      pf_pair_unit(b, tsh, it_q, tile_q);
+    } else {
+      it_q = b / tsh;
+      tile_q = b - it_q * tsh;
+    }
+    it_p = it_q;
+    tile_p = tile_q;
   } else {
-    const int b2 = b - nsh * tsh;
-    it = nsh + b2 / tr;
-    tile = b2 - (it - nsh) * tr;
+    routed = true;
+    b2 = b - nsh * tsh;
+    it_q = nsh + b2 / tr;
+    tile_q = b2 - (it_q - nsh) * tr;
+    const int pr = b2 / (2 * tr);
+    int c;
+    pf_pair_unit(b2 - pr * 2 * tr, tr, c, tile_p);
+    it_p = min(nsh + 2 * pr + c, pf_max_items(E, K, T) - 1);
   }
-  // one round trip: the item's words are read together with the item count
-  // (the list has room for every item the grid can name)
-  // (the empty asm uses all four before the compare: the compiler would
-  // otherwise read the item's words only after it, a second round trip)
-  const int n = items[0];
-  const int e = items[1 + 3 * it], row0 = items[2 + 3 * it], M = items[3 + 3 * it];
-  asm volatile("" ::"s"(n), "s"(e), "s"(row0), "s"(M));
-  u.e = e;
-  u.row0 = row0;
-  u.M = M;
-  u.n0 = tile * kPfRows;
+  // one round trip: the items' words are read together with the list's
+  // first word (the list has room for every item the grid can name)
+  // (the empty asm uses all of them before the compares: the compiler would
+  // otherwise read the items' words only after them, a second round trip)
+  const int w0 = items[0];
+  const int ep = items[1 + 3 * it_p], rp = items[2 + 3 * it_p], Mp = items[3 + 3 * it_p];
+  const int eq = items[1 + 3 * it_q], rq = items[2 + 3 * it_q], Mq = items[3 + 3 * it_q];
+  asm volatile("" ::"s"(w0), "s"(ep), "s"(rp), "s"(Mp), "s"(eq), "s"(rq), "s"(Mq));
+  const int n = w0 & 0xffff, npair = w0 >> 16;
+  const bool pair = routed && b2 < 2 * npair * tr;
+  const int it = pair ? it_p : it_q;
+  u.e = pair ? ep : eq;
+  u.row0 = pair ? rp : rq;
+  u.M = pair ? Mp : Mq;
+  u.n0 = (pair ? tile_p : tile_q) * kPfRows;
   return it < n;
 }
 
@@ -589,7 +632,7 @@ __global__ __launch_bounds__(kBlock, 2) void k_pf_gu(PfArgs a) {
   __shared__ PfShared<2, SB> sh;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   PfUnit u;
-  if (!pf_unit(a.items, a.T, a.Is / kPfRows, a.I / kPfRows, u)) return;
+  if (!pf_unit(a.items, a.T, a.E, a.K, a.Is / kPfRows, a.I / kPfRows, u)) return;
   const bool shared = u.e < 0;
   DevQ W[2];
   if (shared) {
@@ -640,7 +683,7 @@ __global__ __launch_bounds__(kBlock, 3) void k_pf_down(PfArgs a) {
   __shared__ PfShared<1, SB> sh;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   PfUnit u;
-  if (!pf_unit(a.items, a.T, a.H / kPfRows, a.H / kPfRows, u)) return;
+  if (!pf_unit(a.items, a.T, a.E, a.K, a.H / kPfRows, a.H / kPfRows, u)) return;
   const bool shared = u.e < 0;
   const int Kd = shared ? a.Is : a.I;
   const _Float16* src = shared ? a.act_sh : a.act;
