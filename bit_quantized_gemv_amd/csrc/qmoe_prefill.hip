@@ -130,6 +130,7 @@ __global__ __launch_bounds__(1024) void k_pf_dispatch(const int32_t* idx, int n,
   __shared__ int32_t tot[QMOE_MAX_EXPERTS];      // rows per expert
   __shared__ int32_t ist[QMOE_MAX_EXPERTS + 1];  // chunks per rank, then first item per rank
   __shared__ int32_t npair;                       // experts with two chunks
+  __shared__ int32_t rk[QMOE_MAX_EXPERTS];        // rank of each expert
   const int p = threadIdx.x, wave = p >> 6, lane = p & 63;
   for (int i = p; i < 16 * QMOE_MAX_EXPERTS; i += 1024) (&cnt[0][0])[i] = 0;
   __syncthreads();
@@ -158,36 +159,59 @@ __global__ __launch_bounds__(1024) void k_pf_dispatch(const int32_t* idx, int n,
   }
   if (p == 0) off[0] = 0;
   __syncthreads();
-  // experts by decreasing count: rank of expert x, its chunks at that rank
+  // experts by decreasing count: the rank of expert x, summed over `per`
+  // threads (each counts the experts y = part, part + per, ... that come
+  // before x), and its chunks at that rank
   if (p == 0) npair = 0;
   __syncthreads();
-  int xr = 0;
-  if (p < E) {
-    if (tot[p] > kPfMaxM) atomicAdd(&npair, 1);
-    const int cx = tot[p];
-    for (int y = 0; y < E; ++y) {
-      const int cy = tot[y];
-      xr += (cy > cx) || (cy == cx && y < p);
+  {
+    const int per = E <= 128 ? 8 : (E <= 256 ? 4 : 2);
+    const int x = p / per, part = p - x * per;
+    int r = 0;
+    if (x < E) {
+      const int cx = tot[x];
+      for (int y = part; y < E; y += per) {
+        const int cy = tot[y];
+        r += (cy > cx) || (cy == cx && y < x);
+      }
     }
-    ist[xr + 1] = (cx + kPfMaxM - 1) / kPfMaxM;
+    for (int o = 1; o < per; o <<= 1) r += __shfl_xor(r, o);
+    if (x < E && part == 0) {
+      rk[x] = r;
+      ist[r + 1] = (tot[x] + kPfMaxM - 1) / kPfMaxM;
+      if (tot[x] > kPfMaxM) atomicAdd(&npair, 1);
+    }
   }
   if (p == 0) ist[0] = 0;
   __syncthreads();
-  // inclusive scans of off[1..E] and ist[1..E] (Hillis-Steele over up to
-  // 512 entries)
-  for (int d = 1; d < E; d <<= 1) {
-    int v = 0, u = 0;
-    if (p >= d && p < E) {
-      v = off[p + 1 - d];
-      u = ist[p + 1 - d];
+  // inclusive scans of off[1..E] (wave 0) and ist[1..E] (wave 1): each lane
+  // sums a run of up to 8 consecutive entries, the runs' sums are scanned
+  // across the wave by shuffles, and each lane adds its prefix back
+  if (wave < 2) {
+    int32_t* arr = (wave == 0 ? off : ist) + 1;
+    const int run = (E + 63) / 64;
+    const int j0 = lane * run;
+    int loc[8];
+    int sum = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      loc[i] = (i < run && j0 + i < E) ? arr[j0 + i] : 0;
+      sum += loc[i];
     }
-    __syncthreads();
-    if (p >= d && p < E) {
-      off[p + 1] += v;
-      ist[p + 1] += u;
+    int incl = sum;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int v = __shfl_up(incl, o);
+      if (lane >= o) incl += v;
     }
-    __syncthreads();
+    int acc = incl - sum;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      acc += loc[i];
+      if (i < run && j0 + i < E) arr[j0 + i] = acc;
+    }
   }
+  __syncthreads();
   for (int x = p; x <= E; x += 1024) offsets[x] = off[x];
   if (act) {
     int pos = off[e] + cnt[wave][e] + rank;
@@ -204,7 +228,7 @@ __global__ __launch_bounds__(1024) void k_pf_dispatch(const int32_t* idx, int n,
   if (p < E) {
     const int cx = tot[p];
     for (int c = 0; c * kPfMaxM < cx; ++c) {
-      const int it = nsh + ist[xr] + c;
+      const int it = nsh + ist[rk[p]] + c;
       items[1 + 3 * it] = p;
       items[2 + 3 * it] = off[p] + c * kPfMaxM;
       items[3 + 3 * it] = min(cx - c * kPfMaxM, kPfMaxM);
