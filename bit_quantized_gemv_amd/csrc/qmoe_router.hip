@@ -44,7 +44,7 @@ __device__ __forceinline__ bf16x8_t codes8_bf16(uint32_t w0, uint32_t w1) {
   return o;
 }
 
-// grid (ceil(E/16), ceil(T/16)), kRtThreads threads.  NV = ceil(E/64) value
+// grid (ceil(E/16), ceil(T/8)), kRtThreads threads.  NV = ceil(E/64) value
 // slots per lane in the top-k.
 template <int NV>
 __global__ __launch_bounds__(kRtThreads) void k_router_mma(DevQ Wr, const float* lbias,
