@@ -73,6 +73,11 @@ __global__ __launch_bounds__(kRtThreads) void k_router_mma(DevQ Wr, const float*
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = __builtin_bit_cast(__bf16, (uint16_t)0x3F80);
   rt_f4_t acc = {0.f, 0.f, 0.f, 0.f};
+  // the logit bias of the expert this thread sums below, read ahead of the
+  // weights so that it is not a round trip after the reduction
+  float lb = 0.f;
+  if (lbias && threadIdx.x < kRtTile * kRtTile)
+    lb = gptr(lbias)[min(e0 + (int)threadIdx.x % kRtTile, E - 1)];
   // MFMA k slots 8j..8j+7 of the first instruction hold columns 16j..16j+7
   // of the group, those of the second 16j+8..16j+15 (any assignment of
   // columns to slots gives the same exact products)
@@ -118,7 +123,7 @@ __global__ __launch_bounds__(kRtThreads) void k_router_mma(DevQ Wr, const float*
     for (int q = 0; q < kRtWaves; ++q) v += part[q][threadIdx.x];
     const int t = t0 + m, e = e0 + c;
     if (m < kRtTokTile && t < T && e < E) {
-      if (lbias) v += gptr(lbias)[e];
+      if (lbias) v += lb;
       st_dev(logits_ws + (size_t)t * E + e, v);
       if (logits_out) logits_out[(size_t)t * E + e] = v;
     }
